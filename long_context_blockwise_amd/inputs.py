@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for ring-attention workloads.
+
+This module is shared by the HIP path (benchmark, GPU tests) and by the CPU
+oracle's tests.  It holds none of the method's arithmetic: it only describes
+workload shapes and draws seeded random tensors.  Every tensor is drawn in
+float32 from N(0, 1) with a torch generator seeded per (workload seed, tensor,
+chunk), multiplied by the workload's scale, and rounded to the workload dtype
+(round-to-nearest-even for bfloat16).  The same bits are handed to both sides:
+GPU tests copy the generated device tensors to the host for the oracle.
+
+Workloads (one device's share of the ring, shapes from the pages' settings):
+
+* ``tiny_ring_fp32``: 1 batch, 1 head, d=64, fp32, a 1024-token sequence as 4
+  chunks of 256; query chunk 0 against all 4 KV chunks, non-causal.
+* ``prefill_bf16_h32_d128``: 32 heads, d=128, bf16, 32768 tokens as 4 chunks
+  of 8192; query chunk 3 against chunks 0..3, causal; entries N(0,1)*0.5.
+* ``ring_1m_gqa32x8_d128``: 32 query / 8 KV heads, d=128, bf16, 1,048,576
+  tokens as 32 chunks of 32768; the last query chunk, causal; N(0,1)*0.5.
+* ``mla_h16_d512``: 16 query heads sharing one 512-wide KV head, bf16, 131072
+  tokens as 8 chunks of 16384; query chunk 7, causal; N(0,1)*4/sqrt(512).
+* ``decode_b4_gqa32x8_cache1m``: 4 sequences, 32 query / 8 KV heads, d=128,
+  bf16, a 1,048,576-token KV cache in 64 chunks of 16384; 16 new query tokens
+  at cache_idx = 1,048,560 (their K/V are the cache's last 16 slots), causal.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import List, Optional, Tuple
+
+import torch
+
+_TENSOR_Q, _TENSOR_K, _TENSOR_V = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d_qk: int
+    d_v: int
+    dtype: str  # "fp32" | "bf16"
+    chunk_len: int  # tokens per KV chunk
+    P: int  # number of KV chunks
+    Lq: int  # query rows of this device
+    q_offset: int  # absolute position of query row 0
+    causal: bool
+    std: float  # inputs are N(0,1) * std before rounding
+    seed: int
+    # explicit per-chunk lengths (ragged tails); None means all chunk_len
+    chunk_lens: Optional[Tuple[int, ...]] = field(default=None)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    def lens(self) -> List[int]:
+        return list(self.chunk_lens) if self.chunk_lens else [self.chunk_len] * self.P
+
+    def starts(self) -> List[int]:
+        s, out = 0, []
+        for n in self.lens():
+            out.append(s)
+            s += n
+        return out
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_ring_fp32": Workload("tiny_ring_fp32", B=1, Hq=1, Hkv=1, d_qk=64, d_v=64,
+                               dtype="fp32", chunk_len=256, P=4, Lq=256, q_offset=0,
+                               causal=False, std=1.0, seed=1),
+    "prefill_bf16_h32_d128": Workload("prefill_bf16_h32_d128", B=1, Hq=32, Hkv=32,
+                                      d_qk=128, d_v=128, dtype="bf16", chunk_len=8192,
+                                      P=4, Lq=8192, q_offset=3 * 8192, causal=True,
+                                      std=0.5, seed=2),
+    "ring_1m_gqa32x8_d128": Workload("ring_1m_gqa32x8_d128", B=1, Hq=32, Hkv=8,
+                                     d_qk=128, d_v=128, dtype="bf16", chunk_len=32768,
+                                     P=32, Lq=32768, q_offset=31 * 32768, causal=True,
+                                     std=0.5, seed=3),
+    "mla_h16_d512": Workload("mla_h16_d512", B=1, Hq=16, Hkv=1, d_qk=512, d_v=512,
+                             dtype="bf16", chunk_len=16384, P=8, Lq=16384,
+                             q_offset=7 * 16384, causal=True, std=4.0 / 512 ** 0.5,
+                             seed=4),
+    "decode_b4_gqa32x8_cache1m": Workload("decode_b4_gqa32x8_cache1m", B=4, Hq=32,
+                                          Hkv=8, d_qk=128, d_v=128, dtype="bf16",
+                                          chunk_len=16384, P=64, Lq=16,
+                                          q_offset=1048560, causal=True, std=0.5,
+                                          seed=5),
+}
+
+
+def _generator(device, seed: int, tensor: int, chunk: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    # one independent stream per (workload seed, tensor, chunk)
+    g.manual_seed((seed * 1_000_003 + tensor * 65_537 + chunk * 257 + 12_345) % (2**63))
+    return g
+
+
+def draw(shape, std: float, dtype, device, seed: int, tensor: int, chunk: int = 0):
+    """N(0,1)*std in float32 from a seeded stream, rounded to ``dtype``."""
+    g = _generator(device, seed, tensor, chunk)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+@dataclass
+class Inputs:
+    wl: Workload
+    q: torch.Tensor  # [B, Lq, Hq, d_qk]
+    ks: List[torch.Tensor]  # chunk c: [B, len_c, Hkv, d_qk]
+    vs: List[torch.Tensor]  # chunk c: [B, len_c, Hkv, d_v]
+    starts: List[int]
+
+    def chunks(self, order=None):
+        """``[(k, v, start)]`` in ``order`` (default: chunk index order)."""
+        idx = range(len(self.ks)) if order is None else order
+        return [(self.ks[c], self.vs[c], self.starts[c]) for c in idx]
+
+
+def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:
+    """Draw the query chunk and all KV chunks of a workload on ``device``."""
+    dt = wl.torch_dtype
+    q = draw((wl.B, wl.Lq, wl.Hq, wl.d_qk), wl.std if q_std is None else q_std, dt,
+             device, wl.seed, _TENSOR_Q)
+    ks, vs = [], []
+    for c, n in enumerate(wl.lens()):
+        ks.append(draw((wl.B, n, wl.Hkv, wl.d_qk), wl.std, dt, device, wl.seed,
+                       _TENSOR_K, c))
+        vs.append(draw((wl.B, n, wl.Hkv, wl.d_v), wl.std, dt, device, wl.seed,
+                       _TENSOR_V, c))
+    return Inputs(wl, q, ks, vs, wl.starts())
+
+
+def sample_rows(Lq: int, tile: int = 128, seed: int = 0, extra=()) -> List[int]:
+    """A stratified row sample: one seeded random row per ``tile`` rows plus
+    rows at tile and chunk boundaries (and ``extra``), sorted and unique."""
+    g = torch.Generator().manual_seed(seed)
+    rows = set()
+    for t0 in range(0, Lq, tile):
+        n = min(tile, Lq - t0)
+        rows.add(t0 + int(torch.randint(n, (1,), generator=g)))
+    for r in (0, 1, 15, 16, 31, 32, 63, 64, 127, 128, Lq // 2 - 1, Lq // 2, Lq - 2,
+              Lq - 1, *extra):
+        if 0 <= r < Lq:
+            rows.add(int(r))
+    return sorted(rows)

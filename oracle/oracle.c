@@ -1,0 +1,327 @@
+/*
+ * oracle.c - slow, plain, double-precision reference for ring attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library under
+ * long_context_blockwise_amd/) links, loads or calls this file, and this file
+ * shares no code, header, table or helper with it.  Only tests/, the smoke
+ * check and the CPU-baseline leg of bench.py use it.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - oracle_attention: scaled dot-product attention, softmax(Q K^T / sqrt(d)) V,
+ *    evaluated row by row straight from the definition with a two-pass softmax.
+ *      page "从百毫秒到百万Token：长上下文推理优化的工程实践", section
+ *        "注意力机制的数学本质与瓶颈" (the definition);
+ *      page "billion-token context window engineering" (blog.hotdry.top),
+ *        section "核心挑战：注意力机制的二次复杂度困境" (same definition);
+ *      page "Ring Attention：百万 Token 上下文的秘密", §2.3 数学正确性 (ring
+ *        result equals plain attention over all key chunks).
+ *    The key set of a query row is the union of all KV chunks; chunk c holds
+ *    the keys at absolute positions start[c] .. start[c]+len[c]-1, as in the
+ *    sequence sharding of §2.1 分块计算注意力 on the same page.
+ *
+ *  - oracle_ring_step: one step of the chunked online-softmax recurrence
+ *    (running max m, denominator l, unnormalised output O) that one device
+ *    performs per received KV chunk:
+ *      page "Ring Attention：百万 Token 上下文的秘密", §3.1 Flash Ring
+ *        Attention (per-chunk blockwise attention inside the ring loop) and
+ *        §2.2 环形通信 (one chunk per ring step).
+ *    The pages do not write the recurrence out; this is the standard
+ *    flash/online-softmax update, the reading taken for §2.3's equation.
+ *
+ *  - oracle_merge / oracle_finalize: combining two partial states and turning
+ *    a state into the output (O / l), the "global softmax normalisation of
+ *    local outputs" of the attention fusion layer:
+ *      page "从百毫秒到百万Token：长上下文推理优化的工程实践", section
+ *        "系统架构设计", item 4 注意力融合层.
+ *
+ * Causal masking is token level with the diagonal included: a query at
+ * absolute position p sees a key at position t iff t <= p.  The query row r
+ * sits at absolute position q_offset + r (q_offset = chunk index * chunk
+ * length in a prefill ring, or cache_idx in incremental decoding:
+ *   page "RingAttention推理优化：cache_idx参数使用与千万级上下文高效推理实践",
+ *   sections "cache_idx的工作原理" and "增量推理实战").
+ * Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *
+ * Layouts (all contiguous, row-major):
+ *   q       [B][Lq][Hq][dqk]
+ *   k[c]    [B][len[c]][Hkv][dqk]     v[c]  [B][len[c]][Hkv][dv]
+ *   rows    the query rows (indices into 0..Lq-1) to evaluate
+ *   out     [B][n_rows][Hq][dv]       lse   [B][Hq][n_rows]
+ *   m, l    [B][Hq][n_rows]           O     [B][Hq][n_rows][dv]
+ * Element type of q/k/v: ORACLE_F64, ORACLE_F32, or ORACLE_BF16 (raw 16-bit
+ * patterns, upcast exactly).  All arithmetic is double.
+ *
+ * Return value: 0 on success, -1 on an argument error, -2 if out of memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
+
+/* Read element idx of an array of the given element type as a double. */
+static double elem(const void *p, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F64)
+        return ((const double *)p)[idx];
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)p)[idx];
+    /* bfloat16: the upper 16 bits of an IEEE binary32 value */
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int check_shapes(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
+                        int64_t Lq, int n_chunks, const int64_t *len,
+                        int64_t n_rows, const int64_t *rows)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || dqk <= 0 || dv <= 0 || Lq < 0 ||
+        n_chunks < 0 || n_rows < 0)
+        return -1;
+    if (Hq % Hkv != 0)
+        return -1;
+    if (dtype != ORACLE_F64 && dtype != ORACLE_F32 && dtype != ORACLE_BF16)
+        return -1;
+    for (int c = 0; c < n_chunks; ++c)
+        if (len[c] < 0)
+            return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= Lq)
+            return -1;
+    return 0;
+}
+
+/* Score of query (b, r, h) against key j of chunk c, both upcast to double. */
+static double score(const void *q, const void *kc, int dtype, int64_t Lq,
+                    int64_t lenc, int Hq, int Hkv, int dqk, int b, int64_t r,
+                    int h, int64_t j, double scale)
+{
+    int hk = h / (Hq / Hkv);
+    int64_t qb = (((int64_t)b * Lq + r) * Hq + h) * dqk;
+    int64_t kb = (((int64_t)b * lenc + j) * Hkv + hk) * dqk;
+    double dot = 0.0;
+    for (int e = 0; e < dqk; ++e)
+        dot += elem(q, dtype, qb + e) * elem(kc, dtype, kb + e);
+    return dot * scale;
+}
+
+static int visible(int causal, int64_t qpos, int64_t kpos)
+{
+    return !causal || kpos <= qpos;
+}
+
+int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
+                     const void *q, int64_t Lq, int64_t q_offset, int n_chunks,
+                     const void *const *k, const void *const *v,
+                     const int64_t *start, const int64_t *len, int causal,
+                     double scale, int64_t n_rows, const int64_t *rows,
+                     double *out, double *lse)
+{
+    if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, n_chunks, len, n_rows,
+                     rows))
+        return -1;
+    int64_t nkeys = 0;
+    for (int c = 0; c < n_chunks; ++c)
+        nkeys += len[c];
+    int64_t units = (int64_t)B * Hq * n_rows;
+    int err = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nkeys ? nkeys : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!s || !acc) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !acc)
+                continue;
+            int b = (int)(u / ((int64_t)Hq * n_rows));
+            int h = (int)((u / n_rows) % Hq);
+            int64_t i = u % n_rows;
+            int64_t r = rows[i];
+            int64_t qpos = q_offset + r;
+            int hk = h / (Hq / Hkv);
+
+            /* pass 1: scores of all visible keys and their maximum */
+            double mx = -INFINITY;
+            int64_t t = 0;
+            for (int c = 0; c < n_chunks; ++c)
+                for (int64_t j = 0; j < len[c]; ++j, ++t) {
+                    if (!visible(causal, qpos, start[c] + j)) {
+                        s[t] = -INFINITY;
+                        continue;
+                    }
+                    s[t] = score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b,
+                                 r, h, j, scale);
+                    if (s[t] > mx)
+                        mx = s[t];
+                }
+
+            double *o = out + (((int64_t)b * n_rows + i) * Hq + h) * dv;
+            double *ls = lse + ((int64_t)b * Hq + h) * n_rows + i;
+            if (mx == -INFINITY) { /* no visible key: output 0 */
+                for (int e = 0; e < dv; ++e)
+                    o[e] = 0.0;
+                *ls = -INFINITY;
+                continue;
+            }
+            /* pass 2: weights exp(s - max), their sum, and the weighted sum of V */
+            double sum = 0.0;
+            for (int e = 0; e < dv; ++e)
+                acc[e] = 0.0;
+            t = 0;
+            for (int c = 0; c < n_chunks; ++c)
+                for (int64_t j = 0; j < len[c]; ++j, ++t) {
+                    if (s[t] == -INFINITY)
+                        continue;
+                    double w = exp(s[t] - mx);
+                    sum += w;
+                    int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;
+                    for (int e = 0; e < dv; ++e)
+                        acc[e] += w * elem(v[c], dtype, vb + e);
+                }
+            for (int e = 0; e < dv; ++e)
+                o[e] = acc[e] / sum;
+            *ls = mx + log(sum);
+        }
+        free(s);
+        free(acc);
+    }
+    return err;
+}
+
+int oracle_ring_step(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
+                     const void *q, int64_t Lq, int64_t q_offset,
+                     const void *kc, const void *vc, int64_t start,
+                     int64_t len, int causal, double scale, int64_t n_rows,
+                     const int64_t *rows, double *m, double *l, double *O)
+{
+    if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, 1, &len, n_rows, rows))
+        return -1;
+    int64_t units = (int64_t)B * Hq * n_rows;
+    int err = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(len ? len : 1));
+        if (!s) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s)
+                continue;
+            int b = (int)(u / ((int64_t)Hq * n_rows));
+            int h = (int)((u / n_rows) % Hq);
+            int64_t i = u % n_rows;
+            int64_t r = rows[i];
+            int64_t qpos = q_offset + r;
+            int hk = h / (Hq / Hkv);
+            int64_t st = ((int64_t)b * Hq + h) * n_rows + i;
+
+            /* largest score of this chunk's visible keys */
+            double cmax = -INFINITY;
+            for (int64_t j = 0; j < len; ++j) {
+                if (!visible(causal, qpos, start + j)) {
+                    s[j] = -INFINITY;
+                    continue;
+                }
+                s[j] = score(q, kc, dtype, Lq, len, Hq, Hkv, dqk, b, r, h, j,
+                             scale);
+                if (s[j] > cmax)
+                    cmax = s[j];
+            }
+            if (cmax == -INFINITY) /* chunk invisible to this row */
+                continue;
+
+            /* new running max, and the factor that rescales the old state */
+            double m_new = m[st] > cmax ? m[st] : cmax;
+            double alpha = m[st] == -INFINITY ? 0.0 : exp(m[st] - m_new);
+            double *o = O + st * dv;
+            double psum = 0.0;
+            for (int e = 0; e < dv; ++e)
+                o[e] *= alpha;
+            for (int64_t j = 0; j < len; ++j) {
+                if (s[j] == -INFINITY)
+                    continue;
+                double p = exp(s[j] - m_new);
+                psum += p;
+                int64_t vb = (((int64_t)b * len + j) * Hkv + hk) * dv;
+                for (int e = 0; e < dv; ++e)
+                    o[e] += p * elem(vc, dtype, vb + e);
+            }
+            l[st] = alpha * l[st] + psum;
+            m[st] = m_new;
+        }
+        free(s);
+    }
+    return err;
+}
+
+void oracle_state_init(int64_t n, int dv, double *m, double *l, double *O)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.0;
+        for (int e = 0; e < dv; ++e)
+            O[i * dv + e] = 0.0;
+    }
+}
+
+void oracle_merge(int64_t n, int dv, const double *m1, const double *l1,
+                  const double *O1, const double *m2, const double *l2,
+                  const double *O2, double *m, double *l, double *O)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double mx = m1[i] > m2[i] ? m1[i] : m2[i];
+        if (mx == -INFINITY) { /* both partials saw no key */
+            m[i] = -INFINITY;
+            l[i] = 0.0;
+            for (int e = 0; e < dv; ++e)
+                O[i * dv + e] = 0.0;
+            continue;
+        }
+        double a1 = m1[i] == -INFINITY ? 0.0 : exp(m1[i] - mx);
+        double a2 = m2[i] == -INFINITY ? 0.0 : exp(m2[i] - mx);
+        l[i] = a1 * l1[i] + a2 * l2[i];
+        for (int e = 0; e < dv; ++e)
+            O[i * dv + e] = a1 * O1[i * dv + e] + a2 * O2[i * dv + e];
+        m[i] = mx;
+    }
+}
+
+void oracle_finalize(int64_t n, int dv, const double *m, const double *l,
+                     const double *O, double *out, double *lse)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (l[i] > 0.0) {
+            for (int e = 0; e < dv; ++e)
+                out[i * dv + e] = O[i * dv + e] / l[i];
+            lse[i] = m[i] + log(l[i]);
+        } else {
+            for (int e = 0; e < dv; ++e)
+                out[i * dv + e] = 0.0;
+            lse[i] = -INFINITY;
+        }
+    }
+}

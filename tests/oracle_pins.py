@@ -1,0 +1,420 @@
+"""Pins that tie the CPU oracle to facts fixed outside it.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle disagrees
+with something the pages or the mathematics fix independently of the
+oracle's own code:
+
+* a library routine that computes the same definition
+  (``torch.nn.functional.scaled_dot_product_attention`` in float64 with an
+  explicit position mask);
+* closed forms that need no softmax code at all (zero queries give the mean
+  of the visible values, constant values give that constant, two keys give a
+  logistic mix, the first causal row gives V_0, ...);
+* the exact result, computed with 50-digit mpmath arithmetic on tiny inputs,
+  including logits large enough to overflow a softmax without the max shift;
+* invariants the pages assert: the ring result equals plain attention for
+  every chunk count and every chunk order (page "Ring Attention：百万 Token
+  上下文的秘密", §2.2 环形通信 and §2.3 数学正确性), partial states merge
+  into the global softmax (page "从百毫秒到百万Token", 注意力融合层), and a
+  query at cache_idx + t reproduces prefill row cache_idx + t (page
+  "RingAttention推理优化：cache_idx参数使用...", 增量推理实战).
+
+``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py``
+plants mistakes in copies of ``oracle.c`` and checks that each one makes at
+least one pin fail.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import mpmath
+import numpy as np
+import torch
+
+import oracle
+
+TOL = 1e-12
+
+
+def _rand(rng, B, Lq, Hq, Hkv, dqk, dv, lens, std=1.0, vstd=1.0):
+    q = rng.standard_normal((B, Lq, Hq, dqk)) * std
+    chunks, s = [], 0
+    for n in lens:
+        k = rng.standard_normal((B, n, Hkv, dqk)) * std
+        v = rng.standard_normal((B, n, Hkv, dv)) * vstd
+        chunks.append((k, v, s))
+        s += n
+    return q, chunks
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    err = np.where(both_inf, 0.0, np.abs(a - b))
+    bad = ~(err <= tol * (1.0 + np.abs(b)))
+    assert not bad.any(), f"{what}: max err {np.nanmax(err)} (tol {tol})"
+
+
+def _positions(chunks):
+    return np.concatenate([s + np.arange(k.shape[1]) for (k, _, s) in chunks])
+
+
+# --------------------------------------------------------------------------- #
+# library routine
+# --------------------------------------------------------------------------- #
+def _sdpa(q, chunks, q_offset, causal, scale):
+    """float64 SDPA with an explicit boolean position mask (SDPA's own
+    ``is_causal`` aligns the diagonal to the top-left corner, which is wrong
+    for a query chunk at an offset, so it is not used)."""
+    K = torch.from_numpy(np.concatenate([c[0] for c in chunks], axis=1))
+    V = torch.from_numpy(np.concatenate([c[1] for c in chunks], axis=1))
+    Q = torch.from_numpy(q)
+    pos = torch.from_numpy(_positions(chunks))
+    qpos = q_offset + torch.arange(q.shape[1])
+    mask = torch.ones(q.shape[1], K.shape[1], dtype=torch.bool)
+    if causal:
+        mask = pos[None, :] <= qpos[:, None]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Q.permute(0, 2, 1, 3), K.permute(0, 2, 1, 3), V.permute(0, 2, 1, 3),
+        attn_mask=mask, scale=scale, enable_gqa=True)
+    return out.permute(0, 2, 1, 3).numpy()
+
+
+def pin_library_sdpa():
+    rng = np.random.default_rng(101)
+    cases = [
+        # B, Lq, Hq, Hkv, dqk, dv, lens, q_offset, causal
+        (1, 7, 1, 1, 8, 8, [5, 9, 3], 0, False),
+        (2, 6, 4, 2, 5, 3, [4, 4, 4], 9, True),
+        (1, 9, 6, 3, 16, 16, [7, 1, 8, 2], 11, True),
+        (2, 4, 8, 1, 12, 7, [6, 10], 15, True),
+        (1, 5, 2, 2, 4, 9, [3, 3], 0, False),
+        (1, 8, 4, 4, 6, 6, [8, 8, 8], 16, True),   # query chunk = last chunk
+    ]
+    for (B, Lq, Hq, Hkv, dqk, dv, lens, q_off, causal) in cases:
+        q, chunks = _rand(rng, B, Lq, Hq, Hkv, dqk, dv, lens)
+        scale = 1.0 / math.sqrt(dqk)
+        out, _ = oracle.attention(q, chunks, q_off, causal)
+        ref = _sdpa(q, chunks, q_off, causal, scale)
+        _close(out, ref, 1e-12, f"sdpa {B,Lq,Hq,Hkv,dqk,dv,lens,q_off,causal}")
+        # explicit repeat of KV heads (contiguous head groups) gives the same
+        g = Hq // Hkv
+        chunks_rep = [(np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), s)
+                      for (k, v, s) in chunks]
+        out_rep, _ = oracle.attention(q, chunks_rep, q_off, causal)
+        _close(out, out_rep, 1e-14, "gqa == repeated kv heads")
+
+
+# --------------------------------------------------------------------------- #
+# closed forms
+# --------------------------------------------------------------------------- #
+def pin_zero_query_mean():
+    """Q = 0 makes every visible score 0: the output is the plain mean of the
+    visible value rows and lse = log(#visible)."""
+    rng = np.random.default_rng(7)
+    B, Lq, Hq, Hkv, dqk, dv = 2, 6, 4, 2, 8, 5
+    lens = [5, 3, 6]
+    _, chunks = _rand(rng, B, Lq, Hq, Hkv, dqk, dv, lens)
+    q = np.zeros((B, Lq, Hq, dqk))
+    for causal, q_off in ((False, 0), (True, 4), (True, 8)):
+        out, lse = oracle.attention(q, chunks, q_off, causal)
+        V = np.concatenate([c[1] for c in chunks], axis=1)
+        pos = _positions(chunks)
+        for r in range(Lq):
+            vis = pos <= q_off + r if causal else np.ones_like(pos, dtype=bool)
+            n = int(vis.sum())
+            for h in range(Hq):
+                want = V[:, vis, h // (Hq // Hkv), :].mean(axis=1)
+                _close(out[:, r, h, :], want, 1e-14, f"mean row {r} head {h}")
+                _close(lse[:, h, r], np.full(B, math.log(n)), 1e-14, "lse log n")
+
+
+def pin_constant_values():
+    """Softmax weights sum to one: constant value rows give that constant."""
+    rng = np.random.default_rng(8)
+    B, Lq, Hq, Hkv, dqk, dv = 1, 5, 2, 1, 6, 4
+    q, chunks = _rand(rng, B, Lq, Hq, Hkv, dqk, dv, [4, 7], std=2.0)
+    c = np.array([0.5, -3.0, 7.25, 1e-3])
+    chunks = [(k, np.broadcast_to(c, v.shape).copy(), s) for (k, v, s) in chunks]
+    out, _ = oracle.attention(q, chunks, 3, True)
+    _close(out, np.broadcast_to(c, out.shape), 1e-14, "constant values")
+
+
+def pin_first_causal_row():
+    """A causal query at position 0 sees key 0 only: output V_0 exactly."""
+    rng = np.random.default_rng(9)
+    q, chunks = _rand(rng, 2, 3, 4, 2, 8, 8, [4, 4], std=3.0)
+    out, lse = oracle.attention(q, chunks, 0, True, rows=[0])
+    V0 = chunks[0][1][:, 0, :, :]  # [B, Hkv, dv]
+    for h in range(4):
+        assert np.array_equal(out[:, 0, h, :], V0[:, h // 2, :]), "row 0 must equal V_0"
+    # lse = the single score
+    k0 = chunks[0][0][:, 0, :, :]
+    for h in range(4):
+        s = (q[:, 0, h, :] * k0[:, h // 2, :]).sum(-1) / math.sqrt(8)
+        _close(lse[:, h, 0], s, 1e-14, "lse of one key")
+
+
+def pin_two_keys_logistic():
+    """With two visible keys the output is v1 + (v2 - v1) * sigmoid(s2 - s1),
+    s_i = q.k_i / sqrt(d); the scale 1/sqrt(d) is fixed by the definition."""
+    d = 4
+    q = np.array([[[[2.0, 0.0, 1.0, 0.0]]]])  # [1,1,1,4]
+    k = np.array([[[[1.0, 0.0, 0.0, 0.0]], [[0.0, 0.0, 3.0, 0.0]]]])  # [1,2,1,4]
+    v = np.array([[[[1.0, 2.0]], [[-1.0, 5.0]]]])
+    out, lse = oracle.attention(q, [(k, v, 0)], 0, False)
+    s1, s2 = 2.0 / math.sqrt(d), 3.0 / math.sqrt(d)
+    sig = 1.0 / (1.0 + math.exp(-(s2 - s1)))
+    want = v[0, 0, 0] + (v[0, 1, 0] - v[0, 0, 0]) * sig
+    _close(out[0, 0, 0], want, 1e-15, "two-key logistic")
+    _close(lse[0, 0, 0], s1 + math.log1p(math.exp(s2 - s1)), 1e-15, "two-key lse")
+    # explicit scale overrides the default
+    out2, _ = oracle.attention(q, [(k, v, 0)], 0, False, scale=1.0)
+    sig2 = 1.0 / (1.0 + math.exp(-(3.0 - 2.0)))
+    _close(out2[0, 0, 0], v[0, 0, 0] + (v[0, 1, 0] - v[0, 0, 0]) * sig2, 1e-15,
+           "explicit scale")
+
+
+def pin_hardmax_limit():
+    """Q = lambda * K_t with large lambda and orthonormal keys: all weight on
+    key t, output V_t (to double precision)."""
+    d = 8
+    K = np.eye(d)[None, :, None, :]  # [1, 8, 1, 8]
+    rng = np.random.default_rng(3)
+    V = rng.standard_normal((1, d, 1, 5))
+    for t in range(d):
+        q = (60.0 * K[:, t, :, :])[:, None, :, :]  # score gap 60/sqrt(8)*... > 20
+        out, _ = oracle.attention(q * math.sqrt(d), [(K[:, :4], V[:, :4], 0),
+                                                     (K[:, 4:], V[:, 4:], 4)], 0, False)
+        _close(out[0, 0, 0], V[0, t, 0], 1e-20 + 1e-15, f"hardmax key {t}")
+
+
+def pin_empty_rows():
+    """A row that sees no key (all chunks in its future) gives 0 and lse -inf;
+    a chunk entirely in the future leaves the running state bit-identical."""
+    rng = np.random.default_rng(12)
+    q, chunks = _rand(rng, 1, 4, 2, 2, 4, 3, [4, 4])
+    shifted = [(k, v, s + 100) for (k, v, s) in chunks]
+    out, lse = oracle.attention(q, shifted, 0, True)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse)), "empty rows"
+    st = oracle.ring(q, chunks, q_offset=2, causal=True)
+    before = st.copy()
+    oracle.ring_step(st, q, (chunks[0][0], chunks[0][1], 50), 2, True)
+    for a, b in ((st.m, before.m), (st.l, before.l), (st.O, before.O)):
+        assert np.array_equal(a, b), "future chunk must not touch the state"
+
+
+# --------------------------------------------------------------------------- #
+# exact arithmetic on tiny inputs
+# --------------------------------------------------------------------------- #
+def _mp_attention(q, chunks, q_off, causal, scale):
+    mpmath.mp.dps = 50
+    B, Lq, Hq, dqk = q.shape
+    Hkv, dv = chunks[0][0].shape[2], chunks[0][1].shape[3]
+    K = np.concatenate([c[0] for c in chunks], axis=1)
+    V = np.concatenate([c[1] for c in chunks], axis=1)
+    pos = _positions(chunks)
+    out = np.zeros((B, Lq, Hq, dv))
+    lse = np.zeros((B, Hq, Lq))
+    for b, r, h in itertools.product(range(B), range(Lq), range(Hq)):
+        hk = h // (Hq // Hkv)
+        vis = [t for t in range(K.shape[1]) if (not causal) or pos[t] <= q_off + r]
+        if not vis:
+            lse[b, h, r] = -math.inf
+            continue
+        s = {t: mpmath.fsum(mpmath.mpf(float(q[b, r, h, e])) * mpmath.mpf(float(K[b, t, hk, e]))
+                            for e in range(dqk)) * mpmath.mpf(scale) for t in vis}
+        w = {t: mpmath.exp(s[t]) for t in vis}  # exact: no shift needed
+        z = mpmath.fsum(w.values())
+        for e in range(dv):
+            out[b, r, h, e] = float(mpmath.fsum(w[t] * mpmath.mpf(float(V[b, t, hk, e]))
+                                                for t in vis) / z)
+        lse[b, h, r] = float(mpmath.log(z))
+    return out, lse
+
+
+def pin_exact_mpmath():
+    rng = np.random.default_rng(2024)
+    cases = [
+        (1, 3, 1, 1, 3, 2, [2, 3], 0, False, 1.0),
+        (2, 2, 2, 1, 4, 3, [1, 4, 2], 5, True, 1.0),
+        (1, 4, 4, 2, 2, 2, [3, 3], 2, True, 1.0),
+        (1, 3, 2, 2, 4, 1, [4, 2], 3, True, 40.0),   # logits ~ 1e3: overflow w/o shift
+        (1, 2, 1, 1, 1, 2, [6], 0, False, 60.0),
+    ]
+    for (B, Lq, Hq, Hkv, dqk, dv, lens, q_off, causal, std) in cases:
+        q, chunks = _rand(rng, B, Lq, Hq, Hkv, dqk, dv, lens, std=std)
+        scale = 1.0 / math.sqrt(dqk)
+        out, lse = oracle.attention(q, chunks, q_off, causal)
+        ref, ref_lse = _mp_attention(q, chunks, q_off, causal, scale)
+        _close(out, ref, 1e-13, f"mpmath out {lens} std={std}")
+        _close(lse, ref_lse, 1e-13, f"mpmath lse {lens} std={std}")
+        st = oracle.ring(q, chunks, q_offset=q_off, causal=causal)
+        rout, rlse = oracle.finalize(st)
+        _close(rout, ref, 1e-12, f"mpmath ring out {lens} std={std}")
+        _close(rlse, ref_lse, 1e-12, f"mpmath ring lse {lens} std={std}")
+
+
+# --------------------------------------------------------------------------- #
+# invariants the pages assert
+# --------------------------------------------------------------------------- #
+def _split(n, P, rng=None):
+    """Split n keys into P chunks (ragged when P does not divide n)."""
+    if rng is None:
+        base, rem = divmod(n, P)
+        return [base + (1 if i < rem else 0) for i in range(P)]
+    cuts = sorted(rng.choice(np.arange(1, n), size=P - 1, replace=False))
+    return list(np.diff([0, *cuts, n]))
+
+
+def pin_ring_equals_full():
+    """Ring output equals plain attention for every chunk count P and every
+    order in which the chunks arrive."""
+    rng = np.random.default_rng(5)
+    N = 24
+    B, Lq, Hq, Hkv, dqk, dv = 1, 5, 4, 2, 6, 4
+    q = rng.standard_normal((B, Lq, Hq, dqk)) * 1.5
+    Kall = rng.standard_normal((B, N, Hkv, dqk)) * 1.5
+    Vall = rng.standard_normal((B, N, Hkv, dv))
+    for causal, q_off in ((False, 0), (True, 7), (True, 19)):
+        full, full_lse = oracle.attention(q, [(Kall, Vall, 0)], q_off, causal)
+        for P in (1, 2, 3, 4, 5, 6, 8, 12, 24):
+            lens = _split(N, P)
+            starts = np.cumsum([0, *lens[:-1]])
+            chunks = [(Kall[:, s:s + n], Vall[:, s:s + n], int(s)) for s, n in zip(starts, lens)]
+            orders = (list(itertools.permutations(range(P))) if P <= 4 else
+                      [list(range(P)), list(range(P))[::-1]] +
+                      [list(rng.permutation(P)) for _ in range(4)])
+            for order in orders:
+                st = oracle.ring(q, chunks, order=order, q_offset=q_off, causal=causal)
+                out, lse = oracle.finalize(st)
+                _close(out, full, 1e-12, f"ring P={P} order={order} causal={causal}")
+                _close(lse, full_lse, 1e-12, f"ring lse P={P}")
+        # ragged random splits
+        for _ in range(3):
+            lens = _split(N, 5, rng)
+            starts = np.cumsum([0, *lens[:-1]])
+            chunks = [(Kall[:, s:s + n], Vall[:, s:s + n], int(s)) for s, n in zip(starts, lens)]
+            st = oracle.ring(q, chunks, order=list(rng.permutation(5)), q_offset=q_off,
+                             causal=causal)
+            _close(oracle.finalize(st)[0], full, 1e-12, f"ragged ring {lens}")
+
+
+def pin_merge_laws():
+    """Partial states over disjoint key sets merge into the global softmax:
+    merge is commutative, associative, has the empty state as identity, and
+    state(chunks 0..k-1) merged with state(chunks k..P-1) equals state(all)."""
+    rng = np.random.default_rng(6)
+    q, chunks = _rand(rng, 2, 4, 2, 1, 5, 3, [3, 4, 5, 2], std=2.0)
+    for q_off, causal in ((0, False), (6, True)):
+        parts = [oracle.ring(q, [c], q_offset=q_off, causal=causal) for c in chunks]
+        full, _ = oracle.attention(q, chunks, q_off, causal)
+        ab, ba = oracle.merge(parts[0], parts[1]), oracle.merge(parts[1], parts[0])
+        for x, y in ((ab.m, ba.m), (ab.l, ba.l), (ab.O, ba.O)):
+            assert np.array_equal(x, y), "merge must be commutative"
+        left = oracle.merge(oracle.merge(parts[0], parts[1]), parts[2])
+        right = oracle.merge(parts[0], oracle.merge(parts[1], parts[2]))
+        _close(oracle.finalize(left)[0], oracle.finalize(right)[0], 1e-14, "associative")
+        empty = oracle.State(*parts[0].O.shape)
+        idm = oracle.merge(parts[2], empty)
+        for x, y in ((idm.m, parts[2].m), (idm.l, parts[2].l), (idm.O, parts[2].O)):
+            assert np.array_equal(x, y), "empty state must be the identity"
+        for k in range(1, len(chunks)):
+            a = oracle.ring(q, chunks[:k], q_offset=q_off, causal=causal)
+            b = oracle.ring(q, chunks[k:], q_offset=q_off, causal=causal)
+            _close(oracle.finalize(oracle.merge(a, b))[0], full, 1e-13, f"split at {k}")
+        tot = parts[0]
+        for p in parts[1:]:
+            tot = oracle.merge(tot, p)
+        _close(oracle.finalize(tot)[0], full, 1e-13, "merge of per-chunk states")
+
+
+def pin_causal_future_ignored():
+    """Keys after a query's position do not influence it (token-level causal
+    mask, diagonal included): perturbing them leaves the output bit-identical,
+    perturbing the diagonal key changes it."""
+    rng = np.random.default_rng(13)
+    q, chunks = _rand(rng, 1, 6, 2, 2, 4, 4, [8, 8])
+    q_off = 5  # rows at positions 5..10
+    out, _ = oracle.attention(q, chunks, q_off, True)
+    for r in range(6):
+        p = q_off + r
+        pert = []
+        for (k, v, s) in chunks:
+            k2, v2 = k.copy(), v.copy()
+            sel = (s + np.arange(k.shape[1])) > p
+            k2[:, sel] += 10.0
+            v2[:, sel] -= 7.0
+            pert.append((k2, v2, s))
+        o2, _ = oracle.attention(q, pert, q_off, True, rows=[r])
+        assert np.array_equal(o2[:, 0], out[:, r]), f"future keys changed row {r}"
+        diag = []
+        for (k, v, s) in chunks:
+            v2 = v.copy()
+            sel = (s + np.arange(k.shape[1])) == p
+            v2[:, sel] += 1.0
+            diag.append((k, v2, s))
+        o3, _ = oracle.attention(q, diag, q_off, True, rows=[r])
+        assert not np.allclose(o3[:, 0], out[:, r]), f"diagonal key ignored at row {r}"
+
+
+def pin_rows_and_decode_positions():
+    """Evaluating a subset of rows gives the same values as the full run; a
+    query at cache_idx + t (incremental decode) equals prefill row
+    cache_idx + t of the same sequence."""
+    rng = np.random.default_rng(17)
+    B, N, Hq, Hkv, d = 2, 40, 4, 2, 8
+    Qfull = rng.standard_normal((B, N, Hq, d))
+    K = rng.standard_normal((B, N, Hkv, d))
+    V = rng.standard_normal((B, N, Hkv, d))
+    chunks = [(K[:, :16], V[:, :16], 0), (K[:, 16:32], V[:, 16:32], 16),
+              (K[:, 32:], V[:, 32:], 32)]
+    full, full_lse = oracle.attention(Qfull, chunks, 0, True)
+    rows = [0, 3, 17, 39]
+    sub, sub_lse = oracle.attention(Qfull, chunks, 0, True, rows=rows)
+    assert np.array_equal(sub, full[:, rows]) and np.array_equal(sub_lse, full_lse[:, :, rows])
+    for cache_idx, Lq in ((37, 3), (21, 5), (0, 1)):
+        qd = Qfull[:, cache_idx:cache_idx + Lq]
+        dec, dec_lse = oracle.attention(qd, chunks, cache_idx, True)
+        _close(dec, full[:, cache_idx:cache_idx + Lq], 1e-15, f"decode at {cache_idx}")
+        _close(dec_lse, full_lse[:, :, cache_idx:cache_idx + Lq], 1e-15, "decode lse")
+
+
+def pin_input_types():
+    """bf16 and fp32 inputs are upcast exactly: the oracle on bf16 bit
+    patterns equals the oracle on the same values in float64."""
+    rng = np.random.default_rng(19)
+    q, chunks = _rand(rng, 1, 4, 2, 1, 8, 8, [5, 6])
+    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    qb = to_bf16(q)
+    cb = [(to_bf16(k), to_bf16(v), s) for (k, v, s) in chunks]
+    out_b, _ = oracle.attention(qb, cb, 2, True)
+    c64 = [(k.double().numpy(), v.double().numpy(), s) for (k, v, s) in cb]
+    out_64, _ = oracle.attention(qb.double().numpy(), c64, 2, True)
+    assert np.array_equal(out_b, out_64), "bf16 upcast"
+    qf = torch.from_numpy(q).float()
+    cf = [(torch.from_numpy(k).float(), torch.from_numpy(v).float(), s) for (k, v, s) in chunks]
+    out_f, _ = oracle.attention(qf, cf, 2, True)
+    out_f64, _ = oracle.attention(qf.double().numpy(),
+                                  [(k.double().numpy(), v.double().numpy(), s) for (k, v, s) in cf],
+                                  2, True)
+    assert np.array_equal(out_f, out_f64), "fp32 upcast"
+
+
+ALL_PINS = [
+    pin_library_sdpa,
+    pin_zero_query_mean,
+    pin_constant_values,
+    pin_first_causal_row,
+    pin_two_keys_logistic,
+    pin_hardmax_limit,
+    pin_empty_rows,
+    pin_exact_mpmath,
+    pin_ring_equals_full,
+    pin_merge_laws,
+    pin_causal_future_ignored,
+    pin_rows_and_decode_positions,
+    pin_input_types,
+]

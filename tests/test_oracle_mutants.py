@@ -1,0 +1,76 @@
+"""Plant plausible mistakes in copies of oracle.c and check the pins catch each.
+
+Every mutant is a textual edit of the oracle's C source (a dropped term, a
+wrong sign or index, an off-by-one mask, a misread of the pages), compiled to
+its own library in a temporary directory.  The pin suite of
+``oracle_pins.py`` runs against it; at least one pin must fail.  The real
+oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (id, original text, replacement, how many occurrences to replace: 1 or "all")
+MUTANTS = [
+    ("no_rescale_of_O", "o[e] *= alpha;", "(void)alpha;", 1),
+    ("no_rescale_of_l", "l[st] = alpha * l[st] + psum;", "l[st] = l[st] + psum;", 1),
+    ("strict_causal_diagonal", "return !causal || kpos <= qpos;",
+     "return !causal || kpos < qpos;", 1),
+    ("interleaved_gqa_heads", "int hk = h / (Hq / Hkv);", "int hk = h % Hkv;", "all"),
+    ("q_offset_floored_to_512_chunk", "int64_t qpos = q_offset + r;",
+     "int64_t qpos = (q_offset / 512) * 512 + r;", "all"),
+    ("scale_dropped", "return dot * scale;", "return dot;", 1),
+    ("no_max_shift", "double w = exp(s[t] - mx);", "double w = exp(s[t]);", 1),
+    ("lse_without_max", "*ls = mx + log(sum);", "*ls = log(sum);", 1),
+    ("wrong_query_head", "int64_t qb = (((int64_t)b * Lq + r) * Hq + h) * dqk;",
+     "int64_t qb = (((int64_t)b * Lq + r) * Hq + 0) * dqk;", 1),
+    ("key_index_transposed", "int64_t kb = (((int64_t)b * lenc + j) * Hkv + hk) * dqk;",
+     "int64_t kb = (((int64_t)b * lenc + (lenc - 1 - j)) * Hkv + hk) * dqk;", 1),
+    ("value_of_wrong_chunk_key",
+     "int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;",
+     "int64_t vb = (((int64_t)b * len[c] + (j ? j - 1 : 0)) * Hkv + hk) * dv;", 1),
+    ("only_two_chunks_seen", "for (int c = 0; c < n_chunks; ++c)\n                for (int64_t j = 0; j < len[c]; ++j, ++t) {\n                    if (!visible",
+     "for (int c = 0; c < n_chunks && c < 2; ++c)\n                for (int64_t j = 0; j < len[c]; ++j, ++t) {\n                    if (!visible", 1),
+    ("merge_weight_sign", "double a2 = m2[i] == -INFINITY ? 0.0 : exp(m2[i] - mx);",
+     "double a2 = m2[i] == -INFINITY ? 0.0 : exp(mx - m2[i]);", 1),
+    ("merge_drops_second_l", "l[i] = a1 * l1[i] + a2 * l2[i];", "l[i] = a1 * l1[i] + l2[i];", 1),
+    ("finalize_lse_without_m", "lse[i] = m[i] + log(l[i]);", "lse[i] = log(l[i]);", 1),
+    ("ring_step_alpha_inverted", "double alpha = m[st] == -INFINITY ? 0.0 : exp(m[st] - m_new);",
+     "double alpha = m[st] == -INFINITY ? 0.0 : exp(m_new - m[st]);", 1),
+    ("ring_step_ignores_previous_max", "double m_new = m[st] > cmax ? m[st] : cmax;",
+     "double m_new = cmax;", 1),
+    ("empty_row_nan", "if (mx == -INFINITY) { /* no visible key: output 0 */",
+     "if (0) { /* no visible key: output 0 */", 1),
+    ("bf16_truncated_mantissa", "uint32_t bits = (uint32_t)((const uint16_t *)p)[idx] << 16;",
+     "uint32_t bits = ((uint32_t)((const uint16_t *)p)[idx] << 16) & 0xFFFF0000u & ~0x10000u;", 1),
+]
+
+
+def _mutate(text, old, new, count):
+    n = text.count(old)
+    assert n >= 1, f"snippet not found: {old!r}"
+    if count == 1:
+        assert n == 1, f"snippet not unique ({n}x): {old!r}"
+    return text.replace(old, new)
+
+
+@pytest.mark.parametrize("mid,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, monkeypatch, mid, old, new, count):
+    src = open(SRC).read()
+    mutated = _mutate(src, old, new, count)
+    msrc = tmp_path / "oracle_mut.c"
+    msrc.write_text(mutated)
+    lib_path = oracle.build(force=True, src=str(msrc), out=str(tmp_path / "liboracle_mut.so"))
+    monkeypatch.setattr(oracle, "_lib", oracle.load_library(lib_path))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {mid} passed every pin"
