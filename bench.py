@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of one device's share of ring attention on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+  * prefill workloads: the device's query chunk against every KV chunk in
+    ring order, each received chunk staged through the double buffer on the
+    side stream (RA_FLAG_STAGE), causal chunks skipped/masked, output and
+    normalisation fused;
+  * decode workloads: split-KV partials over the cache, then the merge.
+
+Prints ONE JSON line.  `value` is the headline workload's algorithmic
+TFLOP/s (unmasked query-key pairs x 4 x d per head, no dense-tile flops).
+`roofline` prices the dominant kernel against the bf16 MFMA peak (prefill)
+or HBM bandwidth (decode) with its average launch time from HIP events on the
+launch stream; `cpu_baseline` times the CPU oracle on a bounded row sample of
+the same workload.  `secondary` holds the other workloads timed in the run.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--secondary NAMES]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+HEADLINE = "prefill_bf16_h32_d128"
+SECONDARY = "decode_b4_gqa32x8_cache1m"
+
+
+def visible_pairs_per_head(wl, rows=None):
+    """Unmasked (query, key) pairs of one (batch, head) for the given rows."""
+    rows = range(wl.Lq) if rows is None else rows
+    total = 0
+    for start, n in zip(wl.starts(), wl.lens()):
+        for r in rows:
+            pos = wl.q_offset + r
+            if not wl.causal:
+                total += n
+            else:
+                total += max(0, min(n, pos - start + 1))
+    return total
+
+
+def visible_pairs_fast(wl):
+    """Same as visible_pairs_per_head over all rows, in closed form."""
+    total = 0
+    for start, n in zip(wl.starts(), wl.lens()):
+        if not wl.causal:
+            total += n * wl.Lq
+            continue
+        for_lo = wl.q_offset - start + 1  # visible keys of row 0 (unclipped)
+        # sum over r of clip(for_lo + r, 0, n)
+        r_full = max(0, min(wl.Lq, n - for_lo))  # rows with for_lo + r < n
+        acc = 0
+        # rows 0..r_full-1 contribute max(0, for_lo + r)
+        lo = max(0, -for_lo + 1) if for_lo <= 0 else 0
+        lo = min(lo, r_full)
+        if r_full > lo:
+            a, b = for_lo + lo, for_lo + r_full - 1
+            acc += (a + b) * (r_full - lo) // 2
+        acc += (wl.Lq - r_full) * n
+        total += acc
+    return total
+
+
+def algorithmic(wl):
+    pairs = visible_pairs_fast(wl) * wl.B * wl.Hq
+    flops = pairs * 2 * (wl.d_qk + wl.d_v)
+    es = 2 if wl.dtype == "bf16" else 4
+    kv_bytes = sum(wl.lens()) * wl.B * wl.Hkv * (wl.d_qk + wl.d_v) * es
+    qo_bytes = wl.B * wl.Lq * wl.Hq * (wl.d_qk + wl.d_v) * es
+    return flops, kv_bytes + qo_bytes
+
+
+class WorkloadRun:
+    """Inputs resident on the GPU plus the exact call bench.py times."""
+
+    def __init__(self, name, device="cuda:0"):
+        import torch
+
+        from long_context_blockwise_amd import inputs
+        import long_context_blockwise_amd as ra
+
+        self.ra = ra
+        self.torch = torch
+        self.wl = inputs.WORKLOADS[name]
+        wl = self.wl
+        self.decode = wl.Lq <= 16
+        self.x = inputs.make(wl, device)
+        if self.decode:
+            self.order = list(range(wl.P))
+            self.flags = 0  # split-KV + merge
+        else:
+            dev_index = wl.q_offset // wl.chunk_len  # this device's chunk index
+            self.order = ra.ring_attn_ring_order(dev_index, wl.P)
+            self.flags = ra.RA_FLAG_STAGE
+        self.chunks = self.x.chunks(self.order)
+        self.out = torch.empty((wl.B, wl.Lq, wl.Hq, wl.d_v), device=device, dtype=wl.torch_dtype)
+        ws = ra.ring_attn_workspace_size(self.x.q, self.chunks, wl.causal, wl.q_offset, self.flags)
+        self.ws = torch.empty(max(ws, 1), device=device, dtype=torch.uint8)
+        self.ctx = ra.RingAttnContext(torch.device(device).index or 0)
+        cls = ra.ring_attn_plan(wl.Lq, wl.q_offset, wl.causal, [s for (_, _, s) in self.chunks],
+                                [k.shape[1] for (k, _, _) in self.chunks])
+        computed = sum(1 for c in cls if c != ra.RA_CHUNK_SKIP)
+        # kernel launches of the dominant kernel per step
+        self.launches = 1 if self.decode else computed
+        self.flops, self.bytes = algorithmic(wl)
+
+    def step(self):
+        self.ra.ring_attn_fwd(self.x.q, self.chunks, self.wl.causal, self.wl.q_offset,
+                              flags=self.flags, out=self.out, ctx=self.ctx, workspace=self.ws)
+
+    def time(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            self.step()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = [a.elapsed_time(b) for (a, b) in ev]
+        return wall / steps, sum(ev_ms) / len(ev_ms)
+
+    def result(self, sec_per_step, ev_ms):
+        wl = self.wl
+        tflops = self.flops / sec_per_step / 1e12
+        gbs = self.bytes / sec_per_step / 1e9
+        launch_s = ev_ms / 1e3 / self.launches
+        if self.decode:
+            achieved = self.bytes / self.launches / launch_s / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+            metric, value, unit = "decode HBM GB/s at 1M KV", gbs, "GB/s"
+        else:
+            achieved = self.flops / self.launches / launch_s / 1e12
+            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+                        frac=round(achieved / peak, 4), traffic=None)
+            metric, value, unit = "causal attn fwd TFLOP/s (% MFMA peak) per GPU", tflops, "TFLOP/s"
+        return dict(workload=wl.name, metric=metric, value=round(value, 2), unit=unit,
+                    ms_per_step=round(sec_per_step * 1e3, 4),
+                    tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1),
+                    tflops=round(tflops, 2), gbs=round(gbs, 1),
+                    launches_per_step=self.launches, roofline=roof)
+
+
+def cpu_baseline(name, budget_s=15.0):
+    """Time the CPU oracle on a bounded, stratified row sample of a workload
+    (all heads and batches of the sampled rows) and scale to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from long_context_blockwise_amd import inputs
+
+    wl = inputs.WORKLOADS[name]
+    x = inputs.make(wl, "cpu")
+    chunks = x.chunks()
+    rows_all = inputs.sample_rows(wl.Lq, tile=max(1, wl.Lq // 64), seed=1)
+    rng = np.random.default_rng(0)
+    rng.shuffle(rows_all)
+    n, spent, done_rows, t_total = 1, 0.0, [], 0.0
+    while spent < budget_s / 3 and len(done_rows) < len(rows_all):
+        rows = sorted(rows_all[len(done_rows):len(done_rows) + n])
+        t0 = time.perf_counter()
+        oracle.attention(x.q, chunks, wl.q_offset, wl.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        done_rows += rows
+        t_total += dt
+        spent += dt
+        n *= 2
+    pairs = visible_pairs_per_head(wl, done_rows) * wl.B * wl.Hq
+    flops = pairs * 2 * (wl.d_qk + wl.d_v)
+    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=oracle.threads(),
+                kind="oracle",
+                sample=f"{len(done_rows)} of {wl.Lq} query rows (all {wl.B}x{wl.Hq} batch-heads) of "
+                       f"{wl.name}, fp64 C oracle, {t_total:.1f} s, {flops / 1e9:.1f} GFLOP")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", default=SECONDARY, help="comma list, '' for none")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one device's ring share on one GPU; --gpus must be 1 "
+              "(the multi-GPU ring is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    run = WorkloadRun(args.workload)
+    sec, ev_ms = run.time(args.steps, args.warmup)
+    head = run.result(sec, ev_ms)
+    print(f"[bench] {head}", file=sys.stderr, flush=True)
+    del run
+    torch.cuda.empty_cache()
+
+    secondary = []
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        r = WorkloadRun(name)
+        s2, e2 = r.time(max(3, args.steps // 2), max(1, args.warmup))
+        res = r.result(s2, e2)
+        print(f"[bench] {res}", file=sys.stderr, flush=True)
+        secondary.append(res)
+        del r
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline(args.workload)
+    wl = head
+    from long_context_blockwise_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    line = {
+        "metric": head["metric"],
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk,
+                   "chunk_len": w.chunk_len, "P": w.P, "Lq": w.Lq, "q_offset": w.q_offset,
+                   "causal": w.causal, "tokens_per_s": head["tokens_per_s"],
+                   "gpu": props.name, "cus": props.multi_processor_count},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

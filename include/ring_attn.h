@@ -1,0 +1,207 @@
+/*
+ * ring_attn.h - C ABI of libringattn, one device's share of ring attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What one device computes.  The sequence is cut into chunks; this device
+ * holds one query chunk and attends it to every KV chunk as the chunks come
+ * round the ring, one chunk per step, keeping a running softmax state
+ * (running max m, denominator l, unnormalised output O) that is rescaled and
+ * extended chunk after chunk, so that the final O / l equals
+ * softmax(Q K^T * scale) V over all keys:
+ *   - page "Ring Attention：百万 Token 上下文的秘密", §2.1 分块计算注意力
+ *     (sequence sharding), §2.2 环形通信 (one KV chunk per ring step),
+ *     §2.3 数学正确性 (the result equals plain attention), §3.1 Flash Ring
+ *     Attention (blockwise attention per received chunk) and §3.2
+ *     通信-计算重叠 (the next chunk is received while the current one is
+ *     computed, into a second buffer);
+ *   - page "从百毫秒到百万Token：长上下文推理优化的工程实践", section
+ *     "注意力机制的数学本质与瓶颈" (the definition of attention) and
+ *     "系统架构设计" item 注意力融合层 (partial outputs are normalised into
+ *     one global softmax: ring_attn_merge);
+ *   - page "RingAttention推理优化：cache_idx参数使用与千万级上下文高效推理实践",
+ *     sections "cache_idx的工作原理" and "增量推理实战" (queries of an
+ *     incremental step sit at cache_idx, cache_idx+1, ... of the cached
+ *     sequence: the q_offset argument).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers (HIP global memory on the
+ *     context's device) unless stated otherwise; descriptor structs and
+ *     arrays of them are HOST memory, read only during the call.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory in ring_attn_fwd / ring_attn_merge; scratch space comes
+ *     from the caller's workspace (ring_attn_workspace_size).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued after prior work on `stream`; calls return without waiting
+ *     for the GPU.  A context's side stream joins back into `stream` with
+ *     events before ring_attn_fwd returns.
+ *   - Return value: RA_OK (0) or a negative RA_ERR_* code.  Arguments are
+ *     validated before anything is enqueued: on a validation error nothing
+ *     runs.  ring_attn_last_error() describes the most recent failure of the
+ *     calling thread.  Faults inside kernels surface on a later call or
+ *     synchronisation, as usual for HIP.  NaN/Inf inputs are not checked;
+ *     they propagate.
+ *
+ * Layouts.  Tensors are [B, S, H, d] ("BSHD", token-major as in the pages'
+ * [batch, sequence, dim] convention); the head dimension d is contiguous and
+ * the other three strides are given in ELEMENTS per tensor (all-zero strides
+ * mean dense BSHD).  bf16 tensors need 16-byte aligned base pointers and
+ * strides that are multiples of 8 elements; fp32 tensors need 16-byte
+ * aligned pointers and strides that are multiples of 4 elements.
+ * Softmax state buffers are dense fp32: m and l are [B, Lq, Hq], O is
+ * [B, Lq, Hq, d_v]; m is in natural-log units of the scaled logits, l is
+ * sum(exp(s - m)) and O is sum(exp(s - m) * v), so out = O / l and the
+ * log-sum-exp is m + ln(l).  A row that has seen no key has m = -inf, l = 0,
+ * O = 0 and gets out = 0.
+ *
+ * Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ * Causal masking is per token with the diagonal included: the query at
+ * absolute position p sees the key at absolute position t iff t <= p.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define RA_OK 0
+#define RA_ERR_INVALID_ARG (-1) /* null, negative or inconsistent argument */
+#define RA_ERR_UNSUPPORTED (-2) /* dtype / head size / layout not built    */
+#define RA_ERR_WORKSPACE (-3)   /* workspace missing or too small          */
+#define RA_ERR_HIP (-4)         /* HIP runtime or launch failure           */
+
+/* element types */
+#define RA_F32 0
+#define RA_BF16 1
+
+/* ring_attn_fwd flags */
+#define RA_FLAG_STAGE 1u      /* ring stand-in: copy each received chunk into a
+                                 double buffer on the side stream (see fwd) */
+#define RA_FLAG_SPLIT_KV 2u   /* force the split-KV (decode) schedule        */
+#define RA_FLAG_NO_SPLIT_KV 4u /* force the ring schedule                    */
+#define RA_FLAG_ACCUMULATE 8u /* start from the state in m/l/O instead of an
+                                 empty one (resume / continue a ring)        */
+
+/* chunk classes reported by ring_attn_plan */
+#define RA_CHUNK_SKIP 0 /* every key is after every query: not computed   */
+#define RA_CHUNK_FULL 1 /* every key is visible to every query: no mask   */
+#define RA_CHUNK_DIAG 2 /* some keys are masked for some queries          */
+
+typedef struct ra_desc {
+    int32_t B;     /* batch size                                    */
+    int32_t Hq;    /* query heads                                   */
+    int32_t Hkv;   /* key/value heads; Hq % Hkv == 0                */
+    int32_t d_qk;  /* query/key head size                           */
+    int32_t d_v;   /* value/output head size                        */
+    int32_t dtype; /* RA_F32 or RA_BF16: q, k, v and out            */
+    float scale;   /* logit scale; 0 selects 1/sqrt(d_qk)           */
+    int32_t reserved;
+    int64_t q_strides[3]; /* q   [B, Lq, Hq, d_qk]: (batch, token, head) */
+    int64_t k_strides[3]; /* k   [B, len, Hkv, d_qk], every chunk        */
+    int64_t v_strides[3]; /* v   [B, len, Hkv, d_v],  every chunk        */
+    int64_t o_strides[3]; /* out [B, Lq, Hq, d_v]                        */
+} ra_desc;
+
+typedef struct ra_kv_chunk {
+    const void *k;  /* device pointer to the chunk's keys                  */
+    const void *v;  /* device pointer to the chunk's values                */
+    int64_t start;  /* absolute position of the chunk's first key          */
+    int64_t len;    /* number of keys (ragged chunks allowed; 0 = empty)   */
+} ra_kv_chunk;
+
+typedef struct ra_ctx ra_ctx;
+
+/* Library version string (static storage). */
+const char *ring_attn_version(void);
+
+/* Message of the calling thread's most recent failure ("" if none). */
+const char *ring_attn_last_error(void);
+
+/* Create a context on HIP device `device`: it owns one side stream (default
+ * priority) and the events that pace the double buffer.  No device memory.
+ * RA_ERR_HIP if the device does not exist. */
+int ring_attn_ctx_create(int device, ra_ctx **out);
+int ring_attn_ctx_destroy(ra_ctx *ctx);
+
+/* Order in which ring device `device_index` of `P` meets the KV chunks when
+ * every step receives the chunk of the previous device (page "Ring
+ * Attention：百万 Token 上下文的秘密", §3.1: receive from the left
+ * neighbour, send to the right): its own chunk, then device_index-1,
+ * device_index-2, ... modulo P.  Host only; writes P ints to `order`. */
+int ring_attn_ring_order(int device_index, int P, int32_t *order);
+
+/* Chunk classes for a query chunk of Lq rows at absolute positions
+ * q_offset .. q_offset+Lq-1 (host only): cls[c] = RA_CHUNK_SKIP / FULL /
+ * DIAG for the chunk at starts[c] with lens[c] keys.  Non-causal: all FULL
+ * (empty chunks: SKIP). */
+int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int P,
+                   const int64_t *starts, const int64_t *lens, int32_t *cls);
+
+/* Bytes of device workspace ring_attn_fwd needs for these arguments
+ * (host only; k/v pointers are not read).  0 is a valid answer. */
+int ring_attn_workspace_size(const ra_desc *d, int64_t Lq,
+                             const ra_kv_chunk *chunks, int P, int causal,
+                             int64_t q_offset, uint32_t flags, int want_state,
+                             size_t *bytes);
+
+/* One device's share of ring attention.
+ *
+ *   q          [B, Lq, Hq, d_qk] query chunk (device)
+ *   chunks     P KV chunks (host array of device pointers), processed in
+ *              array order: pass them in ring order (ring_attn_ring_order)
+ *              to mirror a ring; the result does not depend on the order
+ *              beyond rounding.  Chunks must not overlap in position.
+ *   causal     0/1; chunks whose keys all follow every query are skipped
+ *   q_offset   absolute position of query row 0: (query chunk index) x
+ *              (chunk length) in a prefill ring, or cache_idx in
+ *              incremental decoding (no rounding to any chunk size)
+ *   flags      RA_FLAG_*:
+ *                STAGE: the first computed chunk is read in place (the
+ *                  device's own chunk); every later chunk is first copied
+ *                  into one of two workspace buffers on the context's side
+ *                  stream, one step ahead of the compute stream, standing in
+ *                  for the receive from the ring neighbour.  Requires chunks
+ *                  whose (token, head) strides are dense.
+ *                SPLIT_KV / NO_SPLIT_KV: choose the schedule.  By default
+ *                  Lq <= 16 (incremental decoding) uses split-KV: the keys
+ *                  are cut into many ranges computed in parallel, each
+ *                  writing a partial state, then merged.  Otherwise chunks
+ *                  are folded in order into one running state.
+ *                ACCUMULATE: m_out/l_out/O_out hold a state to continue from.
+ *   out        [B, Lq, Hq, d_v] in desc->dtype, or NULL
+ *   m_out, l_out, O_out   fp32 state after the call, or all NULL
+ *   workspace, ws_bytes   device scratch of ring_attn_workspace_size bytes
+ *   stream     hipStream_t
+ * At least one of out / (m_out, l_out, O_out) must be given.
+ * Supported: bf16 with d_qk == d_v in {64, 128, 512}; fp32 with d_qk == d_v
+ * in {64, 128}; RA_ERR_UNSUPPORTED otherwise. */
+int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
+                  const ra_kv_chunk *chunks, int P, int causal,
+                  int64_t q_offset, uint32_t flags, void *out, float *m_out,
+                  float *l_out, float *O_out, void *workspace,
+                  size_t ws_bytes, void *stream);
+
+/* Merge n_parts partial softmax states over disjoint key sets into one (the
+ * fusion layer's global normalisation, page "从百毫秒到百万Token", 系统架构设计,
+ * 注意力融合层):
+ *   m = max_i m_i,  l = sum_i e^(m_i - m) l_i,  O = sum_i e^(m_i - m) O_i,
+ * where a part with m_i = -inf has weight 0.
+ *   m_parts, l_parts  [n_parts, rows] fp32 (device)
+ *   O_parts           [n_parts, rows, d_v] fp32 (device)
+ *   m, l, O           merged state (device, may alias nothing), or all NULL
+ *   out               [rows, d_v] = O / l in out_dtype (RA_F32 / RA_BF16), or NULL
+ * rows is any row count (e.g. B*Lq*Hq for fwd states).  n_parts >= 1. */
+int ring_attn_merge(int n_parts, int64_t rows, int d_v, const float *m_parts,
+                    const float *l_parts, const float *O_parts, float *m,
+                    float *l, float *O, void *out, int out_dtype,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

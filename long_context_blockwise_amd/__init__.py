@@ -1,0 +1,30 @@
+"""One device's share of ring attention on AMD Instinct MI355X (gfx950).
+
+The compute path is ``libringattn.so``: hand-written HIP kernels behind the C
+ABI of ``include/ring_attn.h``.  This package holds its sources (``csrc/``),
+the in-tree build (``build.py``), a thin ctypes binding (``ring_attn.py``)
+and seeded synthetic workload inputs (``inputs.py``).  Importing the package
+does not load the library; the first call does, and fails loudly when the
+library is missing.
+"""
+from .ring_attn import (  # noqa: F401
+    EXPORTS,
+    RA_BF16,
+    RA_CHUNK_DIAG,
+    RA_CHUNK_FULL,
+    RA_CHUNK_SKIP,
+    RA_F32,
+    RA_FLAG_ACCUMULATE,
+    RA_FLAG_NO_SPLIT_KV,
+    RA_FLAG_SPLIT_KV,
+    RA_FLAG_STAGE,
+    RingAttnContext,
+    RingAttnError,
+    ring_attn_fwd,
+    ring_attn_last_error,
+    ring_attn_merge,
+    ring_attn_plan,
+    ring_attn_ring_order,
+    ring_attn_version,
+    ring_attn_workspace_size,
+)

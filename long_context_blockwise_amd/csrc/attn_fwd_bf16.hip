@@ -1,0 +1,491 @@
+// attn_fwd_bf16.hip - blockwise attention of a resident query chunk against
+// KV chunks, bf16 inputs, fp32 accumulation, on CDNA4 (gfx950) MFMA.
+//
+// One workgroup owns a tile of query rows and walks the keys of its chunks in
+// tiles of BN keys, keeping the running softmax state of each row (running
+// max m, denominator l, unnormalised output O) in registers: the per-chunk
+// blockwise ("flash") attention of page "Ring Attention：百万 Token 上下文的秘密",
+// §3.1 Flash Ring Attention, with the query block resident and K/V tiles
+// staged in on-chip memory (LDS here).  The state after a chunk is exactly
+// what the next ring step continues from (§2.3 数学正确性 of the same page).
+//
+// Layout of the work on the matrix cores.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys are the M dimension (A
+// operand read from LDS), the 32 query rows of a wave are N (B operand held in
+// registers for the whole launch), d is the reduction.  In the 32x32 result
+// lane l owns query row l%32 and 16 of the 32 keys (the other 16 sit in lane
+// l^32), so every per-row softmax step is lane-local plus one exchange with
+// the partner lane.  The probabilities of that result are already the B
+// operand of O^T = V^T P^T (keys are the reduction), so P never leaves the
+// registers; V^T is the A operand, read from a transposed copy of the V tile
+// in LDS whose key order matches the result layout.
+//
+// Online softmax (base 2): with c = scale*log2(e), p = exp2(s*c - m_ref).  The
+// reference m_ref only moves when the tile maximum exceeds it by more than 8
+// (a factor 256), so the O/l rescale is rare; p <= 256 keeps fp32/bf16 exact
+// enough and the result is identical in exact arithmetic.  The true running
+// max is tracked alongside and the state is renormalised to it at the end, so
+// the exported m is the running maximum.
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+// The softmax reference moves when a tile max exceeds it by more than this
+// (log2 units): p = exp2(s*c - m_ref) <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
+// each XCD runs a contiguous range of logical tiles (tiles that share K/V then
+// share that XCD's L2).
+__device__ inline int xcd_remap(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, s = bid >> 3;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
+}
+
+// Bank swizzle of the transposed V tile: 16-byte unit u of V^T row d is stored
+// at unit u ^ swz(d).  Reads (8 consecutive rows, same unit) and writes (rows 8
+// apart) both spread over all banks.
+template <int U>
+__device__ inline int vt_swizzle(int d) {
+    if constexpr (U >= 8)
+        return (d ^ (d >> 3)) & 7;
+    else
+        return ((d >> 1) ^ (d >> 3)) & (U - 1);
+}
+
+// Slot of key k (within a tile) in a row of V^T: bits 2 and 3 swapped, so that
+// the 8 keys a lane group needs for one PV k-step are contiguous.
+__device__ inline int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__device__ inline bf16x8 to_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ inline unsigned pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+template <int D, int BN, int NW, int KSPLIT>
+struct Cfg {
+    static constexpr int NT = NW * 64;           // threads
+    static constexpr int ROWW = NW / KSPLIT;     // waves along rows
+    static constexpr int BM = 32 * ROWW;         // query rows per workgroup
+    static constexpr int KW = BN / KSPLIT;       // keys per wave per tile
+    static constexpr int KB = KW / 32;           // 32-key blocks per wave
+    static constexpr int DS = D / 16;            // reduction steps of S^T
+    static constexpr int DB = D / 32;            // 32-wide blocks of O^T
+    static constexpr int KROW = D + 8;           // padded K row in LDS (elements)
+    static constexpr int KTILE = BN * KROW;      // elements
+    static constexpr int VTILE = D * BN;         // elements
+    static constexpr int U = BN / 8;             // 16-byte units per V^T row
+    static constexpr int K_UNITS = BN * (D / 8);
+    static constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
+    static constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 d each
+    static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+    static constexpr int LDS_ELEMS = 2 * (KTILE + VTILE);
+    static_assert(KW % 32 == 0, "each wave needs whole 32-key blocks");
+    static_assert(D % 32 == 0, "head size must be a multiple of 32");
+    // cross-wave merge scratch (KSPLIT > 1) reuses the tile buffers
+    static_assert(KSPLIT == 1 ||
+                      (KSPLIT - 1) * ROWW * 64 * (16 * DB + 2) * 4 <= LDS_ELEMS * 2,
+                  "merge scratch must fit in LDS");
+};
+
+template <int D, int BN, int NW, int KSPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1, D <= 64 ? 2 : 1))) void fwd_bf16_kernel(const FwdArgs a) {
+    using C = Cfg<D, BN, NW, KSPLIT>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wr = w % C::ROWW, wk = w / C::ROWW;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    // ---- which tile of which (batch, KV head, key range) -------------------
+    const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
+    int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int rt = lid % a.n_rowtiles;
+    lid /= a.n_rowtiles;
+    const int split = lid % nsplit;
+    lid /= nsplit;
+    const int hk = lid % a.Hkv;
+    const int b = lid / a.Hkv;
+
+    const int64_t Lq = a.Lq, Lq_pad = a.Lq_pad;
+    const int64_t prow_end = (int64_t)a.G * Lq_pad;
+    int64_t p0;
+    if (Lq_pad % C::BM == 0) {  // one head per tile; heaviest (latest) rows first
+        const int64_t ntt = Lq_pad / C::BM;
+        const int gq = rt % a.G;
+        const int64_t tt = ntt - 1 - rt / a.G;
+        p0 = gq * Lq_pad + tt * C::BM;
+    } else {
+        p0 = (int64_t)rt * C::BM;
+    }
+
+    // token range (for causal skipping) of a run of packed rows
+    auto t_range = [&](int64_t pa, int64_t pb, int64_t &lo, int64_t &hi) {
+        pb = pb < prow_end ? pb : prow_end;
+        --pb;
+        if (pa / Lq_pad == pb / Lq_pad) {
+            lo = pa % Lq_pad;
+            hi = pb % Lq_pad;
+            hi = hi < Lq - 1 ? hi : Lq - 1;
+        } else {
+            lo = 0;
+            hi = Lq - 1;
+        }
+    };
+    int64_t wg_tlo, wg_thi, wv_tlo, wv_thi;
+    t_range(p0, p0 + C::BM, wg_tlo, wg_thi);
+    t_range(p0 + 32 * wr, p0 + 32 * wr + 32, wv_tlo, wv_thi);
+
+    // this lane's query row
+    const int64_t prow = p0 + 32 * wr + l32;
+    const int gq = (int)(prow / Lq_pad);
+    const int64_t t = prow % Lq_pad;
+    const bool row_ok = prow < prow_end && t < Lq;
+    const int h = hk * a.G + gq;
+    const int64_t qpos = a.q_offset + t;
+
+    // ---- resident query fragments (B operand of S^T = K Q^T) ---------------
+    bf16x8 qf[C::DS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + b * a.q_sb + t * a.q_ss + h * a.q_sh + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *(const u32x4 *)(qp + 16 * ds);
+            qf[ds] = to_bf16x8(v);
+        }
+    }
+
+    // ---- running state --------------------------------------------------------
+    f32x16 oacc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = kNegInf, m_true = kNegInf, lsum = 0.f;
+    const int64_t srow = ((int64_t)b * Lq + t) * a.Hq + h;  // state row index
+    if (a.load_state && row_ok && wk == 0) {
+        const float m0 = a.m[srow];
+        m_run = m_true = m0 * kLog2e;
+        lsum = g == 0 ? a.l[srow] : 0.f;
+        const float *op = a.O + srow * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 v = *(const f32x4 *)(op + 32 * db + 8 * i4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) oacc[db][4 * i4 + j] = v[j];
+            }
+    }
+    const float c2 = a.scale_log2;
+
+    // ---- K/V tile staging: global -> registers -> LDS --------------------------
+    u32x4 kreg[C::K_PER_T];
+    u32x4 vreg[C::V_PER_T][4];
+
+    auto load_tile = [&](const uint16_t *kbase, const uint16_t *vbase, int64_t k0, int64_t kend) {
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int u = tid + i * C::NT;
+            const int row = u / (D / 8), col = u % (D / 8);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if ((C::K_UNITS % C::NT == 0 || u < C::K_UNITS) && k0 + row < kend)
+                v = *(const u32x4 *)(kbase + (k0 + row) * a.k_ss + col * 8);
+            kreg[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int u = tid + i * C::NT;
+            const int kq = u / (D / 8), dg = u % (D / 8);
+            const bool uok = C::V_UNITS % C::NT == 0 || u < C::V_UNITS;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t key = k0 + 4 * kq + j;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (uok && key < kend) v = *(const u32x4 *)(vbase + key * a.v_ss + dg * 8);
+                vreg[i][j] = v;
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+        uint16_t *Ks = smem + buf * (C::KTILE + C::VTILE);
+        uint16_t *Vt = Ks + C::KTILE;
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int u = tid + i * C::NT;
+            if (C::K_UNITS % C::NT == 0 || u < C::K_UNITS) {
+                const int row = u / (D / 8), col = u % (D / 8);
+                *(u32x4 *)(Ks + row * C::KROW + col * 8) = kreg[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int u = tid + i * C::NT;
+            if (C::V_UNITS % C::NT == 0 || u < C::V_UNITS) {
+                const int kq = u / (D / 8), dg = u % (D / 8);
+                const int slot = vt_slot(4 * kq);  // 4 keys stay adjacent
+                const int unit = slot >> 3, off = slot & 7;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int d = 8 * dg + x;
+                    const unsigned sel = (x & 1) ? 0x07060302u : 0x05040100u;
+                    u32x2 pr;
+                    pr[0] = __builtin_amdgcn_perm(vreg[i][1][x >> 1], vreg[i][0][x >> 1], sel);
+                    pr[1] = __builtin_amdgcn_perm(vreg[i][3][x >> 1], vreg[i][2][x >> 1], sel);
+                    const int phys = unit ^ vt_swizzle<C::U>(d);
+                    *(u32x2 *)(Vt + d * BN + phys * 8 + off) = pr;
+                }
+            }
+        }
+    };
+
+    // ---- one KV tile for this wave ----------------------------------------------
+    auto compute_tile = [&](int buf, int64_t k0, int64_t kend, int64_t cstart, bool masked) {
+        const uint16_t *Ks = smem + buf * (C::KTILE + C::VTILE);
+        const uint16_t *Vt = Ks + C::KTILE;
+        f32x16 sacc[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+        const uint16_t *kp = Ks + (wk * C::KW + l32) * C::KROW + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds)
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) {
+                const bf16x8 kf = *(const bf16x8 *)(kp + 32 * kb * C::KROW + 16 * ds);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb], 0, 0, 0);
+            }
+        if (masked) {
+            // key index of element i: 8*(i/4) + 4*g + i%4 within its 32-key block
+            const int64_t klim = a.causal ? qpos - cstart : (int64_t)1 << 62;
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t key = k0 + wk * C::KW + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+                    if (key >= kend || key > klim) sacc[kb][i] = kNegInf;
+                }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * c2;
+        m_true = fmaxf(m_true, mt);
+        const bool need = mt > m_run + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? exp2_fast(m_run - mt) : 1.f;
+            m_run = need ? mt : m_run;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mref = m_run == kNegInf ? 0.f : m_run;
+        bf16x8 pf[2 * C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float e0 = exp2_fast(__builtin_fmaf(sacc[kb][8 * hh + 2 * j], c2, -mref));
+                    const float e1 = exp2_fast(__builtin_fmaf(sacc[kb][8 * hh + 2 * j + 1], c2, -mref));
+                    lsum += e0 + e1;
+                    pk[j] = pack_bf16(e0, e1);
+                }
+                pf[2 * kb + hh] = to_bf16x8(pk);
+            }
+#pragma unroll
+        for (int ks = 0; ks < 2 * C::KB; ++ks) {
+            const int unit = ((wk * C::KW + 16 * ks) >> 3) + g;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                const int d = 32 * db + l32;
+                const bf16x8 vf = *(const bf16x8 *)(Vt + d * BN + ((unit ^ vt_swizzle<C::U>(d)) << 3));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- walk the chunks --------------------------------------------------------
+    int c_begin = 0, c_end = a.n_chunks, sub = 0;
+    if (a.split_mode) {
+        c_begin = split / a.n_sub;
+        sub = split % a.n_sub;
+        c_end = c_begin + 1;
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        const ChunkArg ch = a.chunks[c];
+        int64_t kbeg = 0, kend = ch.len;
+        if (a.split_mode) {
+            kbeg = sub * a.sub_len;
+            kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
+        }
+        int64_t kstop = kend;
+        if (a.causal) {
+            const int64_t vis = a.q_offset + wg_thi - ch.start + 1;  // keys < vis can be visible
+            kstop = vis < kstop ? vis : kstop;
+        }
+        if (kstop <= kbeg) continue;  // uniform across the workgroup
+        const int ntiles = (int)((kstop - kbeg + BN - 1) / BN);
+        const uint16_t *kbase = (const uint16_t *)ch.k + b * a.k_sb + hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + b * a.v_sb + hk * a.v_sh;
+
+        load_tile(kbase, vbase, kbeg, kend);
+        store_tile(0);
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int64_t k0 = kbeg + (int64_t)it * BN;
+            if (it + 1 < ntiles) load_tile(kbase, vbase, k0 + BN, kend);
+            // this wave's keys k0 + wk*KW .. + KW-1
+            const int64_t wk0 = k0 + wk * C::KW;
+            const bool skip = a.causal && ch.start + wk0 > a.q_offset + wv_thi;
+            const bool full = wk0 + C::KW <= kend &&
+                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
+            if (!skip) compute_tile(it & 1, k0, kend, ch.start, !full);
+            if (it + 1 < ntiles) store_tile((it + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: combine key-split waves, renormalise, write ------------------
+    if (m_true != kNegInf) {
+        const float alpha = exp2_fast(m_run - m_true);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    if constexpr (KSPLIT > 1) {
+        // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows
+        float *scr = reinterpret_cast<float *>(smem);
+        constexpr int STRIDE = 16 * C::DB + 2;
+        if (wk > 0) {
+            float *p = scr + ((wr * (KSPLIT - 1) + (wk - 1)) * STRIDE) * 64 + lane;
+            p[0] = m_true;
+            p[64] = lsum;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[(2 + 16 * db + i) * 64] = oacc[db][i];
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll 1
+            for (int o = 0; o < KSPLIT - 1; ++o) {
+                const float *p = scr + ((wr * (KSPLIT - 1) + o) * STRIDE) * 64 + lane;
+                const float m1 = p[0], l1 = p[64];
+                const float mn = fmaxf(m_true, m1);
+                if (mn == kNegInf) continue;
+                const float a0 = m_true == kNegInf ? 0.f : exp2_fast(m_true - mn);
+                const float a1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - mn);
+                lsum = a0 * lsum + a1 * l1;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        oacc[db][i] = a0 * oacc[db][i] + a1 * p[(2 + 16 * db + i) * 64];
+                m_true = mn;
+            }
+        }
+        if (wk > 0) return;
+    }
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (!row_ok) return;
+
+    if (a.split_mode || a.store_state) {
+        const int64_t slot_rows = (int64_t)a.B * Lq * a.Hq;
+        float *mp = a.split_mode ? a.pm + (a.part_base + split) * slot_rows : a.m;
+        float *lp = a.split_mode ? a.pl + (a.part_base + split) * slot_rows : a.l;
+        float *Op = a.split_mode ? a.pO + (a.part_base + split) * slot_rows * D : a.O;
+        if (g == 0) {
+            mp[srow] = m_true == kNegInf ? kNegInf : m_true * kLn2;
+            lp[srow] = ltot;
+        }
+        float *op = Op + srow * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                f32x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = oacc[db][4 * i4 + j];
+                *(f32x4 *)(op + 32 * db + 8 * i4) = v;
+            }
+    }
+    if (!a.split_mode && a.store_out) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        uint16_t *op = (uint16_t *)a.out + b * a.o_sb + t * a.o_ss + h * a.o_sh + 4 * g;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                u32x2 v;
+                v[0] = pack_bf16(oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv);
+                v[1] = pack_bf16(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+                *(u32x2 *)(op + 32 * db + 8 * i4) = v;
+            }
+    }
+}
+
+template <int D, int BN, int NW, int KSPLIT>
+hipError_t launch(const FwdArgs &a, hipStream_t s) {
+    using C = Cfg<D, BN, NW, KSPLIT>;
+    const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
+    const int64_t grid = (int64_t)a.B * a.Hkv * nsplit * a.n_rowtiles;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, KSPLIT>), dim3((unsigned)grid), dim3(C::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shapes per head size: (keys per tile, waves, key split of a tile).
+// Prefill: 4 waves x 32 rows = 128 rows per workgroup.  Split (decode): the
+// 64 packed rows of a KV head's query group, two waves per 32 rows, each
+// taking half of every key tile.
+int fwd_bf16_row_tile(int d, bool split_mode) {
+    if (d == 64) return Cfg<64, 64, 4, 1>::BM;
+    if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, 64, 4, 1>::BM;
+    if (d == 512) return Cfg<512, 32, 4, 1>::BM;
+    return 0;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s) {
+    switch (d) {
+    case 64: return launch<64, 64, 4, 1>(a, s);
+    case 128: return split_mode ? launch<128, 64, 4, 2>(a, s) : launch<128, 64, 4, 1>(a, s);
+    case 512: return launch<512, 32, 4, 1>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ra

@@ -1,0 +1,69 @@
+// ra_internal.h - argument blocks shared by the host runtime and the HIP
+// kernels of libringattn.  Not part of the public ABI (include/ring_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// KV chunks one kernel launch can walk (kernel arguments are at most 4 KiB).
+constexpr int kMaxChunks = 64;
+
+struct ChunkArg {
+    const void *k;
+    const void *v;
+    int64_t start;  // absolute position of key 0
+    int64_t len;    // keys in the chunk
+};
+
+// Arguments of the forward kernels (bf16 MFMA and fp32 paths).
+//
+// Query rows are "packed" per KV head: packed row p = g * Lq_pad + t is token
+// t of query head hk * G + g.  Lq_pad == Lq packs the G heads densely
+// (incremental decoding: G heads x a few tokens fill one tile); Lq_pad
+// rounded up to the row tile keeps every tile inside one head (prefill).
+struct FwdArgs {
+    const void *q;
+    void *out;                 // [B, Lq, Hq, d_v] in the input dtype, or null
+    float *m, *l, *O;          // running state [B, Lq, Hq](, d_v), or null
+    float *pm, *pl, *pO;       // split mode: partial states [slot][B, Lq, Hq](, d_v)
+    int64_t q_sb, q_ss, q_sh;  // element strides (batch, token, head)
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_ss, o_sh;
+    int64_t Lq, Lq_pad, q_offset;
+    int64_t sub_len;           // split mode: keys per sub-range of a chunk
+    int B, Hq, Hkv, G;
+    int causal;
+    int load_state;            // start from (m, l, O) instead of empty
+    int store_state;           // write (m, l, O)
+    int store_out;             // write out = O / l
+    int split_mode;            // 0: fold all chunks; 1: one (chunk, sub-range) per workgroup
+    int n_sub;                 // split mode: sub-ranges per chunk
+    int part_base;             // split mode: partial slot of (chunk 0, sub 0)
+    int n_rowtiles;            // row tiles per (batch, KV head)
+    int n_chunks;
+    float scale_log2;          // logit scale * log2(e)
+    ChunkArg chunks[kMaxChunks];
+};
+
+struct MergeArgs {
+    const float *pm, *pl, *pO;  // [n, rows](, d_v)
+    float *m, *l, *O;           // merged state or null
+    void *out;                  // [rows, d_v] or null
+    int64_t rows;
+    int n_parts;
+    int d_v;
+    int out_bf16;
+};
+
+// Launchers (defined next to their kernels).  They return hipSuccess or the
+// launch error; bm_out reports the row tile the kernel uses.
+int fwd_bf16_row_tile(int d, bool split_mode);
+hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s);
+int fwd_f32_row_tile(int d);
+hipError_t launch_fwd_f32(const FwdArgs &a, int d, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,283 @@
+"""Thin ctypes binding of libringattn (include/ring_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels of ``libringattn.so``.  PyTorch supplies device memory and streams.
+The functions keep the C names; tensors are torch CUDA (HIP) tensors in the
+[B, S, H, d] layout, chunks are ``(k, v, start)`` tuples.
+
+If the library is missing or cannot be loaded every call raises
+:class:`RingAttnError` -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libringattn.so")
+
+RA_OK = 0
+RA_ERR_INVALID_ARG = -1
+RA_ERR_UNSUPPORTED = -2
+RA_ERR_WORKSPACE = -3
+RA_ERR_HIP = -4
+RA_F32, RA_BF16 = 0, 1
+RA_FLAG_STAGE = 1
+RA_FLAG_SPLIT_KV = 2
+RA_FLAG_NO_SPLIT_KV = 4
+RA_FLAG_ACCUMULATE = 8
+RA_CHUNK_SKIP, RA_CHUNK_FULL, RA_CHUNK_DIAG = 0, 1, 2
+
+EXPORTS = ("ring_attn_version", "ring_attn_last_error", "ring_attn_ctx_create",
+           "ring_attn_ctx_destroy", "ring_attn_ring_order", "ring_attn_plan",
+           "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge")
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"ring_attn error {code}: {msg}")
+        self.code = code
+
+
+class ra_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
+                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3)]
+
+
+class ra_kv_chunk(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("start", ctypes.c_int64),
+                ("len", ctypes.c_int64)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libringattn (once) and declare the C signatures."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RingAttnError(RA_ERR_HIP, f"{path} is missing: build it with "
+                                "`python -m long_context_blockwise_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.ring_attn_version.restype = ctypes.c_char_p
+        lib.ring_attn_last_error.restype = ctypes.c_char_p
+        lib.ring_attn_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
+        lib.ring_attn_ctx_destroy.argtypes = [vp]
+        lib.ring_attn_ring_order.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i32)]
+        lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64),
+                                       ctypes.POINTER(i64), ctypes.POINTER(i32)]
+        lib.ring_attn_workspace_size.argtypes = [ctypes.POINTER(ra_desc), i64, ctypes.POINTER(ra_kv_chunk),
+                                                 ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32,
+                                                 ctypes.c_int, ctypes.POINTER(sz)]
+        lib.ring_attn_fwd.argtypes = [vp, ctypes.POINTER(ra_desc), vp, i64, ctypes.POINTER(ra_kv_chunk),
+                                      ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp,
+                                      vp, sz, vp]
+        lib.ring_attn_merge.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_int, vp]
+        for name in ("ring_attn_ctx_create", "ring_attn_ctx_destroy", "ring_attn_ring_order",
+                     "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != RA_OK:
+        raise RingAttnError(rc, load().ring_attn_last_error().decode(errors="replace"))
+
+
+def ring_attn_version() -> str:
+    return load().ring_attn_version().decode()
+
+
+def ring_attn_last_error() -> str:
+    return load().ring_attn_last_error().decode(errors="replace")
+
+
+def ring_attn_ring_order(device_index: int, P: int) -> List[int]:
+    arr = (ctypes.c_int32 * max(P, 1))()
+    _check(load().ring_attn_ring_order(device_index, P, arr))
+    return list(arr)[:P]
+
+
+def ring_attn_plan(Lq: int, q_offset: int, causal: bool, starts: Sequence[int],
+                   lens: Sequence[int]) -> List[int]:
+    P = len(starts)
+    st = (ctypes.c_int64 * max(P, 1))(*starts)
+    ln = (ctypes.c_int64 * max(P, 1))(*lens)
+    cls = (ctypes.c_int32 * max(P, 1))()
+    _check(load().ring_attn_plan(Lq, q_offset, int(bool(causal)), P, st, ln, cls))
+    return list(cls)[:P]
+
+
+class RingAttnContext:
+    """Owns a side stream and the double-buffer events on one device."""
+
+    def __init__(self, device: int = 0):
+        self.device = device
+        h = ctypes.c_void_p()
+        _check(load().ring_attn_ctx_create(device, ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            load().ring_attn_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_ctx_cache = {}
+
+
+def default_context(device: int) -> RingAttnContext:
+    if device not in _ctx_cache:
+        _ctx_cache[device] = RingAttnContext(device)
+    return _ctx_cache[device]
+
+
+# --------------------------------------------------------------------------- #
+# descriptor marshalling
+# --------------------------------------------------------------------------- #
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise RingAttnError(RA_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _strides(t) -> Tuple[int, int, int]:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise RingAttnError(RA_ERR_INVALID_ARG, "tensors must be [B, S, H, d] with d contiguous")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]:
+    """ra_desc and the ra_kv_chunk array for a query tensor and (k, v, start) chunks."""
+    B, Lq, Hq, dqk = q.shape
+    if not chunks:
+        raise RingAttnError(RA_ERR_INVALID_ARG, "at least one chunk is needed to know Hkv/d_v")
+    k0, v0 = chunks[0][0], chunks[0][1]
+    d = ra_desc()
+    d.B, d.Hq, d.Hkv, d.d_qk, d.d_v = B, Hq, k0.shape[2], dqk, v0.shape[3]
+    d.dtype = _dtype_code(q)
+    d.scale = float(scale)
+    d.q_strides[:] = _strides(q)
+    if out is not None:
+        d.o_strides[:] = _strides(out)
+    dense = all(k.is_contiguous() and v.is_contiguous() for (k, v, _) in chunks)
+    if not dense:
+        ks, vs = _strides(k0), _strides(v0)
+        for (k, v, _) in chunks:
+            if _strides(k) != ks or _strides(v) != vs:
+                raise RingAttnError(RA_ERR_INVALID_ARG, "non-contiguous chunks must share strides")
+        d.k_strides[:] = ks
+        d.v_strides[:] = vs
+    arr = (ra_kv_chunk * len(chunks))()
+    for i, (k, v, start) in enumerate(chunks):
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise RingAttnError(RA_ERR_INVALID_ARG, "q, k and v must share a dtype")
+        arr[i].k = k.data_ptr()
+        arr[i].v = v.data_ptr()
+        arr[i].start = int(start)
+        arr[i].len = int(k.shape[1])
+    return d, arr
+
+
+def ring_attn_workspace_size(q, chunks, causal: bool = False, q_offset: int = 0, flags: int = 0,
+                             want_state: bool = False, scale: float = 0.0) -> int:
+    d, arr = make_desc(q, chunks, scale)
+    n = ctypes.c_size_t()
+    _check(load().ring_attn_workspace_size(ctypes.byref(d), q.shape[1], arr, len(chunks),
+                                           int(bool(causal)), int(q_offset), int(flags),
+                                           int(bool(want_state)), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: int = 0,
+                  out=None, state=None, want_out: bool = True, want_state: bool = False,
+                  scale: float = 0.0, ctx: Optional[RingAttnContext] = None, workspace=None,
+                  stream=None):
+    """One device's share of ring attention; returns ``(out, state)``.
+
+    ``state`` (if given) is a tuple ``(m, l, O)`` of fp32 tensors ``[B, Lq, Hq]``,
+    ``[B, Lq, Hq]``, ``[B, Lq, Hq, d_v]`` that receives the softmax state (and
+    supplies the starting state with ``RA_FLAG_ACCUMULATE``); with
+    ``want_state`` and no ``state`` the binding allocates it.
+    """
+    import torch
+
+    B, Lq, Hq, _ = q.shape
+    dv = chunks[0][1].shape[3]
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if out is None and want_out:
+        out = torch.empty((B, Lq, Hq, dv), device=q.device, dtype=q.dtype)
+    if state is None and want_state:
+        state = (torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
+                 torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
+                 torch.empty((B, Lq, Hq, dv), device=q.device, dtype=torch.float32))
+    d, arr = make_desc(q, chunks, scale, out)
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.ring_attn_workspace_size(ctypes.byref(d), Lq, arr, len(chunks), int(bool(causal)),
+                                        int(q_offset), int(flags), int(state is not None),
+                                        ctypes.byref(n)))
+    ws_bytes = int(n.value)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    if ctx is None:
+        ctx = default_context(dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    m, l, O = state if state is not None else (None, None, None)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(lib.ring_attn_fwd(ctx.handle, ctypes.byref(d), q.data_ptr(), Lq, arr, len(chunks),
+                             int(bool(causal)), int(q_offset), int(flags), ptr(out), ptr(m), ptr(l),
+                             ptr(O), ptr(workspace) if ws_bytes else None,
+                             ws_bytes if ws_bytes else 0, stream.cuda_stream))
+    return out, state
+
+
+def ring_attn_merge(m_parts, l_parts, O_parts, out_dtype=None, *, out=None, state=None,
+                    want_out: bool = True, want_state: bool = False, stream=None):
+    """Merge stacked partial states ``[n, rows]``/``[n, rows, d_v]``; returns ``(out, state)``."""
+    import torch
+
+    n, rows, dv = O_parts.shape
+    if out_dtype is None:
+        out_dtype = torch.float32
+    if out is None and want_out:
+        out = torch.empty((rows, dv), device=O_parts.device, dtype=out_dtype)
+    if state is None and want_state:
+        state = (torch.empty(rows, device=O_parts.device, dtype=torch.float32),
+                 torch.empty(rows, device=O_parts.device, dtype=torch.float32),
+                 torch.empty((rows, dv), device=O_parts.device, dtype=torch.float32))
+    for t in (m_parts, l_parts, O_parts):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise RingAttnError(RA_ERR_INVALID_ARG, "partials must be contiguous fp32")
+    if stream is None:
+        stream = torch.cuda.current_stream(O_parts.device)
+    m, l, O = state if state is not None else (None, None, None)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    code = RA_BF16 if (out is not None and out.dtype == torch.bfloat16) else RA_F32
+    _check(load().ring_attn_merge(n, rows, dv, m_parts.data_ptr(), l_parts.data_ptr(),
+                                  O_parts.data_ptr(), ptr(m), ptr(l), ptr(O), ptr(out), code,
+                                  stream.cuda_stream))
+    return out, state

@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-only logic (ring order, chunk classes,
+workspace sizing, argument validation) behaves as documented.  No kernel is
+launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_blockwise_amd as ra
+from long_context_blockwise_amd import ring_attn as rb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rb.LIB_PATH):
+        from long_context_blockwise_amd import build
+
+        build.build()
+    return rb.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ring_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(ra.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert "gfx950" in ra.ring_attn_version()
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 7, 32])
+def test_ring_order_receives_from_previous_device(lib, P):
+    for i in range(P):
+        order = ra.ring_attn_ring_order(i, P)
+        assert order[0] == i
+        assert sorted(order) == list(range(P))
+        # step s+1 holds the chunk device i-1 held at step s
+        for s in range(P - 1):
+            prev = ra.ring_attn_ring_order((i - 1) % P, P)
+            assert order[s + 1] == prev[s]
+
+
+def test_ring_order_rejects_bad_args(lib):
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_ring_order(4, 4)
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_ring_order(0, 0)
+
+
+def _brute_class(Lq, q_off, causal, start, n):
+    if n == 0 or Lq == 0:
+        return ra.RA_CHUNK_SKIP
+    vis = [[(not causal) or (start + j <= q_off + r) for j in range(n)] for r in range(Lq)]
+    if not any(any(row) for row in vis):
+        return ra.RA_CHUNK_SKIP
+    if all(all(row) for row in vis):
+        return ra.RA_CHUNK_FULL
+    return ra.RA_CHUNK_DIAG
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_plan_matches_brute_force(lib, causal):
+    starts = [0, 5, 9, 20, 21, 30]
+    lens = [5, 4, 11, 1, 9, 0]
+    for Lq in (1, 3, 8):
+        for q_off in (0, 4, 5, 8, 9, 19, 20, 29, 35):
+            got = ra.ring_attn_plan(Lq, q_off, causal, starts, lens)
+            want = [_brute_class(Lq, q_off, causal, s, n) for s, n in zip(starts, lens)]
+            assert got == want, (Lq, q_off)
+
+
+def test_plan_of_the_prefill_share():
+    # query chunk 3 of 4 x 8192, causal: 0..2 unmasked, 3 on the diagonal
+    cls = ra.ring_attn_plan(8192, 3 * 8192, True, [0, 8192, 16384, 24576], [8192] * 4)
+    assert cls == [ra.RA_CHUNK_FULL] * 3 + [ra.RA_CHUNK_DIAG]
+    # decode: 16 tokens at cache_idx 1048560 against 64 x 16384
+    cls = ra.ring_attn_plan(16, 1048560, True, [16384 * i for i in range(64)], [16384] * 64)
+    assert cls == [ra.RA_CHUNK_FULL] * 63 + [ra.RA_CHUNK_DIAG]
+
+
+def _desc(B=1, Hq=4, Hkv=2, d=128, dtype=ra.RA_BF16):
+    x = rb.ra_desc()
+    x.B, x.Hq, x.Hkv, x.d_qk, x.d_v, x.dtype = B, Hq, Hkv, d, d, dtype
+    return x
+
+
+def _chunks(lens, start=0):
+    arr = (rb.ra_kv_chunk * len(lens))()
+    s = start
+    for i, n in enumerate(lens):
+        arr[i].k = arr[i].v = 1 << 12
+        arr[i].start, arr[i].len = s, n
+        s += n
+    return arr
+
+
+def _ws(lib, d, Lq, arr, P, causal, q_off, flags, want_state):
+    n = ctypes.c_size_t()
+    rc = lib.ring_attn_workspace_size(ctypes.byref(d), Lq, arr, P, causal, q_off, flags, want_state,
+                                      ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size(lib):
+    d = _desc(B=2, Hq=4, Hkv=2, d=128)
+    arr = _chunks([64, 64, 64])
+    # in place, one launch, caller keeps no state: nothing needed
+    assert _ws(lib, d, 64, arr, 3, 0, 0, 0, 0) == (0, 0)
+    # staged: two buffers of K+V of the largest received chunk, plus the running state
+    rc, n = _ws(lib, d, 64, arr, 3, 0, 0, ra.RA_FLAG_STAGE, 0)
+    stage = 2 * 64 * 2 * 128 * 2 * 2  # B * len * Hkv * (dk + dv) * 2 bytes
+    state = 2 * 64 * 4 * (128 + 2) * 4
+    assert rc == 0 and n == 2 * stage + state
+    rc, n2 = _ws(lib, d, 64, arr, 3, 0, 0, ra.RA_FLAG_STAGE, 1)
+    assert rc == 0 and n2 == 2 * stage
+    # split-KV (decode): partial states
+    rc, n3 = _ws(lib, d, 4, arr, 3, 0, 0, 0, 1)
+    assert rc == 0 and n3 > 0 and n3 % (2 * 4 * 4 * (128 + 2) * 4) == 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: setattr(d, "Hkv", 3), rb.RA_ERR_INVALID_ARG),
+    (lambda d: setattr(d, "B", 0), rb.RA_ERR_INVALID_ARG),
+    (lambda d: setattr(d, "dtype", 7), rb.RA_ERR_INVALID_ARG),
+    (lambda d: setattr(d, "d_qk", 96), rb.RA_ERR_UNSUPPORTED),
+    (lambda d: (setattr(d, "d_qk", 256), setattr(d, "d_v", 256)), rb.RA_ERR_UNSUPPORTED),
+    (lambda d: setattr(d, "scale", -1.0), rb.RA_ERR_INVALID_ARG),
+    (lambda d: d.q_strides.__setitem__(1, 3), rb.RA_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(lib, mutate, code):
+    d = _desc()
+    mutate(d)
+    rc, _ = _ws(lib, d, 16, _chunks([32]), 1, 0, 0, 0, 0)
+    assert rc == code
+    assert lib.ring_attn_last_error()
+
+
+def test_fp32_head_sizes(lib):
+    assert _ws(lib, _desc(d=64, dtype=ra.RA_F32), 8, _chunks([8]), 1, 0, 0, 0, 1)[0] == 0
+    assert _ws(lib, _desc(d=512, dtype=ra.RA_F32), 8, _chunks([8]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_UNSUPPORTED
+
+
+def test_chunk_validation(lib):
+    d = _desc()
+    arr = _chunks([32, 32])
+    arr[1].start = 16  # overlaps chunk 0
+    assert _ws(lib, d, 8, arr, 2, 0, 0, 0, 0)[0] == rb.RA_ERR_INVALID_ARG
+    arr = _chunks([32])
+    arr[0].len = -1
+    assert _ws(lib, d, 8, arr, 1, 0, 0, 0, 0)[0] == rb.RA_ERR_INVALID_ARG
+    assert _ws(lib, d, 8, _chunks([8]), 1, 0, -1, 0, 0)[0] == rb.RA_ERR_INVALID_ARG
+    assert _ws(lib, d, 8, _chunks([8]), 1, 0, 0, 0x40, 0)[0] == rb.RA_ERR_INVALID_ARG
+    both = ra.RA_FLAG_SPLIT_KV | ra.RA_FLAG_STAGE
+    assert _ws(lib, d, 8, _chunks([8]), 1, 0, 0, both, 0)[0] == rb.RA_ERR_INVALID_ARG
+
+
+def test_fwd_rejects_null_context_before_enqueueing(lib):
+    d = _desc()
+    rc = lib.ring_attn_fwd(None, ctypes.byref(d), 1 << 12, 8, _chunks([8]), 1, 0, 0, 0, 1 << 12,
+                           None, None, None, None, 0, None)
+    assert rc == rb.RA_ERR_INVALID_ARG
+
+
+def test_merge_validation(lib):
+    assert lib.ring_attn_merge(0, 4, 128, 1 << 12, 1 << 12, 1 << 12, None, None, None, 1 << 12, 0,
+                               None) == rb.RA_ERR_INVALID_ARG
+    assert lib.ring_attn_merge(1, 4, 6, 1 << 12, 1 << 12, 1 << 12, None, None, None, 1 << 12, 0,
+                               None) == rb.RA_ERR_INVALID_ARG
+    # only some of m, l, O
+    assert lib.ring_attn_merge(1, 4, 8, 1 << 12, 1 << 12, 1 << 12, 1 << 12, None, None, None, 0,
+                               None) == rb.RA_ERR_INVALID_ARG
+
+
+def test_context_needs_a_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    assert lib.ring_attn_ctx_create(0, ctypes.byref(h)) == rb.RA_ERR_HIP
