@@ -48,6 +48,11 @@ constexpr float kRescaleThreshold = 8.0f;
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of x over lanes l and l^32 (the two lanes that share a query row).
+// (v_permlane32_swap with both operands equal is folded by the compiler to a
+// single result, losing the other half, so the exchange uses ds_bpermute.)
+__device__ inline float max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
 // Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
 // each XCD runs a contiguous range of logical tiles (tiles that share K/V then
 // share that XCD's L2).
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_pair(mx);
         const float mt = mx * c2;
         m_true = fmaxf(m_true, mt);
         const bool need = mt > m_run + kRescaleThreshold;

@@ -390,6 +390,7 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     Strides st;
     int rc = check_desc(d, Lq, &st);
     if (rc) return rc;
+    if (Lq == 0) return RA_OK;  // nothing to compute or write
     const bool have_state = m_out || l_out || O_out;
     if (have_state && !(m_out && l_out && O_out))
         return fail(RA_ERR_INVALID_ARG, "m_out, l_out and O_out must be given together");
@@ -409,7 +410,6 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total, ws_bytes);
     if (pl.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
         return fail(RA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-    if (Lq == 0) return RA_OK;
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return fail(RA_ERR_HIP, "hipSetDevice(%d) failed", ctx->device);

@@ -70,18 +70,17 @@ def kv_slice(chunks, hk):
 
 def sampled_reference(q, chunks, q_offset, causal, rows, kv_heads, batches=None):
     """Oracle values for the given rows, for the query heads of the given KV
-    heads (and batches): returns {(b, hk): out [1, n_rows, G, d_v]}."""
+    heads (and batches): returns {(b, hk): out [1, n_rows, G, d_v]}.  Slices
+    are cut on the device and only they are copied to the host."""
     B, _, Hq, _ = q.shape
     Hkv = chunks[0][0].shape[2]
     G = Hq // Hkv
     res = {}
-    qh = q.cpu()
-    hc = to_host(chunks)
     for b in (range(B) if batches is None else batches):
         for hk in kv_heads:
-            qs = group_slice(qh[b:b + 1], hk, G).contiguous()
-            cs = [(k[b:b + 1, :, hk:hk + 1].contiguous(), v[b:b + 1, :, hk:hk + 1].contiguous(), s)
-                  for (k, v, s) in hc]
+            qs = q[b:b + 1, :, hk * G:(hk + 1) * G].cpu().contiguous()
+            cs = [(k[b:b + 1, :, hk:hk + 1].cpu().contiguous(), v[b:b + 1, :, hk:hk + 1].cpu().contiguous(), s)
+                  for (k, v, s) in chunks]
             out, _ = oracle.attention(qs, cs, q_offset, causal, rows=rows)
             res[(b, hk)] = out
     return res

@@ -1,0 +1,54 @@
+"""The five workloads at full size, in the launch configuration bench.py
+times (bench.WorkloadRun: staged ring for prefill shares, split-KV + merge
+for decoding), checked against the oracle on sampled outputs the oracle
+computes row by row: stratified query rows (one per tile plus tile and
+chunk boundaries) for a subset of (batch, KV head) groups, every query head
+of each group."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from parity import check, gather_sampled, sampled_reference
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from long_context_blockwise_amd import inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # workload: (row tile of the sample, KV heads, batches)
+    "tiny_ring_fp32": (1, [0], None),
+    "prefill_bf16_h32_d128": (512, list(range(0, 32, 3)), None),
+    "ring_1m_gqa32x8_d128": (4096, [0, 5], None),
+    "mla_h16_d512": (1024, [0], None),
+    "decode_b4_gqa32x8_cache1m": (1, [0, 7], [0, 3]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_workload_full_size(name):
+    tile, kv_heads, batches = CASES[name]
+    print(f"[workload] {name}", flush=True)
+    run = bench.WorkloadRun(name)
+    wl = run.wl
+    run.step()
+    run.step()  # second call reuses staging buffers and events
+    torch.cuda.synchronize()
+    if tile == 1:
+        rows = list(range(wl.Lq))
+    else:
+        rows = inputs.sample_rows(wl.Lq, tile=tile, seed=3,
+                                  extra=(wl.Lq - 64, wl.Lq - 65, 8191, 8192, 16383, 16384))
+    ref = sampled_reference(run.x.q, run.x.chunks(), wl.q_offset, wl.causal, rows, kv_heads, batches)
+    G = wl.Hq // wl.Hkv
+    got = np.concatenate([gather_sampled(run.out, rows, b, hk, G) for (b, hk) in ref])
+    want = np.concatenate(list(ref.values()))
+    e = check(got, want, wl.dtype, name)
+    print(f"[workload] {name}: {e}", flush=True)
+    del run
+    torch.cuda.empty_cache()
