@@ -9,21 +9,27 @@
 // staged in on-chip memory (LDS here).  The state after a chunk is exactly
 // what the next ring step continues from (§2.3 数学正确性 of the same page).
 //
-// Layout of the work on the matrix cores.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys are the M dimension (A
-// operand read from LDS), the 32 query rows of a wave are N (B operand held in
-// registers for the whole launch), d is the reduction.  In the 32x32 result
-// lane l owns query row l%32 and 16 of the 32 keys (the other 16 sit in lane
-// l^32), so every per-row softmax step is lane-local plus one exchange with
-// the partner lane.  The probabilities of that result are already the B
-// operand of O^T = V^T P^T (keys are the reduction), so P never leaves the
-// registers; V^T is the A operand, read from a transposed copy of the V tile
-// in LDS whose key order matches the result layout.
+// Data movement.  K and V tiles go from HBM straight into LDS with
+// buffer_load ... lds (no registers, no VALU); the buffer descriptor covers
+// only the valid keys, so a ragged tail is zero-filled by the hardware.  Both
+// tiles stay row-major ([key][d]) with the 16-byte units of row r stored at
+// unit ^ swz(r), which makes the two read patterns below bank-conflict free.
+// Tiles are double buffered: tile t+1 is requested before tile t is computed.
+//
+// Matrix cores.  Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: keys are M (A operand, ds_read_b128 from LDS),
+// the wave's 32 query rows are N (B operand, registers for the whole launch).
+// In the 32x32 result lane l owns query row l%32 and 16 of the 32 keys (the
+// rest sit in lane l^32), so each per-row softmax step is lane-local plus one
+// exchange with the partner lane.  The probabilities in that layout are
+// already the B operand of O^T = V^T P^T; the V^T A operand is read from the
+// row-major V tile with ds_read_b64_tr_b16 (4x4 transposes within each 16
+// lanes), in the key order the result layout dictates.
 //
 // Online softmax (base 2): with c = scale*log2(e), p = exp2(s*c - m_ref).  The
-// reference m_ref only moves when the tile maximum exceeds it by more than 8
-// (a factor 256), so the O/l rescale is rare; p <= 256 keeps fp32/bf16 exact
-// enough and the result is identical in exact arithmetic.  The true running
+// reference m_ref only moves when a tile maximum exceeds it by more than 8
+// (a factor 256), so the O/l rescale is rare; p <= 256 is harmless in fp32 and
+// bf16, and the result is identical in exact arithmetic.  The true running
 // max is tracked alongside and the state is renormalised to it at the end, so
 // the exported m is the running maximum.
 #include "ra_internal.h"
@@ -38,6 +44,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
@@ -45,6 +55,8 @@ constexpr float kLog2e = 1.442695040888963407f;
 // The softmax reference moves when a tile max exceeds it by more than this
 // (log2 units): p = exp2(s*c - m_ref) <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+// gfx9 buffer descriptor word 3 for raw (untyped) dword access
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -62,26 +74,29 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
 }
 
-// Bank swizzle of the transposed V tile: 16-byte unit u of V^T row d is stored
-// at unit u ^ swz(d).  Reads (8 consecutive rows, same unit) and writes (rows 8
-// apart) both spread over all banks.
-template <int U>
-__device__ inline int vt_swizzle(int d) {
-    if constexpr (U >= 8)
-        return (d ^ (d >> 3)) & 7;
-    else
-        return ((d >> 1) ^ (d >> 3)) & (U - 1);
-}
-
-// Slot of key k (within a tile) in a row of V^T: bits 2 and 3 swapped, so that
-// the 8 keys a lane group needs for one PV k-step are contiguous.
-__device__ inline int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Swizzle of the 16-byte units of LDS row r (key r of a tile): unit u is
+// stored at u ^ swz(r).  Eight consecutive rows read at one unit (K fragment
+// reads) land on 8 distinct units, and the 4 rows x 2 units of one transposed
+// V read do too.
+__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 __device__ inline bf16x8 to_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ inline unsigned pack_bf16(float a, float b) {
     f32x2 v = {a, b};
     return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ inline bf16x8 lds_read_b128(const char *smem, int byte) {
+    return *reinterpret_cast<const bf16x8 *>(smem + byte);
+}
+
+// Two transposed 4-key reads make one V^T A-operand fragment.
+__device__ inline bf16x8 lds_read_vt(const char *smem, int byte0, int byte1) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(smem + byte0));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(smem + byte1));
+    const s16x8 xy = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, xy);
 }
 
 template <int D, int BN, int NW, int KSPLIT>
@@ -93,27 +108,25 @@ struct Cfg {
     static constexpr int KB = KW / 32;           // 32-key blocks per wave
     static constexpr int DS = D / 16;            // reduction steps of S^T
     static constexpr int DB = D / 32;            // 32-wide blocks of O^T
-    static constexpr int KROW = D + 8;           // padded K row in LDS (elements)
-    static constexpr int KTILE = BN * KROW;      // elements
-    static constexpr int VTILE = D * BN;         // elements
-    static constexpr int U = BN / 8;             // 16-byte units per V^T row
-    static constexpr int K_UNITS = BN * (D / 8);
-    static constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
-    static constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 d each
-    static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-    static constexpr int LDS_ELEMS = 2 * (KTILE + VTILE);
+    static constexpr int ROWB = D * 2;           // bytes per K/V row in LDS
+    static constexpr int UPR = D / 8;            // 16-byte units per row
+    static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
+    static constexpr int BUF = 2 * TILE;         // K + V
+    static constexpr int LDS = 2 * BUF;          // double buffered
+    static constexpr int LOADS = TILE / 1024;    // 1 KiB wave loads per K (or V) tile
+    static constexpr int LOADS_PER_WAVE = LOADS / NW;
     static_assert(KW % 32 == 0, "each wave needs whole 32-key blocks");
-    static_assert(D % 32 == 0, "head size must be a multiple of 32");
-    // cross-wave merge scratch (KSPLIT > 1) reuses the tile buffers
-    static_assert(KSPLIT == 1 ||
-                      (KSPLIT - 1) * ROWW * 64 * (16 * DB + 2) * 4 <= LDS_ELEMS * 2,
+    static_assert(D % 64 == 0, "head size must be a multiple of 64");
+    static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+    static_assert(KSPLIT == 1 || (KSPLIT - 1) * ROWW * 64 * (16 * DB + 2) * 4 <= LDS,
                   "merge scratch must fit in LDS");
 };
 
 template <int D, int BN, int NW, int KSPLIT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1, D <= 64 ? 2 : 1))) void fwd_bf16_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
+void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -203,82 +216,69 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64
     }
     const float c2 = a.scale_log2;
 
-    // ---- K/V tile staging: global -> registers -> LDS --------------------------
-    u32x4 kreg[C::K_PER_T];
-    u32x4 vreg[C::V_PER_T][4];
+    // ---- per-lane LDS addresses (bytes, buffer 0) ------------------------------
+    // K fragment (kb, ds): row wk*KW + 32kb + l32, unit 2ds+g -> stored at
+    // (2ds+g) ^ swz(l32&7); for ds = 4a + x that is 8a + ((2x+g) ^ sw).
+    int kaddr[4];
+    {
+        const int sw = swz(l32 & 7);
+        const int rowb = (wk * C::KW + l32) * C::ROWB;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) kaddr[x] = rowb + (((2 * x + g) ^ sw) << 4);
+    }
+    // V^T fragment (ks, db): lane = 16*G + 4k + q provides V[key][d] with
+    // key = wk*KW + 16ks + 4(G>>1) + 8hh + k and d = 32db + 16(G&1) + 4q.
+    int vaddr[2];
+    {
+        const int G = lane >> 4, k = (lane >> 2) & 3, q = lane & 3;
+        const int gi = G & 1, gk = G >> 1;
+        const int s = 2 * k + gk;  // swz of the row (row & 7 == 4gk + k)
+        const int c = 2 * gi + (q >> 1);
+        const int f = s >> 2;
+        const int A = (wk * C::KW + 4 * gk + k) * C::ROWB + ((c ^ (s & 3)) << 4) + ((q & 1) << 3);
+        vaddr[0] = A + 64 * f;        // even d-blocks: + 128 * (db / 2)
+        vaddr[1] = A + 64 * (1 - f);  // odd d-blocks
+    }
 
-    auto load_tile = [&](const uint16_t *kbase, const uint16_t *vbase, int64_t k0, int64_t kend) {
+    // ---- K/V tile loads: HBM -> LDS, no registers --------------------------------
+    auto load_tile = [&](const uint16_t *kbase, const uint16_t *vbase, int64_t k0, int64_t kend, int buf) {
+        const int nvalid = (int)(kend - k0 < BN ? kend - k0 : BN);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kbase + k0 * a.k_ss), (short)0, (int)(nvalid * a.k_ss * 2), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vbase + k0 * a.v_ss), (short)0, (int)(nvalid * a.v_ss * 2), kBufferFlags);
+        char *kt = smem + buf * C::BUF;
+        char *vt = kt + C::TILE;
 #pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int u = tid + i * C::NT;
-            const int row = u / (D / 8), col = u % (D / 8);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if ((C::K_UNITS % C::NT == 0 || u < C::K_UNITS) && k0 + row < kend)
-                v = *(const u32x4 *)(kbase + (k0 + row) * a.k_ss + col * 8);
-            kreg[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = tid + i * C::NT;
-            const int kq = u / (D / 8), dg = u % (D / 8);
-            const bool uok = C::V_UNITS % C::NT == 0 || u < C::V_UNITS;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t key = k0 + 4 * kq + j;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (uok && key < kend) v = *(const u32x4 *)(vbase + key * a.v_ss + dg * 8);
-                vreg[i][j] = v;
-            }
+        for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
+            const int inst = j * NW + w;
+            const int pos = inst * 64 + lane;
+            const int r = pos / C::UPR, u = (pos % C::UPR) ^ swz(r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kt + inst * 1024), 16,
+                                                     (unsigned)(r * a.k_ss * 2 + u * 16), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vt + inst * 1024), 16,
+                                                     (unsigned)(r * a.v_ss * 2 + u * 16), 0, 0, 0);
         }
     };
-
-    auto store_tile = [&](int buf) {
-        uint16_t *Ks = smem + buf * (C::KTILE + C::VTILE);
-        uint16_t *Vt = Ks + C::KTILE;
-#pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int u = tid + i * C::NT;
-            if (C::K_UNITS % C::NT == 0 || u < C::K_UNITS) {
-                const int row = u / (D / 8), col = u % (D / 8);
-                *(u32x4 *)(Ks + row * C::KROW + col * 8) = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = tid + i * C::NT;
-            if (C::V_UNITS % C::NT == 0 || u < C::V_UNITS) {
-                const int kq = u / (D / 8), dg = u % (D / 8);
-                const int slot = vt_slot(4 * kq);  // 4 keys stay adjacent
-                const int unit = slot >> 3, off = slot & 7;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const int d = 8 * dg + x;
-                    const unsigned sel = (x & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 pr;
-                    pr[0] = __builtin_amdgcn_perm(vreg[i][1][x >> 1], vreg[i][0][x >> 1], sel);
-                    pr[1] = __builtin_amdgcn_perm(vreg[i][3][x >> 1], vreg[i][2][x >> 1], sel);
-                    const int phys = unit ^ vt_swizzle<C::U>(d);
-                    *(u32x2 *)(Vt + d * BN + phys * 8 + off) = pr;
-                }
-            }
-        }
+    auto wait_tile = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     };
 
     // ---- one KV tile for this wave ----------------------------------------------
     auto compute_tile = [&](int buf, int64_t k0, int64_t kend, int64_t cstart, bool masked) {
-        const uint16_t *Ks = smem + buf * (C::KTILE + C::VTILE);
-        const uint16_t *Vt = Ks + C::KTILE;
+        const char *kt = smem + buf * C::BUF;
+        const char *vt = kt + C::TILE;
         f32x16 sacc[C::KB];
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const uint16_t *kp = Ks + (wk * C::KW + l32) * C::KROW + 8 * g;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) {
-                const bf16x8 kf = *(const bf16x8 *)(kp + 32 * kb * C::KROW + 16 * ds);
+                const bf16x8 kf = lds_read_b128(kt, kaddr[ds & 3] + 128 * (ds >> 2) + 32 * kb * C::ROWB);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb], 0, 0, 0);
             }
         if (masked) {
@@ -327,15 +327,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64
                 pf[2 * kb + hh] = to_bf16x8(pk);
             }
 #pragma unroll
-        for (int ks = 0; ks < 2 * C::KB; ++ks) {
-            const int unit = ((wk * C::KW + 16 * ks) >> 3) + g;
+        for (int ks = 0; ks < 2 * C::KB; ++ks)
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-                const int d = 32 * db + l32;
-                const bf16x8 vf = *(const bf16x8 *)(Vt + d * BN + ((unit ^ vt_swizzle<C::U>(d)) << 3));
+                const int base = vaddr[db & 1] + 128 * (db >> 1) + 16 * ks * C::ROWB;
+                const bf16x8 vf = lds_read_vt(vt, base, base + 8 * C::ROWB);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
             }
-        }
     };
 
     // ---- walk the chunks --------------------------------------------------------
@@ -362,20 +360,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64
         const uint16_t *kbase = (const uint16_t *)ch.k + b * a.k_sb + hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + b * a.v_sb + hk * a.v_sh;
 
-        load_tile(kbase, vbase, kbeg, kend);
-        store_tile(0);
-        __syncthreads();
+        __syncthreads();  // the previous chunk's last tile is no longer read
+        load_tile(kbase, vbase, kbeg, kend, 0);
+        wait_tile();
         for (int it = 0; it < ntiles; ++it) {
             const int64_t k0 = kbeg + (int64_t)it * BN;
-            if (it + 1 < ntiles) load_tile(kbase, vbase, k0 + BN, kend);
+            if (it + 1 < ntiles) load_tile(kbase, vbase, k0 + BN, kend, (it + 1) & 1);
             // this wave's keys k0 + wk*KW .. + KW-1
             const int64_t wk0 = k0 + wk * C::KW;
             const bool skip = a.causal && ch.start + wk0 > a.q_offset + wv_thi;
             const bool full = wk0 + C::KW <= kend &&
                               (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
             if (!skip) compute_tile(it & 1, k0, kend, ch.start, !full);
-            if (it + 1 < ntiles) store_tile((it + 1) & 1);
-            __syncthreads();
+            wait_tile();
         }
     }
 
@@ -390,6 +387,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64
     }
     if constexpr (KSPLIT > 1) {
         // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows
+        __syncthreads();
         float *scr = reinterpret_cast<float *>(smem);
         constexpr int STRIDE = 16 * C::DB + 2;
         if (wk > 0) {

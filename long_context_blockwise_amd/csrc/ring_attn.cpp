@@ -98,6 +98,10 @@ int check_desc(const ra_desc *d, int64_t Lq, Strides *st) {
         return RA_OK;
     };
     int rc;
+    // kernels address one key tile (<= 64 rows) with 32-bit byte offsets
+    for (int i = 0; i < 3; ++i)
+        if (d->k_strides[i] >= ((int64_t)1 << 24) || d->v_strides[i] >= ((int64_t)1 << 24))
+            return fail(RA_ERR_UNSUPPORTED, "k/v strides must be below 2^24 elements");
     if ((rc = fill(d->q_strides, st->q, Lq, d->Hq, d->d_qk, "q"))) return rc;
     if ((rc = fill(d->o_strides, st->o, Lq, d->Hq, d->d_v, "out"))) return rc;
     // k/v: dense strides depend on each chunk's length; 0 in st->k[0] marks "dense"
