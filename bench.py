@@ -173,7 +173,7 @@ def cpu_baseline(name, budget_s=15.0):
     wl = inputs.WORKLOADS[name]
     x = inputs.make(wl, "cpu")
     chunks = x.chunks()
-    rows_all = inputs.sample_rows(wl.Lq, tile=max(1, wl.Lq // 64), seed=1)
+    rows_all = inputs.sample_rows(wl.Lq, tile=max(1, wl.Lq // 2048), seed=1)
     rng = np.random.default_rng(0)
     rng.shuffle(rows_all)
     n, spent, done_rows, t_total = 1, 0.0, [], 0.0

@@ -14,7 +14,9 @@
 // only the valid keys, so a ragged tail is zero-filled by the hardware.  Both
 // tiles stay row-major ([key][d]) with the 16-byte units of row r stored at
 // unit ^ swz(r), which makes the two read patterns below bank-conflict free.
-// Tiles are double buffered: tile t+1 is requested before tile t is computed.
+// Tile buffers are separate LDS arrays, each named statically where it is
+// used, so the compiler can tell reads of one buffer from the in-flight loads
+// into another and does not stall the reads on them.
 //
 // Matrix cores.  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16: keys are M (A operand, ds_read_b128 from LDS),
@@ -32,7 +34,30 @@
 // bf16, and the result is identical in exact arithmetic.  The true running
 // max is tracked alongside and the state is renormalised to it at the end, so
 // the exported m is the running maximum.
+//
+// Scheduling.  Tile t+1 is requested (HBM -> LDS) before tile t is computed;
+// two workgroups share a CU, so while one wave of a SIMD turns scores into
+// probabilities the other can feed the matrix cores.  For split-KV decoding
+// KSPLIT waves share each row block, each over its part of every key tile,
+// and merge their states through LDS at the end.
 #include "ra_internal.h"
+
+// Tuning knobs (compile-time): LDS fragments read ahead of the MFMAs (0 lets
+// the compiler schedule them), whether waves raise their issue priority while
+// they feed the matrix cores, and the key tile and stage count of the d=128
+// query-chunk kernel.
+#ifndef RA_TUNE_PF
+#define RA_TUNE_PF 4
+#endif
+#ifndef RA_TUNE_SETPRIO
+#define RA_TUNE_SETPRIO 1
+#endif
+#ifndef RA_TUNE_BN128
+#define RA_TUNE_BN128 64
+#endif
+#ifndef RA_TUNE_NS
+#define RA_TUNE_NS 2
+#endif
 
 namespace ra {
 namespace {
@@ -61,9 +86,17 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Maximum of x over lanes l and l^32 (the two lanes that share a query row).
-// (v_permlane32_swap with both operands equal is folded by the compiler to a
-// single result, losing the other half, so the exchange uses ds_bpermute.)
-__device__ inline float max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second; with both holding x, one holds the low half twice and
+// the other the high half twice, so their max is the pair max in every lane.
+// It is written as inline asm because the compiler's builtin returns the same
+// register for both results.  The s_nops cover the VALU-write -> permlane and
+// permlane -> VALU-read wait states, which the compiler does not see inside asm.
+__device__ inline float max_pair(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
 
 // Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
 // each XCD runs a contiguous range of logical tiles (tiles that share K/V then
@@ -75,10 +108,19 @@ __device__ inline int xcd_remap(int bid, int n) {
 }
 
 // Swizzle of the 16-byte units of LDS row r (key r of a tile): unit u is
-// stored at u ^ swz(r).  Eight consecutive rows read at one unit (K fragment
-// reads) land on 8 distinct units, and the 4 rows x 2 units of one transposed
-// V read do too.
-__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// stored at u ^ swz<D>(r).  gfx950's LDS serves 256 bytes (64 banks) per
+// cycle: 16 lanes of a ds_read_b128, 32 lanes of a ds_read_b64_tr_b16.  A K
+// fragment read touches 16 consecutive rows at one unit; a transposed V read
+// touches 4 consecutive rows x 4 units.  With rows of >= 256 bytes both land on
+// 16 distinct units of a 256-byte window when swz(r) = 4(r&3) + ((r>>2)&3).
+// 128-byte rows (d=64) pair up in a window, so the row-pair index r>>1 is used.
+template <int D>
+__device__ inline int swz(int r) {
+    if constexpr (D >= 128)
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 __device__ inline bf16x8 to_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -87,16 +129,20 @@ __device__ inline unsigned pack_bf16(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ inline bf16x8 lds_read_b128(const char *smem, int byte) {
-    return *reinterpret_cast<const bf16x8 *>(smem + byte);
+__device__ inline bf16x8 lds_read_b128(const char *lds, int byte) {
+    return *reinterpret_cast<const bf16x8 *>(lds + byte);
 }
 
 // Two transposed 4-key reads make one V^T A-operand fragment.
-__device__ inline bf16x8 lds_read_vt(const char *smem, int byte0, int byte1) {
-    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(smem + byte0));
-    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(smem + byte1));
+__device__ inline bf16x8 lds_read_vt(const char *lds, int byte0, int byte1) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + byte0));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + byte1));
     const s16x8 xy = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, xy);
+}
+
+__device__ inline f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int D, int BN, int NW, int KSPLIT>
@@ -111,382 +157,588 @@ struct Cfg {
     static constexpr int ROWB = D * 2;           // bytes per K/V row in LDS
     static constexpr int UPR = D / 8;            // 16-byte units per row
     static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
-    static constexpr int BUF = 2 * TILE;         // K + V
-    static constexpr int LDS = 2 * BUF;          // double buffered
     static constexpr int LOADS = TILE / 1024;    // 1 KiB wave loads per K (or V) tile
     static constexpr int LOADS_PER_WAVE = LOADS / NW;
+    static constexpr int PF = RA_TUNE_PF;        // LDS fragments read ahead of the MFMAs
+    static constexpr int SWB = D >= 128 ? 16 : 8;  // units covered by the swizzle
+    static constexpr int NKA = SWB / 2;            // per-lane K address patterns
+    static constexpr int NVD = SWB / 4;            // per-lane V^T address patterns per read
     static_assert(KW % 32 == 0, "each wave needs whole 32-key blocks");
     static_assert(D % 64 == 0, "head size must be a multiple of 64");
     static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
-    static_assert(KSPLIT == 1 || (KSPLIT - 1) * ROWW * 64 * (16 * DB + 2) * 4 <= LDS,
-                  "merge scratch must fit in LDS");
 };
 
-template <int D, int BN, int NW, int KSPLIT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
-void fwd_bf16_kernel(const FwdArgs a) {
-    using C = Cfg<D, BN, NW, KSPLIT>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+// ---------------------------------------------------------------------------
+// Pieces shared by both kernels
+// ---------------------------------------------------------------------------
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int wr = w % C::ROWW, wk = w / C::ROWW;
-    const int l32 = lane & 31, g = lane >> 5;
+// Rows and key range of one workgroup.
+struct WorkTile {
+    int b, hk, split;
+    int64_t p0;              // first packed row
+    int64_t wg_tlo, wg_thi;  // token range of the workgroup's rows
+};
 
-    // ---- which tile of which (batch, KV head, key range) -------------------
+__device__ inline void token_range(const FwdArgs &a, int64_t pa, int64_t pb, int64_t &lo, int64_t &hi) {
+    const int64_t pend = (int64_t)a.G * a.Lq_pad;
+    pb = (pb < pend ? pb : pend) - 1;
+    if (pa / a.Lq_pad == pb / a.Lq_pad) {
+        lo = pa % a.Lq_pad;
+        hi = pb % a.Lq_pad;
+        hi = hi < a.Lq - 1 ? hi : a.Lq - 1;
+    } else {
+        lo = 0;
+        hi = a.Lq - 1;
+    }
+}
+
+template <class C>
+__device__ inline WorkTile work_tile(const FwdArgs &a) {
+    WorkTile wt;
     const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
     int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int rt = lid % a.n_rowtiles;
     lid /= a.n_rowtiles;
-    const int split = lid % nsplit;
+    wt.split = lid % nsplit;
     lid /= nsplit;
-    const int hk = lid % a.Hkv;
-    const int b = lid / a.Hkv;
-
-    const int64_t Lq = a.Lq, Lq_pad = a.Lq_pad;
-    const int64_t prow_end = (int64_t)a.G * Lq_pad;
-    int64_t p0;
-    if (Lq_pad % C::BM == 0) {  // one head per tile; heaviest (latest) rows first
-        const int64_t ntt = Lq_pad / C::BM;
+    wt.hk = lid % a.Hkv;
+    wt.b = lid / a.Hkv;
+    if (a.Lq_pad % C::BM == 0) {  // one head per tile; heaviest (latest) rows first
+        const int64_t ntt = a.Lq_pad / C::BM;
         const int gq = rt % a.G;
         const int64_t tt = ntt - 1 - rt / a.G;
-        p0 = gq * Lq_pad + tt * C::BM;
+        wt.p0 = gq * a.Lq_pad + tt * C::BM;
     } else {
-        p0 = (int64_t)rt * C::BM;
+        wt.p0 = (int64_t)rt * C::BM;
     }
+    token_range(a, wt.p0, wt.p0 + C::BM, wt.wg_tlo, wt.wg_thi);
+    return wt;
+}
 
-    // token range (for causal skipping) of a run of packed rows
-    auto t_range = [&](int64_t pa, int64_t pb, int64_t &lo, int64_t &hi) {
-        pb = pb < prow_end ? pb : prow_end;
-        --pb;
-        if (pa / Lq_pad == pb / Lq_pad) {
-            lo = pa % Lq_pad;
-            hi = pb % Lq_pad;
-            hi = hi < Lq - 1 ? hi : Lq - 1;
-        } else {
-            lo = 0;
-            hi = Lq - 1;
-        }
-    };
-    int64_t wg_tlo, wg_thi, wv_tlo, wv_thi;
-    t_range(p0, p0 + C::BM, wg_tlo, wg_thi);
-    t_range(p0 + 32 * wr, p0 + 32 * wr + 32, wv_tlo, wv_thi);
+// The query row a lane owns.
+struct LaneRow {
+    int64_t t, qpos, srow;
+    int h;
+    bool ok;
+};
 
-    // this lane's query row
-    const int64_t prow = p0 + 32 * wr + l32;
-    const int gq = (int)(prow / Lq_pad);
-    const int64_t t = prow % Lq_pad;
-    const bool row_ok = prow < prow_end && t < Lq;
-    const int h = hk * a.G + gq;
-    const int64_t qpos = a.q_offset + t;
+__device__ inline LaneRow lane_row(const FwdArgs &a, const WorkTile &wt, int64_t prow) {
+    LaneRow r;
+    const int gq = (int)(prow / a.Lq_pad);
+    r.t = prow % a.Lq_pad;
+    r.ok = prow < (int64_t)a.G * a.Lq_pad && r.t < a.Lq;
+    r.h = wt.hk * a.G + gq;
+    r.qpos = a.q_offset + r.t;
+    r.srow = ((int64_t)wt.b * a.Lq + r.t) * a.Hq + r.h;  // state row index
+    return r;
+}
 
-    // ---- resident query fragments (B operand of S^T = K Q^T) ---------------
-    bf16x8 qf[C::DS];
-    {
-        const uint16_t *qp = (const uint16_t *)a.q + b * a.q_sb + t * a.q_ss + h * a.q_sh + 8 * g;
+// Resident query fragments (B operand of S^T = K Q^T): lane holds d = 16ds + 8g .. +8.
+template <class C>
+__device__ inline void load_q(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, bf16x8 (&qf)[C::DS]) {
+    const uint16_t *qp = (const uint16_t *)a.q + wt.b * a.q_sb + r.t * a.q_ss + r.h * a.q_sh + 8 * g;
 #pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *(const u32x4 *)(qp + 16 * ds);
-            qf[ds] = to_bf16x8(v);
-        }
+    for (int ds = 0; ds < C::DS; ++ds) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r.ok) v = *(const u32x4 *)(qp + 16 * ds);
+        qf[ds] = to_bf16x8(v);
     }
+}
 
-    // ---- running state --------------------------------------------------------
-    f32x16 oacc[C::DB];
+// Starting state: empty, or (m, l, O) from the caller.  O^T element i of block
+// db in lane l is d = 32db + 8(i/4) + 4g + i%4; lane pairs split l.
+template <class C>
+__device__ inline void load_state(const FwdArgs &a, const LaneRow &r, int g, bool owner, f32x16 (&o)[C::DB],
+                                  float &m_run, float &m_true, float &lsum) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = kNegInf, m_true = kNegInf, lsum = 0.f;
-    const int64_t srow = ((int64_t)b * Lq + t) * a.Hq + h;  // state row index
-    if (a.load_state && row_ok && wk == 0) {
-        const float m0 = a.m[srow];
-        m_run = m_true = m0 * kLog2e;
-        lsum = g == 0 ? a.l[srow] : 0.f;
-        const float *op = a.O + srow * D + 4 * g;
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    m_run = m_true = kNegInf;
+    lsum = 0.f;
+    if (!(a.load_state && r.ok && owner)) return;
+    m_run = m_true = a.m[r.srow] * kLog2e;
+    lsum = g == 0 ? a.l[r.srow] : 0.f;
+    const float *op = a.O + r.srow * (C::DB * 32) + 4 * g;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 v = *(const f32x4 *)(op + 32 * db + 8 * i4);
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 v = *(const f32x4 *)(op + 32 * db + 8 * i4);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) oacc[db][4 * i4 + j] = v[j];
-            }
+            for (int j = 0; j < 4; ++j) o[db][4 * i4 + j] = v[j];
+        }
+}
+
+// Per-lane LDS byte addresses.  The swizzle only touches the low 4 bits of a
+// unit index (3 for d=64), so every read is a per-lane base plus a
+// compile-time offset.
+// K fragment (kb, ds): row r0 + 32kb + l32, unit u = 2ds+g, stored at u ^ swz(row)
+// (r0 and 32kb keep the low 4 bits of the row).
+template <class C>
+__device__ inline void k_addrs(int r0, int l32, int g, int (&kaddr)[C::NKA]) {
+    const int sw = swz<C::DB * 32>(l32);
+    const int rowb = (r0 + l32) * C::ROWB;
+#pragma unroll
+    for (int x = 0; x < C::NKA; ++x) kaddr[x] = rowb + (((2 * x + g) ^ sw) << 4);
+}
+// V^T fragment (ks, db), read hh of 2: lane = 16G + 4k + q provides V[key][d]
+// with key = r0 + 16ks + 4(G>>1) + 8hh + k and d = 32db + 16(G&1) + 4q,
+// i.e. unit u = 4db + 2(G&1) + (q>>1), half q&1.
+template <class C>
+__device__ inline void v_addrs(int r0, int lane, int (&vaddr)[2][C::NVD]) {
+    const int G = lane >> 4, k = (lane >> 2) & 3, q = lane & 3;
+    const int gi = G & 1, gk = G >> 1;
+    const int c = 2 * gi + (q >> 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int row = r0 + 4 * gk + 8 * hh + k;
+        const int sw = swz<C::DB * 32>(row);
+#pragma unroll
+        for (int dbl = 0; dbl < C::NVD; ++dbl)
+            vaddr[hh][dbl] = row * C::ROWB + (((4 * dbl + c) ^ sw) << 4) + ((q & 1) << 3);
     }
-    const float c2 = a.scale_log2;
+}
 
-    // ---- per-lane LDS addresses (bytes, buffer 0) ------------------------------
-    // K fragment (kb, ds): row wk*KW + 32kb + l32, unit 2ds+g -> stored at
-    // (2ds+g) ^ swz(l32&7); for ds = 4a + x that is 8a + ((2x+g) ^ sw).
-    int kaddr[4];
-    {
-        const int sw = swz(l32 & 7);
-        const int rowb = (wk * C::KW + l32) * C::ROWB;
+template <class C>
+__device__ inline bf16x8 kfrag(const char *kt, const int (&kaddr)[C::NKA], int ds, int kb) {
+    return lds_read_b128(kt, kaddr[ds % C::NKA] + 16 * C::SWB * (ds / C::NKA) + 32 * kb * C::ROWB);
+}
+
+template <class C>
+__device__ inline bf16x8 vfrag(const char *vt, const int (&vaddr)[2][C::NVD], int ks, int db) {
+    const int off = 16 * C::SWB * (db / C::NVD) + 16 * ks * C::ROWB;
+    return lds_read_vt(vt, vaddr[0][db % C::NVD] + off, vaddr[1][db % C::NVD] + off);
+}
+
+// One K (or V) tile, keys k0 .. k0+BN-1 of a chunk, HBM -> LDS; keys >= kend
+// are zero-filled by the descriptor.  Each wave issues LOADS_PER_WAVE loads.
+template <class C>
+__device__ inline void load_tile(const uint16_t *base, int64_t stride, int64_t k0, int64_t kend, char *dst,
+                                 int w, int lane) {
+    constexpr int BN = C::TILE / C::ROWB;
+    const int nvalid = (int)(kend - k0 < BN ? kend - k0 : BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + k0 * stride), (short)0, (int)(nvalid * stride * 2), kBufferFlags);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) kaddr[x] = rowb + (((2 * x + g) ^ sw) << 4);
+    for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
+        const int inst = j * (C::NT / 64) + w;
+        const int pos = inst * 64 + lane;
+        const int r = pos / C::UPR, u = (pos % C::UPR) ^ swz<C::DB * 32>(r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + inst * 1024), 16,
+                                                 (unsigned)(r * stride * 2 + u * 16), 0, 0, 0);
     }
-    // V^T fragment (ks, db): lane = 16*G + 4k + q provides V[key][d] with
-    // key = wk*KW + 16ks + 4(G>>1) + 8hh + k and d = 32db + 16(G&1) + 4q.
-    int vaddr[2];
-    {
-        const int G = lane >> 4, k = (lane >> 2) & 3, q = lane & 3;
-        const int gi = G & 1, gk = G >> 1;
-        const int s = 2 * k + gk;  // swz of the row (row & 7 == 4gk + k)
-        const int c = 2 * gi + (q >> 1);
-        const int f = s >> 2;
-        const int A = (wk * C::KW + 4 * gk + k) * C::ROWB + ((c ^ (s & 3)) << 4) + ((q & 1) << 3);
-        vaddr[0] = A + 64 * f;        // even d-blocks: + 128 * (db / 2)
-        vaddr[1] = A + 64 * (1 - f);  // odd d-blocks
-    }
+}
 
-    // ---- K/V tile loads: HBM -> LDS, no registers --------------------------------
-    auto load_tile = [&](const uint16_t *kbase, const uint16_t *vbase, int64_t k0, int64_t kend, int buf) {
-        const int nvalid = (int)(kend - k0 < BN ? kend - k0 : BN);
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + k0 * a.k_ss), (short)0, (int)(nvalid * a.k_ss * 2), kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vbase + k0 * a.v_ss), (short)0, (int)(nvalid * a.v_ss * 2), kBufferFlags);
-        char *kt = smem + buf * C::BUF;
-        char *vt = kt + C::TILE;
+// Mask keys a lane's row must not see: element i of block kb is key
+// 32kb + 8(i/4) + 4g + i%4 relative to the wave's first key wk0; visible iff
+// wk0 + key < kend and, causally, cstart + wk0 + key <= qpos.
+template <class C>
+__device__ inline void mask_scores(f32x16 (&s)[C::KB], const FwdArgs &a, int64_t qpos, int64_t cstart,
+                                   int64_t wk0, int64_t kend, int g) {
+    int64_t lim = a.causal ? qpos - cstart - wk0 : (int64_t)C::KW;
+    lim = lim < -1 ? -1 : (lim > C::KW ? C::KW : lim);
+    int64_t end = kend - wk0;
+    end = end > C::KW ? C::KW : end;
+    const int ilim = (int)lim, iend = (int)end;
 #pragma unroll
-        for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
-            const int inst = j * NW + w;
-            const int pos = inst * 64 + lane;
-            const int r = pos / C::UPR, u = (pos % C::UPR) ^ swz(r);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kt + inst * 1024), 16,
-                                                     (unsigned)(r * a.k_ss * 2 + u * 16), 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vt + inst * 1024), 16,
-                                                     (unsigned)(r * a.v_ss * 2 + u * 16), 0, 0, 0);
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= iend || key > ilim) s[kb][i] = kNegInf;
         }
-    };
-    auto wait_tile = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
+}
 
-    // ---- one KV tile for this wave ----------------------------------------------
-    auto compute_tile = [&](int buf, int64_t k0, int64_t kend, int64_t cstart, bool masked) {
-        const char *kt = smem + buf * C::BUF;
-        const char *vt = kt + C::TILE;
-        f32x16 sacc[C::KB];
+// New tile maximum: update the true max, and move the reference (rescaling O
+// and l) when the tile max exceeds it by more than the threshold.
+template <class C>
+__device__ inline void update_max(const f32x16 (&s)[C::KB], float c2, float &m_run, float &m_true, float &lsum,
+                                  f32x16 (&o)[C::DB]) {
+    float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds)
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-                const bf16x8 kf = lds_read_b128(kt, kaddr[ds & 3] + 128 * (ds >> 2) + 32 * kb * C::ROWB);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb], 0, 0, 0);
-            }
-        if (masked) {
-            // key index of element i: 8*(i/4) + 4*g + i%4 within its 32-key block
-            const int64_t klim = a.causal ? qpos - cstart : (int64_t)1 << 62;
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int64_t key = k0 + wk * C::KW + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key >= kend || key > klim) sacc[kb][i] = kNegInf;
-                }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = max_pair(mx);
-        const float mt = mx * c2;
-        m_true = fmaxf(m_true, mt);
-        const bool need = mt > m_run + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float alpha = need ? exp2_fast(m_run - mt) : 1.f;
-            m_run = need ? mt : m_run;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-        const float mref = m_run == kNegInf ? 0.f : m_run;
-        bf16x8 pf[2 * C::KB];
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                u32x4 pk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float e0 = exp2_fast(__builtin_fmaf(sacc[kb][8 * hh + 2 * j], c2, -mref));
-                    const float e1 = exp2_fast(__builtin_fmaf(sacc[kb][8 * hh + 2 * j + 1], c2, -mref));
-                    lsum += e0 + e1;
-                    pk[j] = pack_bf16(e0, e1);
-                }
-                pf[2 * kb + hh] = to_bf16x8(pk);
-            }
-#pragma unroll
-        for (int ks = 0; ks < 2 * C::KB; ++ks)
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const int base = vaddr[db & 1] + 128 * (db >> 1) + 16 * ks * C::ROWB;
-                const bf16x8 vf = lds_read_vt(vt, base, base + 8 * C::ROWB);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
-            }
-    };
-
-    // ---- walk the chunks --------------------------------------------------------
-    int c_begin = 0, c_end = a.n_chunks, sub = 0;
-    if (a.split_mode) {
-        c_begin = split / a.n_sub;
-        sub = split % a.n_sub;
-        c_end = c_begin + 1;
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-        const ChunkArg ch = a.chunks[c];
-        int64_t kbeg = 0, kend = ch.len;
-        if (a.split_mode) {
-            kbeg = sub * a.sub_len;
-            kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
-        }
-        int64_t kstop = kend;
-        if (a.causal) {
-            const int64_t vis = a.q_offset + wg_thi - ch.start + 1;  // keys < vis can be visible
-            kstop = vis < kstop ? vis : kstop;
-        }
-        if (kstop <= kbeg) continue;  // uniform across the workgroup
-        const int ntiles = (int)((kstop - kbeg + BN - 1) / BN);
-        const uint16_t *kbase = (const uint16_t *)ch.k + b * a.k_sb + hk * a.k_sh;
-        const uint16_t *vbase = (const uint16_t *)ch.v + b * a.v_sb + hk * a.v_sh;
-
-        __syncthreads();  // the previous chunk's last tile is no longer read
-        load_tile(kbase, vbase, kbeg, kend, 0);
-        wait_tile();
-        for (int it = 0; it < ntiles; ++it) {
-            const int64_t k0 = kbeg + (int64_t)it * BN;
-            if (it + 1 < ntiles) load_tile(kbase, vbase, k0 + BN, kend, (it + 1) & 1);
-            // this wave's keys k0 + wk*KW .. + KW-1
-            const int64_t wk0 = k0 + wk * C::KW;
-            const bool skip = a.causal && ch.start + wk0 > a.q_offset + wv_thi;
-            const bool full = wk0 + C::KW <= kend &&
-                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
-            if (!skip) compute_tile(it & 1, k0, kend, ch.start, !full);
-            wait_tile();
-        }
-    }
-
-    // ---- epilogue: combine key-split waves, renormalise, write ------------------
-    if (m_true != kNegInf) {
-        const float alpha = exp2_fast(m_run - m_true);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_pair(mx);
+    const float mt = mx * c2;
+    m_true = fmaxf(m_true, mt);
+    const bool need = mt > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? exp2_fast(m_run - mt) : 1.f;
+        m_run = need ? mt : m_run;
         lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    if constexpr (KSPLIT > 1) {
-        // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows
-        __syncthreads();
-        float *scr = reinterpret_cast<float *>(smem);
-        constexpr int STRIDE = 16 * C::DB + 2;
-        if (wk > 0) {
-            float *p = scr + ((wr * (KSPLIT - 1) + (wk - 1)) * STRIDE) * 64 + lane;
-            p[0] = m_true;
-            p[64] = lsum;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) p[(2 + 16 * db + i) * 64] = oacc[db][i];
-        }
-        __syncthreads();
-        if (wk == 0) {
-#pragma unroll 1
-            for (int o = 0; o < KSPLIT - 1; ++o) {
-                const float *p = scr + ((wr * (KSPLIT - 1) + o) * STRIDE) * 64 + lane;
-                const float m1 = p[0], l1 = p[64];
-                const float mn = fmaxf(m_true, m1);
-                if (mn == kNegInf) continue;
-                const float a0 = m_true == kNegInf ? 0.f : exp2_fast(m_true - mn);
-                const float a1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - mn);
-                lsum = a0 * lsum + a1 * l1;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        oacc[db][i] = a0 * oacc[db][i] + a1 * p[(2 + 16 * db + i) * 64];
-                m_true = mn;
-            }
-        }
-        if (wk > 0) return;
-    }
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!row_ok) return;
+}
 
-    if (a.split_mode || a.store_state) {
-        const int64_t slot_rows = (int64_t)a.B * Lq * a.Hq;
-        float *mp = a.split_mode ? a.pm + (a.part_base + split) * slot_rows : a.m;
-        float *lp = a.split_mode ? a.pl + (a.part_base + split) * slot_rows : a.l;
-        float *Op = a.split_mode ? a.pO + (a.part_base + split) * slot_rows * D : a.O;
-        if (g == 0) {
-            mp[srow] = m_true == kNegInf ? kNegInf : m_true * kLn2;
-            lp[srow] = ltot;
+// p = exp2(s*c - m_ref) as bf16 B operands of O^T += V^T P^T; adds the fp32 p to lsum.
+template <class C>
+__device__ inline void probabilities(const f32x16 (&s)[C::KB], float c2, float m_run, float &lsum,
+                                     bf16x8 (&pf)[2 * C::KB]) {
+    const float mref = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            u32x4 pk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e0 = exp2_fast(__builtin_fmaf(s[kb][8 * hh + 2 * j], c2, -mref));
+                const float e1 = exp2_fast(__builtin_fmaf(s[kb][8 * hh + 2 * j + 1], c2, -mref));
+                lsum += e0 + e1;
+                pk[j] = pack_bf16(e0, e1);
+            }
+            pf[2 * kb + hh] = to_bf16x8(pk);
         }
-        float *op = Op + srow * D + 4 * g;
+}
+
+// S^T (KB 32-key blocks) = K Q^T from an LDS tile, PF fragments in flight.
+template <class C>
+__device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[C::DS],
+                              f32x16 (&s)[C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    constexpr int N = C::DS * C::KB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = kfrag<C>(kt, kaddr, n / C::KB, n % C::KB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        s[n % C::KB] = mfma(fr[n % PF], qf[n / C::KB], s[n % C::KB]);
+        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, (n + PF) / C::KB, (n + PF) % C::KB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// O^T += V^T P^T over the wave's keys of an LDS tile, PF fragments in flight.
+template <class C>
+__device__ inline void accumulate_pv(const char *vt, const int (&vaddr)[2][C::NVD], const bf16x8 (&pf)[2 * C::KB],
+                                     f32x16 (&o)[C::DB]) {
+    constexpr int N = 2 * C::KB * C::DB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = vfrag<C>(vt, vaddr, n / C::DB, n % C::DB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        o[n % C::DB] = mfma(fr[n % PF], pf[n / C::DB], o[n % C::DB]);
+        if (n + PF < N) fr[n % PF] = vfrag<C>(vt, vaddr, (n + PF) / C::DB, (n + PF) % C::DB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Final state of a lane's row: renormalise to the true max, then write the
+// state (or a split partial) and/or the normalised output.
+template <class C>
+__device__ inline void renormalise(float m_run, float m_true, float &lsum, f32x16 (&o)[C::DB]) {
+    if (m_true == kNegInf) return;
+    const float alpha = exp2_fast(m_run - m_true);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+}
+
+template <class C>
+__device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g,
+                                     const f32x16 (&o)[C::DB], float m_true, float ltot) {
+    constexpr int D = C::DB * 32;
+    if (!r.ok) return;
+    if (a.split_mode || a.store_state) {
+        const int64_t slot_rows = (int64_t)a.B * a.Lq * a.Hq;
+        float *mp = a.split_mode ? a.pm + (a.part_base + wt.split) * slot_rows : a.m;
+        float *lp = a.split_mode ? a.pl + (a.part_base + wt.split) * slot_rows : a.l;
+        float *Op = a.split_mode ? a.pO + (a.part_base + wt.split) * slot_rows * D : a.O;
+        if (g == 0) {
+            mp[r.srow] = m_true == kNegInf ? kNegInf : m_true * kLn2;
+            lp[r.srow] = ltot;
+        }
+        float *op = Op + r.srow * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 f32x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = oacc[db][4 * i4 + j];
+                for (int j = 0; j < 4; ++j) v[j] = o[db][4 * i4 + j];
                 *(f32x4 *)(op + 32 * db + 8 * i4) = v;
             }
     }
     if (!a.split_mode && a.store_out) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        uint16_t *op = (uint16_t *)a.out + b * a.o_sb + t * a.o_ss + h * a.o_sh + 4 * g;
+        uint16_t *op = (uint16_t *)a.out + wt.b * a.o_sb + r.t * a.o_ss + r.h * a.o_sh + 4 * g;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 u32x2 v;
-                v[0] = pack_bf16(oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv);
-                v[1] = pack_bf16(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+                v[0] = pack_bf16(o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv);
+                v[1] = pack_bf16(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
                 *(u32x2 *)(op + 32 * db + 8 * i4) = v;
             }
     }
 }
 
-template <int D, int BN, int NW, int KSPLIT>
-hipError_t launch(const FwdArgs &a, hipStream_t s) {
+// Key range of chunk c for this workgroup; returns false when nothing is visible.
+__device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, int sub, int64_t &kbeg,
+                                   int64_t &kend, int &ntiles, int bn) {
+    const ChunkArg &ch = a.chunks[c];
+    kbeg = 0;
+    kend = ch.len;
+    if (a.split_mode) {
+        kbeg = sub * a.sub_len;
+        kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
+    }
+    int64_t kstop = kend;
+    if (a.causal) {
+        const int64_t vis = a.q_offset + wt.wg_thi - ch.start + 1;  // keys < vis can be visible
+        kstop = vis < kstop ? vis : kstop;
+    }
+    if (kstop <= kbeg) return false;
+    ntiles = (int)((kstop - kbeg + bn - 1) / bn);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Tile stages: NS statically named K and V buffers per workgroup.  Tile t
+// lives in stage t % NS; loads run NS-1 tiles ahead of the compute, and each
+// wait lets the loads of later tiles stay in flight.
+// ---------------------------------------------------------------------------
+#define RA_STAGE_ARRAYS(NS, TILE)                                                   \
+    __shared__ __attribute__((aligned(1024))) char kb0[TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char kb1[TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char kb2[(NS) > 2 ? (TILE) : 16];    \
+    __shared__ __attribute__((aligned(1024))) char kb3[(NS) > 3 ? (TILE) : 16];    \
+    __shared__ __attribute__((aligned(1024))) char kb4[(NS) > 4 ? (TILE) : 16];    \
+    __shared__ __attribute__((aligned(1024))) char vb0[TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char vb1[TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char vb2[(NS) > 2 ? (TILE) : 16];    \
+    __shared__ __attribute__((aligned(1024))) char vb3[(NS) > 3 ? (TILE) : 16];    \
+    __shared__ __attribute__((aligned(1024))) char vb4[(NS) > 4 ? (TILE) : 16];    \
+    auto kst = [&](auto u) -> char * {                                             \
+        constexpr int U = decltype(u)::value % (NS);                               \
+        if constexpr (U == 0) return kb0;                                          \
+        else if constexpr (U == 1) return kb1;                                     \
+        else if constexpr (U == 2) return kb2;                                     \
+        else if constexpr (U == 3) return kb3;                                     \
+        else return kb4;                                                           \
+    };                                                                             \
+    auto vst = [&](auto u) -> char * {                                             \
+        constexpr int U = decltype(u)::value % (NS);                               \
+        if constexpr (U == 0) return vb0;                                          \
+        else if constexpr (U == 1) return vb1;                                     \
+        else if constexpr (U == 2) return vb2;                                     \
+        else if constexpr (U == 3) return vb3;                                     \
+        else return vb4;                                                           \
+    };
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// Workgroup barrier for the tile buffers: each wave's own LDS reads and
+// writes have completed (lgkmcnt 0) and the compiler may not move memory
+// operations across it.  Unlike __syncthreads() it does not wait for the
+// wave's in-flight HBM->LDS tile loads (that fence would drain vmcnt and
+// serialise the prefetch); their completion is waited for explicitly.
+__device__ inline void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most `tiles` tiles' loads (LPT load instructions each) of
+// this wave are still in flight, then synchronise the workgroup.
+template <int LPT>
+__device__ inline void wait_tiles_in_flight(int tiles) {
+    switch (tiles) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory"); break;
+    }
+    tile_barrier();
+}
+
+// Run f(ic<t % NS>{}, t) for tiles t = 0 .. n-1: the stage of every call is a
+// compile-time constant, so each call names its LDS buffers statically.
+template <int NS, class F>
+__device__ inline void for_tiles(int n, F &&f) {
+    static_assert(NS >= 2 && NS <= 5, "2..5 stages");
+    for (int t = 0; t < n; t += NS) {
+        f(ic<0>{}, t);
+        if (t + 1 < n) f(ic<1>{}, t + 1);
+        if constexpr (NS > 2) if (t + 2 < n) f(ic<2 % NS>{}, t + 2);
+        if constexpr (NS > 3) if (t + 3 < n) f(ic<3 % NS>{}, t + 3);
+        if constexpr (NS > 4) if (t + 4 < n) f(ic<4 % NS>{}, t + 4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The attention kernel: one tile at a time (query-chunk prefill and split-KV decoding)
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW, int KSPLIT, int NS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
+void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(NS, C::TILE)
+    // merge scratch of the key-split waves: slot s spans tile buffers 2s, 2s+1
+    static_assert(KSPLIT == 1 || (C::ROWW * (KSPLIT - 1) <= 2 && (16 * C::DB + 2) * 64 * 4 <= 2 * C::TILE),
+                  "merge scratch must fit in the tile buffers");
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wr = w % C::ROWW, wk = w / C::ROWW;
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;
+    token_range(a, wt.p0 + 32 * wr, wt.p0 + 32 * wr + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * wr + l32);
+
+    bf16x8 qf[C::DS];
+    load_q<C>(a, wt, row, g, qf);
+    f32x16 oacc[C::DB];
+    float m_run, m_true, lsum;
+    load_state<C>(a, row, g, wk == 0, oacc, m_run, m_true, lsum);
+    const float c2 = a.scale_log2;
+    int kaddr[C::NKA];
+    k_addrs<C>(wk * C::KW, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(wk * C::KW, lane, vaddr);
+
+    int c_begin = 0, c_end = a.n_chunks, sub = 0;
+    if (a.split_mode) {
+        c_begin = wt.split / a.n_sub;
+        sub = wt.split % a.n_sub;
+        c_end = c_begin + 1;
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto issue = [&](auto u, int t) {
+            const int64_t k0 = kbeg + (int64_t)t * BN;
+            load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
+            load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+        };
+        auto wait_for = [&](int need, int last) {
+            const int after = last - need;
+            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+        };
+
+        tile_barrier();  // the previous chunk's tiles are no longer read
+        const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
+        for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+        wait_for(0, pre - 1);
+        for_tiles<NS>(ntiles, [&](auto u, int it) {
+            constexpr int U = decltype(u)::value;
+            if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+            // this wave's keys k0 + wk*KW .. + KW-1
+            const int64_t k0 = kbeg + (int64_t)it * BN;
+            const int64_t wk0 = k0 + wk * C::KW;
+            const bool skip = a.causal && ch.start + wk0 > a.q_offset + wv_thi;
+            const bool full = wk0 + C::KW <= kend &&
+                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
+            if (!skip) {
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+                f32x16 s[C::KB];
+                scores<C>(kst(u), kaddr, qf, s);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+                if (!full) mask_scores<C>(s, a, row.qpos, ch.start, wk0, kend, g);
+                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                bf16x8 pf[2 * C::KB];
+                probabilities<C>(s, c2, m_run, lsum, pf);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+                accumulate_pv<C>(vst(u), vaddr, pf, oacc);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+            }
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
+        });
+    }
+
+    renormalise<C>(m_run, m_true, lsum, oacc);
+    if constexpr (KSPLIT > 1) {
+        // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows.
+        // Value idx of a lane in slot sl is float idx*64 + lane of the slot,
+        // which spans tile buffers 2sl and 2sl+1.
+        __syncthreads();
+        constexpr int TF = C::TILE / 4;  // floats per tile buffer
+        auto at = [&](int sl, int idx) -> float & {
+            const int f = idx * 64 + lane;
+            const int bi = 2 * sl + f / TF;
+            char *buf = bi == 0 ? kb0 : bi == 1 ? kb1 : bi == 2 ? vb0 : vb1;
+            return reinterpret_cast<float *>(buf)[f % TF];
+        };
+        if (wk > 0) {
+            const int sl = wr * (KSPLIT - 1) + (wk - 1);
+            at(sl, 0) = m_true;
+            at(sl, 1) = lsum;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) at(sl, 2 + 16 * db + i) = oacc[db][i];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll 1
+        for (int o = 0; o < KSPLIT - 1; ++o) {
+            const int sl = wr * (KSPLIT - 1) + o;
+            const float m1 = at(sl, 0), l1 = at(sl, 1);
+            const float mn = fmaxf(m_true, m1);
+            if (mn == kNegInf) continue;
+            const float a0 = m_true == kNegInf ? 0.f : exp2_fast(m_true - mn);
+            const float a1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - mn);
+            lsum = a0 * lsum + a1 * l1;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] = a0 * oacc[db][i] + a1 * at(sl, 2 + 16 * db + i);
+            m_true = mn;
+        }
+    }
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    write_results<C>(a, wt, row, g, oacc, m_true, ltot);
+}
+
+template <class C, class K>
+hipError_t launch(K kernel, const FwdArgs &a, hipStream_t s) {
     const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
     const int64_t grid = (int64_t)a.B * a.Hkv * nsplit * a.n_rowtiles;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, KSPLIT>), dim3((unsigned)grid), dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile shapes per head size: (keys per tile, waves, key split of a tile).
-// Prefill: 4 waves x 32 rows = 128 rows per workgroup.  Split (decode): the
-// 64 packed rows of a KV head's query group, two waves per 32 rows, each
-// taking half of every key tile.
+// Tile shapes per head size.  Query-chunk prefill: 4 waves x 32 rows = 128
+// rows per workgroup, 64-key tiles (d <= 128), two stages.  Split (decoding):
+// the packed rows of a KV head's query group; at d=128 two waves per 32 rows,
+// each taking half of every key tile.  d=512: 32-key tiles.
 int fwd_bf16_row_tile(int d, bool split_mode) {
     if (d == 64) return Cfg<64, 64, 4, 1>::BM;
-    if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, 64, 4, 1>::BM;
+    if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, RA_TUNE_BN128, 4, 1>::BM;
     if (d == 512) return Cfg<512, 32, 4, 1>::BM;
     return 0;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s) {
     switch (d) {
-    case 64: return launch<64, 64, 4, 1>(a, s);
-    case 128: return split_mode ? launch<128, 64, 4, 2>(a, s) : launch<128, 64, 4, 1>(a, s);
-    case 512: return launch<512, 32, 4, 1>(a, s);
+    case 64: return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2>, a, s);
+    case 128:
+        if (split_mode) return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2>, a, s);
+        return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>, a, s);
+    case 512: return launch<Cfg<512, 32, 4, 1>>(fwd_bf16_kernel<512, 32, 4, 1, 2>, a, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -39,17 +39,33 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 
     float mx = kNegInf;
     for (int i = 0; i < a.n_parts; ++i) mx = fmaxf(mx, a.pm[i * a.rows + row]);
+    // weights are branch free (a part with m = -inf gets 0 and holds O = 0), so
+    // the loads of consecutive parts are independent and stay in flight together
+    const float mref = mx == kNegInf ? 0.f : mx;
     float l = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (mx != kNegInf) {
-        for (int i = 0; i < a.n_parts; ++i) {
-            const float mi = a.pm[i * a.rows + row];
-            if (mi == kNegInf) continue;
-            const float w = expf(mi - mx);
-            l += w * a.pl[i * a.rows + row];
-            const f32x4 v = *(const f32x4 *)(a.pO + (i * a.rows + row) * a.d_v + e);
-            o += w * v;
+    int i = 0;
+    for (; i + 4 <= a.n_parts; i += 4) {
+        float w[4], li[4];
+        f32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mi = a.pm[(i + j) * a.rows + row];
+            li[j] = a.pl[(i + j) * a.rows + row];
+            v[j] = *(const f32x4 *)(a.pO + ((i + j) * a.rows + row) * a.d_v + e);
+            w[j] = mi == kNegInf ? 0.f : expf(mi - mref);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            l += w[j] * li[j];
+            o += w[j] * v[j];
+        }
+    }
+    for (; i < a.n_parts; ++i) {
+        const float mi = a.pm[i * a.rows + row];
+        const float w = mi == kNegInf ? 0.f : expf(mi - mref);
+        l += w * a.pl[i * a.rows + row];
+        o += w * *(const f32x4 *)(a.pO + (i * a.rows + row) * a.d_v + e);
     }
     if (a.m) {
         if (e == 0) {

@@ -67,6 +67,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RingAttnError(RA_ERR_HIP, f"{path} is missing: build it with "
                                 "`python -m long_context_blockwise_amd.build`")
+        # torch ships its own HIP runtime under the same soname; loading torch
+        # first makes the library bind to that one runtime, so device pointers
+        # and streams from torch are valid in the library's calls
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(path)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.ring_attn_version.restype = ctypes.c_char_p
