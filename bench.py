@@ -35,6 +35,19 @@ PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of each workload's dominant kernel, from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs of this script, scaled by what the same
+# counters read for a plain 1 GiB elementwise copy (--copy-calibration):
+# FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  Valid only for the kernel sources
+# they were taken on; any change to them voids the figures (traffic -> null).
+KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_context_blockwise_amd/csrc/ra_internal.h",
+                  "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
+MEASURED_TRAFFIC = {
+    "digest": "772407a218f20225",
+    "prefill_bf16_h32_d128": 6.6713e8,
+    "decode_b4_gqa32x8_cache1m": 1.7250e10,
+}
+
 HEADLINE = "prefill_bf16_h32_d128"
 SECONDARY = "decode_b4_gqa32x8_cache1m"
 
@@ -73,6 +86,23 @@ def visible_pairs_fast(wl):
         acc += (wl.Lq - r_full) * n
         total += acc
     return total
+
+
+def kernel_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch measured on the current kernel sources, else None."""
+    if name not in MEASURED_TRAFFIC or kernel_digest() != MEASURED_TRAFFIC["digest"]:
+        return None
+    return MEASURED_TRAFFIC[name]
 
 
 def algorithmic(wl):
@@ -147,13 +177,13 @@ class WorkloadRun:
         if self.decode:
             achieved = self.bytes / self.launches / launch_s / 1e9
             roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+                        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name))
             metric, value, unit = "decode HBM GB/s at 1M KV", gbs, "GB/s"
         else:
             achieved = self.flops / self.launches / launch_s / 1e12
             peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
             roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
-                        frac=round(achieved / peak, 4), traffic=None)
+                        frac=round(achieved / peak, 4), traffic=measured_traffic(wl.name))
             metric, value, unit = "causal attn fwd TFLOP/s (% MFMA peak) per GPU", tflops, "TFLOP/s"
         return dict(workload=wl.name, metric=metric, value=round(value, 2), unit=unit,
                     ms_per_step=round(sec_per_step * 1e3, 4),
@@ -162,7 +192,7 @@ class WorkloadRun:
                     launches_per_step=self.launches, roofline=roof)
 
 
-def cpu_baseline(name, budget_s=15.0):
+def cpu_baseline(name, budget_s=20.0):
     """Time the CPU oracle on a bounded, stratified row sample of a workload
     (all heads and batches of the sampled rows) and scale to TFLOP/s."""
     import numpy as np
@@ -177,7 +207,7 @@ def cpu_baseline(name, budget_s=15.0):
     rng = np.random.default_rng(0)
     rng.shuffle(rows_all)
     n, spent, done_rows, t_total = 1, 0.0, [], 0.0
-    while spent < budget_s / 3 and len(done_rows) < len(rows_all):
+    while spent < budget_s / 2 and len(done_rows) < len(rows_all):
         rows = sorted(rows_all[len(done_rows):len(done_rows) + n])
         t0 = time.perf_counter()
         oracle.attention(x.q, chunks, wl.q_offset, wl.causal, rows=rows)
@@ -202,6 +232,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--secondary", default=SECONDARY, help="comma list, '' for none")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run one plain elementwise copy of BYTES bytes (reads BYTES, writes "
+                         "BYTES) to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one device's ring share on one GPU; --gpus must be 1 "
@@ -211,6 +244,15 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
+        return
     props = torch.cuda.get_device_properties(0)
     run = WorkloadRun(args.workload)
     sec, ev_ms = run.time(args.steps, args.warmup)

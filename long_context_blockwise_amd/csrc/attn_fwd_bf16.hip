@@ -233,25 +233,28 @@ __device__ inline LaneRow lane_row(const FwdArgs &a, const WorkTile &wt, int64_t
     return r;
 }
 
-// Resident query fragments (B operand of S^T = K Q^T): lane holds d = 16ds + 8g .. +8.
-template <class C>
-__device__ inline void load_q(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, bf16x8 (&qf)[C::DS]) {
-    const uint16_t *qp = (const uint16_t *)a.q + wt.b * a.q_sb + r.t * a.q_ss + r.h * a.q_sh + 8 * g;
+// Resident query fragments (B operand of S^T = K Q^T) for dimensions d0 ..
+// d0 + 16*NDS - 1: fragment ds of a lane holds d = d0 + 16ds + 8g .. +8.
+template <int NDS>
+__device__ inline void load_q(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0,
+                              bf16x8 (&qf)[NDS]) {
+    const uint16_t *qp = (const uint16_t *)a.q + wt.b * a.q_sb + r.t * a.q_ss + r.h * a.q_sh + d0 + 8 * g;
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
+    for (int ds = 0; ds < NDS; ++ds) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r.ok) v = *(const u32x4 *)(qp + 16 * ds);
         qf[ds] = to_bf16x8(v);
     }
 }
 
-// Starting state: empty, or (m, l, O) from the caller.  O^T element i of block
-// db in lane l is d = 32db + 8(i/4) + 4g + i%4; lane pairs split l.
-template <class C>
-__device__ inline void load_state(const FwdArgs &a, const LaneRow &r, int g, bool owner, f32x16 (&o)[C::DB],
-                                  float &m_run, float &m_true, float &lsum) {
+// Starting state: empty, or (m, l, O) from the caller, for output dimensions
+// dv0 .. dv0 + 32*NDB - 1 of rows with d_v = DV.  O^T element i of block db in
+// lane l is d = dv0 + 32db + 8(i/4) + 4g + i%4; lane pairs split l.
+template <int DV, int NDB>
+__device__ inline void load_state(const FwdArgs &a, const LaneRow &r, int g, bool owner, int dv0,
+                                  f32x16 (&o)[NDB], float &m_run, float &m_true, float &lsum) {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
     m_run = m_true = kNegInf;
@@ -259,9 +262,9 @@ __device__ inline void load_state(const FwdArgs &a, const LaneRow &r, int g, boo
     if (!(a.load_state && r.ok && owner)) return;
     m_run = m_true = a.m[r.srow] * kLog2e;
     lsum = g == 0 ? a.l[r.srow] : 0.f;
-    const float *op = a.O + r.srow * (C::DB * 32) + 4 * g;
+    const float *op = a.O + r.srow * DV + dv0 + 4 * g;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const f32x4 v = *(const f32x4 *)(op + 32 * db + 8 * i4);
@@ -352,9 +355,9 @@ __device__ inline void mask_scores(f32x16 (&s)[C::KB], const FwdArgs &a, int64_t
 
 // New tile maximum: update the true max, and move the reference (rescaling O
 // and l) when the tile max exceeds it by more than the threshold.
-template <class C>
+template <class C, int NDB>
 __device__ inline void update_max(const f32x16 (&s)[C::KB], float c2, float &m_run, float &m_true, float &lsum,
-                                  f32x16 (&o)[C::DB]) {
+                                  f32x16 (&o)[NDB]) {
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -369,7 +372,7 @@ __device__ inline void update_max(const f32x16 (&s)[C::KB], float c2, float &m_r
         m_run = need ? mt : m_run;
         lsum *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
@@ -396,15 +399,16 @@ __device__ inline void probabilities(const f32x16 (&s)[C::KB], float c2, float m
         }
 }
 
-// S^T (KB 32-key blocks) = K Q^T from an LDS tile, PF fragments in flight.
-template <class C>
-__device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[C::DS],
+// S^T (KB 32-key blocks) = K Q^T from an LDS tile over the NDS reduction
+// steps whose K units start at kt, PF fragments in flight.
+template <class C, int NDS>
+__device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[NDS],
                               f32x16 (&s)[C::KB]) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    constexpr int N = C::DS * C::KB;
+    constexpr int N = NDS * C::KB;
     constexpr int PF = C::PF > 0 ? C::PF : N;
     bf16x8 fr[PF];
 #pragma unroll
@@ -417,53 +421,56 @@ __device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const 
     }
 }
 
-// O^T += V^T P^T over the wave's keys of an LDS tile, PF fragments in flight.
-template <class C>
+// O^T += V^T P^T over the wave's keys of an LDS tile, for the NDB output
+// blocks whose V units start at vt, PF fragments in flight.
+template <class C, int NDB>
 __device__ inline void accumulate_pv(const char *vt, const int (&vaddr)[2][C::NVD], const bf16x8 (&pf)[2 * C::KB],
-                                     f32x16 (&o)[C::DB]) {
-    constexpr int N = 2 * C::KB * C::DB;
+                                     f32x16 (&o)[NDB]) {
+    constexpr int N = 2 * C::KB * NDB;
     constexpr int PF = C::PF > 0 ? C::PF : N;
     bf16x8 fr[PF];
 #pragma unroll
-    for (int n = 0; n < PF && n < N; ++n) fr[n] = vfrag<C>(vt, vaddr, n / C::DB, n % C::DB);
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = vfrag<C>(vt, vaddr, n / NDB, n % NDB);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        o[n % C::DB] = mfma(fr[n % PF], pf[n / C::DB], o[n % C::DB]);
-        if (n + PF < N) fr[n % PF] = vfrag<C>(vt, vaddr, (n + PF) / C::DB, (n + PF) % C::DB);
+        o[n % NDB] = mfma(fr[n % PF], pf[n / NDB], o[n % NDB]);
+        if (n + PF < N) fr[n % PF] = vfrag<C>(vt, vaddr, (n + PF) / NDB, (n + PF) % NDB);
         if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Final state of a lane's row: renormalise to the true max, then write the
 // state (or a split partial) and/or the normalised output.
-template <class C>
-__device__ inline void renormalise(float m_run, float m_true, float &lsum, f32x16 (&o)[C::DB]) {
+template <int NDB>
+__device__ inline void renormalise(float m_run, float m_true, float &lsum, f32x16 (&o)[NDB]) {
     if (m_true == kNegInf) return;
     const float alpha = exp2_fast(m_run - m_true);
     lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
 }
 
-template <class C>
-__device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g,
-                                     const f32x16 (&o)[C::DB], float m_true, float ltot) {
-    constexpr int D = C::DB * 32;
+// Final (or partial) results of output dimensions dv0 .. dv0 + 32*NDB - 1 of
+// rows with d_v = DV: the state (or a split partial) and/or the normalised
+// output; m and l are written by the lanes with write_ml.
+template <int DV, int NDB>
+__device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int dv0,
+                                     bool write_ml, const f32x16 (&o)[NDB], float m_true, float ltot) {
     if (!r.ok) return;
     if (a.split_mode || a.store_state) {
         const int64_t slot_rows = (int64_t)a.B * a.Lq * a.Hq;
         float *mp = a.split_mode ? a.pm + (a.part_base + wt.split) * slot_rows : a.m;
         float *lp = a.split_mode ? a.pl + (a.part_base + wt.split) * slot_rows : a.l;
-        float *Op = a.split_mode ? a.pO + (a.part_base + wt.split) * slot_rows * D : a.O;
-        if (g == 0) {
+        float *Op = a.split_mode ? a.pO + (a.part_base + wt.split) * slot_rows * DV : a.O;
+        if (g == 0 && write_ml) {
             mp[r.srow] = m_true == kNegInf ? kNegInf : m_true * kLn2;
             lp[r.srow] = ltot;
         }
-        float *op = Op + r.srow * D + 4 * g;
+        float *op = Op + r.srow * DV + dv0 + 4 * g;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 f32x4 v;
@@ -474,9 +481,9 @@ __device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const
     }
     if (!a.split_mode && a.store_out) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        uint16_t *op = (uint16_t *)a.out + wt.b * a.o_sb + r.t * a.o_ss + r.h * a.o_sh + 4 * g;
+        uint16_t *op = (uint16_t *)a.out + wt.b * a.o_sb + r.t * a.o_ss + r.h * a.o_sh + dv0 + 4 * g;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 u32x2 v;
@@ -599,10 +606,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
     const LaneRow row = lane_row(a, wt, wt.p0 + 32 * wr + l32);
 
     bf16x8 qf[C::DS];
-    load_q<C>(a, wt, row, g, qf);
+    load_q(a, wt, row, g, 0, qf);
     f32x16 oacc[C::DB];
     float m_run, m_true, lsum;
-    load_state<C>(a, row, g, wk == 0, oacc, m_run, m_true, lsum);
+    load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
     const float c2 = a.scale_log2;
     int kaddr[C::NKA];
     k_addrs<C>(wk * C::KW, l32, g, kaddr);
@@ -665,7 +672,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
         });
     }
 
-    renormalise<C>(m_run, m_true, lsum, oacc);
+    renormalise(m_run, m_true, lsum, oacc);
     if constexpr (KSPLIT > 1) {
         // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows.
         // Value idx of a lane in slot sl is float idx*64 + lane of the slot,
@@ -706,7 +713,131 @@ void fwd_bf16_kernel(const FwdArgs a) {
         }
     }
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    write_results<C>(a, wt, row, g, oacc, m_true, ltot);
+    write_results<D>(a, wt, row, g, 0, true, oacc, m_true, ltot);
+}
+
+// ---------------------------------------------------------------------------
+// Wide heads (d = 512): two waves share each 32-row block, each holding half
+// of the query dimensions and half of the output dimensions, so neither the
+// resident Q nor the O accumulator of a wave outgrows the register file.  Per
+// tile each wave computes the scores over its half of d_qk, the pair swaps
+// these partial scores through LDS and adds them (the sum is commutative, so
+// both waves hold bitwise the same scores and run the same softmax), and each
+// wave multiplies the probabilities into its half of O.
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NRB>
+struct CfgHalf : Cfg<D, BN, 2 * NRB, 1> {
+    static constexpr int BM = 32 * NRB;  // query rows per workgroup
+    static constexpr int DSH = D / 32;   // reduction steps of a half of d_qk
+    static constexpr int DBH = D / 64;   // 32-wide O^T blocks of a half of d_v
+};
+
+template <int D, int BN, int NRB, int NS>
+__global__ __launch_bounds__(NRB * 128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_half_kernel(const FwdArgs a) {
+    using C = CfgHalf<D, BN, NRB>;
+    static_assert(C::KB == 1, "one 32-key block per tile");
+    static_assert((D / 16) % C::SWB == 0, "each half of a row covers whole swizzle windows");
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(NS, C::TILE)
+    // partial scores of each wave: [row block][half][4 x 64 lanes] of f32x4
+    __shared__ __attribute__((aligned(16))) f32x4 xs[NRB][2][4 * 64];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rb = w >> 1, hf = w & 1;
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;
+    token_range(a, wt.p0 + 32 * rb, wt.p0 + 32 * rb + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * rb + l32);
+
+    bf16x8 qf[C::DSH];
+    load_q(a, wt, row, g, hf * (D / 2), qf);
+    f32x16 oacc[C::DBH];
+    float m_run, m_true, lsum;
+    load_state<D>(a, row, g, true, hf * (D / 2), oacc, m_run, m_true, lsum);
+    const float c2 = a.scale_log2;
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+    // byte offset of this wave's half of every K and V row: D/2 bf16 values,
+    // whole swizzle windows, so the per-lane addresses carry over unchanged
+    const int half_off = hf * D;
+    f32x4 *xs_mine = xs[rb][hf];
+    const f32x4 *xs_other = xs[rb][hf ^ 1];
+
+    int c_begin = 0, c_end = a.n_chunks, sub = 0;
+    if (a.split_mode) {
+        c_begin = wt.split / a.n_sub;
+        sub = wt.split % a.n_sub;
+        c_end = c_begin + 1;
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto issue = [&](auto u, int t) {
+            const int64_t k0 = kbeg + (int64_t)t * BN;
+            load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
+            load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+        };
+        auto wait_for = [&](int need, int last) {
+            const int after = last - need;
+            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+        };
+
+        tile_barrier();  // the previous chunk's tiles are no longer read
+        const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
+        for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+        wait_for(0, pre - 1);
+        for_tiles<NS>(ntiles, [&](auto u, int it) {
+            constexpr int U = decltype(u)::value;
+            if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+            const int64_t k0 = kbeg + (int64_t)it * BN;
+            // both waves of a row block take the same branch
+            const bool skip = a.causal && ch.start + k0 > a.q_offset + wv_thi;
+            const bool full = k0 + BN <= kend && (!a.causal || ch.start + k0 + BN - 1 <= a.q_offset + wv_tlo);
+            f32x16 s[1];
+            if (!skip) {
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+                scores<C>(kst(u) + half_off, kaddr, qf, s);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    xs_mine[i4 * 64 + lane] = f32x4{s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]};
+            }
+            tile_barrier();  // partial scores visible to the partner wave
+            if (!skip) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 o = xs_other[i4 * 64 + lane];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s[0][4 * i4 + j] += o[j];
+                }
+                if (!full) mask_scores<C>(s, a, row.qpos, ch.start, k0, kend, g);
+                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                bf16x8 pf[2];
+                probabilities<C>(s, c2, m_run, lsum, pf);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+                accumulate_pv<C>(vst(u) + half_off, vaddr, pf, oacc);
+                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+            }
+            // the next tile's partial scores overwrite xs only after this barrier
+            // (after a chunk's last tile: the barrier at the next chunk's start)
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
+        });
+    }
+
+    renormalise(m_run, m_true, lsum, oacc);
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    write_results<D>(a, wt, row, g, hf * (D / 2), hf == 0, oacc, m_true, ltot);
 }
 
 template <class C, class K>
@@ -724,11 +855,12 @@ hipError_t launch(K kernel, const FwdArgs &a, hipStream_t s) {
 // Tile shapes per head size.  Query-chunk prefill: 4 waves x 32 rows = 128
 // rows per workgroup, 64-key tiles (d <= 128), two stages.  Split (decoding):
 // the packed rows of a KV head's query group; at d=128 two waves per 32 rows,
-// each taking half of every key tile.  d=512: 32-key tiles.
+// each taking half of every key tile.  d=512: 2 row blocks x 2 halves of the
+// head dimensions = 64 rows per workgroup, 32-key tiles.
 int fwd_bf16_row_tile(int d, bool split_mode) {
     if (d == 64) return Cfg<64, 64, 4, 1>::BM;
     if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, RA_TUNE_BN128, 4, 1>::BM;
-    if (d == 512) return Cfg<512, 32, 4, 1>::BM;
+    if (d == 512) return CfgHalf<512, 32, 2>::BM;
     return 0;
 }
 
@@ -738,7 +870,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t
     case 128:
         if (split_mode) return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2>, a, s);
         return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>, a, s);
-    case 512: return launch<Cfg<512, 32, 4, 1>>(fwd_bf16_kernel<512, 32, 4, 1, 2>, a, s);
+    case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2, 2>, a, s);
     default: return hipErrorInvalidValue;
     }
 }
