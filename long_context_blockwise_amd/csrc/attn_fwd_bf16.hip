@@ -98,6 +98,12 @@ __device__ inline float max_pair(float x) {
     return fmaxf(a, b);
 }
 
+// Index of the calling wave in its workgroup, as a scalar: the compiler
+// cannot see that threadIdx.x >> 6 is uniform across a wave, and would keep
+// everything derived from it (row ranges, branch conditions) in vector
+// registers and exec-masked branches.
+__device__ inline int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
 // each XCD runs a contiguous range of logical tiles (tiles that share K/V then
 // share that XCD's L2).
@@ -316,40 +322,52 @@ __device__ inline bf16x8 vfrag(const char *vt, const int (&vaddr)[2][C::NVD], in
 
 // One K (or V) tile, keys k0 .. k0+BN-1 of a chunk, HBM -> LDS; keys >= kend
 // are zero-filled by the descriptor.  Each wave issues LOADS_PER_WAVE loads.
+// The host keeps token strides below 2^24 elements, so the byte offsets
+// within a tile (< BN x stride x 2 < 2^31) are computed in 32 bits.
 template <class C>
 __device__ inline void load_tile(const uint16_t *base, int64_t stride, int64_t k0, int64_t kend, char *dst,
                                  int w, int lane) {
     constexpr int BN = C::TILE / C::ROWB;
-    const int nvalid = (int)(kend - k0 < BN ? kend - k0 : BN);
+    const unsigned stride_b = (unsigned)stride * 2u;
+    const unsigned nvalid = (unsigned)(kend - k0 < BN ? kend - k0 : BN);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(base + k0 * stride), (short)0, (int)(nvalid * stride * 2), kBufferFlags);
+        (void *)(base + k0 * stride), (short)0, (int)(nvalid * stride_b), kBufferFlags);
 #pragma unroll
     for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
         const int inst = j * (C::NT / 64) + w;
         const int pos = inst * 64 + lane;
         const int r = pos / C::UPR, u = (pos % C::UPR) ^ swz<C::DB * 32>(r);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + inst * 1024), 16,
-                                                 (unsigned)(r * stride * 2 + u * 16), 0, 0, 0);
+                                                 (unsigned)r * stride_b + (unsigned)(u * 16), 0, 0, 0);
     }
 }
 
-// Mask keys a lane's row must not see: element i of block kb is key
-// 32kb + 8(i/4) + 4g + i%4 relative to the wave's first key wk0; visible iff
-// wk0 + key < kend and, causally, cstart + wk0 + key <= qpos.
+// Keys of a chunk a lane's row may see, counted from the chunk's first
+// processed key kbeg: keys kbeg .. kbeg + n - 1 exist (below kend) and, for
+// causal attention, sit at absolute positions <= the row's position.  Clamped
+// to [0, 2^30] so that per-tile offsets stay in 32 bits.
+__device__ inline int visible_keys(const FwdArgs &a, const LaneRow &r, int64_t cstart, int64_t kbeg, int64_t kend) {
+    int64_t n = kend - kbeg;
+    if (a.causal) {
+        const int64_t vis = r.qpos - cstart - kbeg + 1;
+        n = vis < n ? vis : n;
+    }
+    n = n < 0 ? 0 : n;
+    return (int)(n < (1 << 30) ? n : (1 << 30));
+}
+
+// Mask the keys a lane's row must not see in a tile whose first key is
+// `rel` keys after kbeg: element i of block kb is key 32kb + 8(i/4) + 4g +
+// i%4 of the tile, visible iff it is below vis - rel.
 template <class C>
-__device__ inline void mask_scores(f32x16 (&s)[C::KB], const FwdArgs &a, int64_t qpos, int64_t cstart,
-                                   int64_t wk0, int64_t kend, int g) {
-    int64_t lim = a.causal ? qpos - cstart - wk0 : (int64_t)C::KW;
-    lim = lim < -1 ? -1 : (lim > C::KW ? C::KW : lim);
-    int64_t end = kend - wk0;
-    end = end > C::KW ? C::KW : end;
-    const int ilim = (int)lim, iend = (int)end;
+__device__ inline void mask_scores(f32x16 (&s)[C::KB], int vis, int rel, int g) {
+    const int lim = vis - rel - 4 * g;  // compare against the lane-independent part of the key
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= iend || key > ilim) s[kb][i] = kNegInf;
+            const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
+            if (key >= lim) s[kb][i] = kNegInf;
         }
 }
 
@@ -519,33 +537,24 @@ __device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, 
 // lives in stage t % NS; loads run NS-1 tiles ahead of the compute, and each
 // wait lets the loads of later tiles stay in flight.
 // ---------------------------------------------------------------------------
-#define RA_STAGE_ARRAYS(NS, TILE)                                                   \
-    __shared__ __attribute__((aligned(1024))) char kb0[TILE];                      \
-    __shared__ __attribute__((aligned(1024))) char kb1[TILE];                      \
-    __shared__ __attribute__((aligned(1024))) char kb2[(NS) > 2 ? (TILE) : 16];    \
-    __shared__ __attribute__((aligned(1024))) char kb3[(NS) > 3 ? (TILE) : 16];    \
-    __shared__ __attribute__((aligned(1024))) char kb4[(NS) > 4 ? (TILE) : 16];    \
-    __shared__ __attribute__((aligned(1024))) char vb0[TILE];                      \
-    __shared__ __attribute__((aligned(1024))) char vb1[TILE];                      \
-    __shared__ __attribute__((aligned(1024))) char vb2[(NS) > 2 ? (TILE) : 16];    \
-    __shared__ __attribute__((aligned(1024))) char vb3[(NS) > 3 ? (TILE) : 16];    \
-    __shared__ __attribute__((aligned(1024))) char vb4[(NS) > 4 ? (TILE) : 16];    \
-    auto kst = [&](auto u) -> char * {                                             \
-        constexpr int U = decltype(u)::value % (NS);                               \
-        if constexpr (U == 0) return kb0;                                          \
-        else if constexpr (U == 1) return kb1;                                     \
-        else if constexpr (U == 2) return kb2;                                     \
-        else if constexpr (U == 3) return kb3;                                     \
-        else return kb4;                                                           \
-    };                                                                             \
-    auto vst = [&](auto u) -> char * {                                             \
-        constexpr int U = decltype(u)::value % (NS);                               \
-        if constexpr (U == 0) return vb0;                                          \
-        else if constexpr (U == 1) return vb1;                                     \
-        else if constexpr (U == 2) return vb2;                                     \
-        else if constexpr (U == 3) return vb3;                                     \
-        else return vb4;                                                           \
-    };
+// K and V of a tile share one array (K first, V at +TILE); the compiler
+// tracks in-flight HBM->LDS loads per array, and a handful of arrays stays
+// within what it can tell apart.
+#define RA_STAGE_ARRAYS(NS, TILE)                                                      \
+    __shared__ __attribute__((aligned(1024))) char kv0[2 * (TILE)];                   \
+    __shared__ __attribute__((aligned(1024))) char kv1[2 * (TILE)];                   \
+    __shared__ __attribute__((aligned(1024))) char kv2[(NS) > 2 ? 2 * (TILE) : 16];   \
+    __shared__ __attribute__((aligned(1024))) char kv3[(NS) > 3 ? 2 * (TILE) : 16];   \
+    __shared__ __attribute__((aligned(1024))) char kv4[(NS) > 4 ? 2 * (TILE) : 16];   \
+    auto kst = [&](auto u) -> char * {                                                \
+        constexpr int U = decltype(u)::value % (NS);                                  \
+        if constexpr (U == 0) return kv0;                                             \
+        else if constexpr (U == 1) return kv1;                                        \
+        else if constexpr (U == 2) return kv2;                                        \
+        else if constexpr (U == 3) return kv3;                                        \
+        else return kv4;                                                              \
+    };                                                                                \
+    auto vst = [&](auto u) -> char * { return kst(u) + (TILE); };
 
 template <int N>
 using ic = std::integral_constant<int, N>;
@@ -597,7 +606,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
     static_assert(KSPLIT == 1 || (C::ROWW * (KSPLIT - 1) <= 2 && (16 * C::DB + 2) * 64 * 4 <= 2 * C::TILE),
                   "merge scratch must fit in the tile buffers");
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_index();
     const int wr = w % C::ROWW, wk = w / C::ROWW;
     const int l32 = lane & 31, g = lane >> 5;
     const WorkTile wt = work_tile<C>(a);
@@ -627,6 +636,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
         int ntiles;
         if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         const ChunkArg ch = a.chunks[c];
+        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto issue = [&](auto u, int t) {
@@ -657,7 +667,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 f32x16 s[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);
                 if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-                if (!full) mask_scores<C>(s, a, row.qpos, ch.start, wk0, kend, g);
+                if (!full) mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
                 update_max<C>(s, c2, m_run, m_true, lsum, oacc);
                 bf16x8 pf[2 * C::KB];
                 probabilities<C>(s, c2, m_run, lsum, pf);
@@ -682,7 +692,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
         auto at = [&](int sl, int idx) -> float & {
             const int f = idx * 64 + lane;
             const int bi = 2 * sl + f / TF;
-            char *buf = bi == 0 ? kb0 : bi == 1 ? kb1 : bi == 2 ? vb0 : vb1;
+            char *buf = bi < 2 ? kv0 + bi * C::TILE : kv1 + (bi - 2) * C::TILE;
             return reinterpret_cast<float *>(buf)[f % TF];
         };
         if (wk > 0) {
@@ -743,7 +753,7 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
     // partial scores of each wave: [row block][half][4 x 64 lanes] of f32x4
     __shared__ __attribute__((aligned(16))) f32x4 xs[NRB][2][4 * 64];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_index();
     const int rb = w >> 1, hf = w & 1;
     const int l32 = lane & 31, g = lane >> 5;
     const WorkTile wt = work_tile<C>(a);
@@ -778,6 +788,7 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
         int ntiles;
         if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         const ChunkArg ch = a.chunks[c];
+        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto issue = [&](auto u, int t) {
@@ -818,7 +829,7 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) s[0][4 * i4 + j] += o[j];
                 }
-                if (!full) mask_scores<C>(s, a, row.qpos, ch.start, k0, kend, g);
+                if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
                 update_max<C>(s, c2, m_run, m_true, lsum, oacc);
                 bf16x8 pf[2];
                 probabilities<C>(s, c2, m_run, lsum, pf);
