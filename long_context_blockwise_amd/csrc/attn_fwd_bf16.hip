@@ -597,7 +597,7 @@ __device__ inline void for_tiles(int n, F &&f) {
 // The attention kernel: one tile at a time (query-chunk prefill and split-KV decoding)
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW, int KSPLIT, int NS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
     constexpr int LPT = 2 * C::LOADS_PER_WAVE;
