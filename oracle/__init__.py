@@ -76,6 +76,8 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_finalize.restype = None
     lib.oracle_finalize.argtypes = [i64, i32, vp, vp, vp, vp, vp]
+    lib.oracle_dequant_fp8.restype = i32
+    lib.oracle_dequant_fp8.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp]
     return lib
 
 
@@ -122,9 +124,49 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+def _u8(x):
+    """Raw bytes of an 8-bit tensor/array as a contiguous uint8 numpy array."""
+    if hasattr(x, "detach"):
+        import torch
+
+        x = x.detach().cpu().contiguous()
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        return np.ascontiguousarray(x.numpy())
+    return np.ascontiguousarray(np.asarray(x).view(np.uint8))
+
+
+KV_SCALE_BLOCK = 64  # tokens per shared exponent of an 8-bit KV cache
+
+
+def dequant_fp8(codes, exps, block: int = KV_SCALE_BLOCK) -> np.ndarray:
+    """Decode an 8-bit (OCP FP8 E4M3) KV tensor ``codes [B, len, H, d]`` whose
+    blocks of ``block`` tokens per (batch, head) share the power-of-two scale
+    2^(e-127) in ``exps [B, H, ceil(len/block)]``; returns float64."""
+    c = _u8(codes)
+    e = _u8(exps)
+    if c.ndim != 4 or e.ndim != 3:
+        raise ValueError("codes must be [B, len, H, d] and exps [B, H, nblk]")
+    B, n, H, d = (int(x) for x in c.shape)
+    if e.shape != (B, H, (n + block - 1) // block):
+        raise ValueError(f"exps shape {e.shape} does not match codes {c.shape}")
+    out = np.zeros(c.shape, dtype=np.float64)
+    if _get_lib().oracle_dequant_fp8(B, n, H, d, block, _ptr(c), _ptr(e), _ptr(out)) != 0:
+        raise ValueError("oracle_dequant_fp8 failed")
+    return out
+
+
+def _decoded(chunk):
+    """(k, v, start) of a chunk; 8-bit chunks (k, v, start, k_exp, v_exp) are decoded."""
+    if len(chunk) == 5:
+        k, v, start, ke, ve = chunk
+        return dequant_fp8(k, ke), dequant_fp8(v, ve), start
+    return chunk
+
+
 def _chunk_arrays(chunks, dtype, code):
     ks, vs, starts, lens = [], [], [], []
-    for (k, v, start) in chunks:
+    for (k, v, start) in (_decoded(c) for c in chunks):
         ka, kc = _to_numpy(k, dtype)
         va, vc = _to_numpy(v, dtype)
         if kc != code or vc != code:
@@ -143,6 +185,9 @@ class _Problem:
 
     def __init__(self, q, chunks, dtype, rows):
         self.q, self.code = _to_numpy(q, dtype)
+        if any(len(c) == 5 for c in chunks):  # decoded 8-bit KV: compute in float64
+            q64 = q.detach().cpu().double().numpy() if hasattr(q, "detach") else np.asarray(q, np.float64)
+            self.q, self.code = np.ascontiguousarray(q64), _F64
         if self.q.ndim != 4:
             raise ValueError("q must be [B, Lq, Hq, d_qk]")
         self.B, self.Lq, self.Hq, self.dqk = (int(s) for s in self.q.shape)

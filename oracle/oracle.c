@@ -53,6 +53,18 @@
  * patterns, upcast exactly).  All arithmetic is double.
  *
  * Return value: 0 on success, -1 on an argument error, -2 if out of memory.
+ *
+ *  - oracle_dequant_fp8: 8-bit keys/values of a quantised KV cache turned
+ *    back into numbers.  The pages recommend storing the KV cache in 8 bits
+ *    (page "billion-token context window engineering", section on production
+ *    parameters: 4/8-bit KV-cache quantisation for serving; page
+ *    "RingAttention与RAG技术对比及实战应用", §2.3: FP8 deployment) without
+ *    fixing a format.  The reading taken: OCP FP8 E4M3 codes (1 sign bit,
+ *    4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal;
+ *    S.1111.111 is NaN; no infinities; largest finite value 448), each block
+ *    of 64 consecutive tokens of one (batch, KV head) sharing a power-of-two
+ *    scale 2^(e - 127) given by an 8-bit biased exponent e (1 .. 254).
+ *    The attention itself is then oracle_attention on the decoded values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -324,4 +336,38 @@ void oracle_finalize(int64_t n, int dv, const double *m, const double *l,
             lse[i] = -INFINITY;
         }
     }
+}
+
+/* Value of one OCP FP8 E4M3 code. */
+static double fp8_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7, ex = (code >> 3) & 15, man = code & 7;
+    double v;
+    if (ex == 15 && man == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)man, -9); /* subnormal: man/8 * 2^(1-7) */
+    else
+        v = ldexp(8.0 + man, ex - 10); /* (1 + man/8) * 2^(ex-7) */
+    return sign ? -v : v;
+}
+
+/* codes [B][len][H][d] with exponents [B][H][ceil(len/block)] -> out (double,
+ * same layout as codes).  Returns -1 on bad arguments. */
+int oracle_dequant_fp8(int B, int64_t len, int H, int d, int block,
+                       const uint8_t *codes, const uint8_t *exps, double *out)
+{
+    if (B < 0 || len < 0 || H <= 0 || d <= 0 || block <= 0 || (len && (!codes || !exps || !out)))
+        return -1;
+    int64_t nblk = (len + block - 1) / block;
+    for (int b = 0; b < B; ++b)
+        for (int64_t t = 0; t < len; ++t)
+            for (int h = 0; h < H; ++h) {
+                int e = exps[((int64_t)b * H + h) * nblk + t / block];
+                double scale = ldexp(1.0, e - 127);
+                int64_t base = (((int64_t)b * len + t) * H + h) * d;
+                for (int i = 0; i < d; ++i)
+                    out[base + i] = fp8_e4m3_value(codes[base + i]) * scale;
+            }
+    return 0;
 }

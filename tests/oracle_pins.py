@@ -403,6 +403,64 @@ def pin_input_types():
     assert np.array_equal(out_f, out_f64), "fp32 upcast"
 
 
+def pin_fp8_decode_library():
+    """8-bit KV decoding against torch's own OCP FP8 E4M3 conversion
+    (``torch.float8_e4m3fn``), for all 256 codes at several block exponents,
+    with every block of 64 tokens taking its own exponent."""
+    import torch
+
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    ref_codes = codes.view(torch.float8_e4m3fn).double()
+    # [B=2, len=256 (4 blocks of 64), H=3, d=1]: token t of batch b, head h holds code (t + 37h + 11b) % 256
+    B, n, H = 2, 256, 3
+    t = torch.arange(n).view(1, n, 1, 1)
+    h = torch.arange(H).view(1, 1, H, 1)
+    b = torch.arange(B).view(B, 1, 1, 1)
+    idx = (t + 37 * h + 11 * b) % 256
+    c = codes[idx]
+    exps = torch.tensor([[[127, 128, 120, 134], [1, 254, 127, 100], [140, 127, 126, 129]],
+                         [[127, 127, 127, 127], [130, 90, 160, 127], [127, 2, 253, 127]]], dtype=torch.uint8)
+    got = oracle.dequant_fp8(c, exps)
+    scale = torch.pow(2.0, exps.double() - 127)  # [B, H, 4]
+    ref = ref_codes[idx] * scale.permute(0, 2, 1).repeat_interleave(64, dim=1).unsqueeze(-1)
+    r = ref.numpy()
+    same = (got == r) | (np.isnan(got) & np.isnan(r))
+    assert same.all(), ("fp8 decode", np.argwhere(~same)[:5])
+    assert np.isnan(got).sum() == np.isnan(r).sum() > 0
+
+
+def pin_fp8_attention_equals_decoded():
+    """Attention over 8-bit chunks equals attention over the same chunks
+    decoded by torch (ragged chunk lengths, GQA, causal offsets)."""
+    import torch
+
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, d, Lq = 2, 4, 2, 8, 5
+    q = torch.from_numpy(rng.normal(size=(B, Lq, Hq, d))).to(torch.bfloat16)
+    chunks8, chunks64, start = [], [], 0
+    for n in (70, 64, 3):
+        nb = (n + 63) // 64
+        k = torch.from_numpy(rng.normal(size=(B, n, Hkv, d)) * 3).to(torch.float8_e4m3fn)
+        v = torch.from_numpy(rng.normal(size=(B, n, Hkv, d))).to(torch.float8_e4m3fn)
+        ke = torch.from_numpy(rng.integers(122, 131, size=(B, Hkv, nb))).to(torch.uint8)
+        ve = torch.from_numpy(rng.integers(122, 131, size=(B, Hkv, nb))).to(torch.uint8)
+        def dec(x, e):
+            s = torch.pow(2.0, e.double() - 127).permute(0, 2, 1).repeat_interleave(64, dim=1)[:, :x.shape[1]]
+            return (x.double() * s.unsqueeze(-1)).numpy()
+        chunks8.append((k, v, start, ke, ve))
+        chunks64.append((dec(k, ke), dec(v, ve), start))
+        start += n
+    for causal, off in ((True, 130), (False, 0), (True, 66)):
+        a, la = oracle.attention(q, chunks8, off, causal)
+        b, lb = oracle.attention(q.double().numpy(), chunks64, off, causal)
+        _close(a, b, 1e-13, f"fp8 attention causal={causal} off={off}")
+        _close(la, lb, 1e-13, "fp8 lse")
+    st = oracle.ring(q, chunks8, order=[2, 0, 1], q_offset=130, causal=True)
+    o, _ = oracle.finalize(st)
+    ref, _ = oracle.attention(q.double().numpy(), chunks64, 130, True)
+    _close(o, ref, 1e-12, "fp8 ring")
+
+
 ALL_PINS = [
     pin_library_sdpa,
     pin_zero_query_mean,
@@ -417,4 +475,6 @@ ALL_PINS = [
     pin_causal_future_ignored,
     pin_rows_and_decode_positions,
     pin_input_types,
+    pin_fp8_decode_library,
+    pin_fp8_attention_equals_decoded,
 ]

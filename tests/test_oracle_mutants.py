@@ -48,6 +48,12 @@ MUTANTS = [
      "if (0) { /* no visible key: output 0 */", 1),
     ("bf16_truncated_mantissa", "uint32_t bits = (uint32_t)((const uint16_t *)p)[idx] << 16;",
      "uint32_t bits = ((uint32_t)((const uint16_t *)p)[idx] << 16) & 0xFFFF0000u & ~0x10000u;", 1),
+    ("fp8_fnuz_exponent_bias", "v = ldexp(8.0 + man, ex - 10);", "v = ldexp(8.0 + man, ex - 11);", 1),
+    ("fp8_subnormal_as_normal", "v = ldexp((double)man, -9);", "v = ldexp(8.0 + man, -10);", 1),
+    ("fp8_no_nan_code", "if (ex == 15 && man == 7)\n        return NAN;", "if (0)\n        return NAN;", 1),
+    ("fp8_scale_bias", "double scale = ldexp(1.0, e - 127);", "double scale = ldexp(1.0, e - 128);", 1),
+    ("fp8_scale_block_of_next_token", "exps[((int64_t)b * H + h) * nblk + t / block]",
+     "exps[((int64_t)b * H + h) * nblk + (t + 1) / block]", 1),
 ]
 
 
