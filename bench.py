@@ -49,7 +49,7 @@ MEASURED_TRAFFIC = {
 }
 
 HEADLINE = "prefill_bf16_h32_d128"
-SECONDARY = "decode_b4_gqa32x8_cache1m"
+SECONDARY = "decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8"
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -109,7 +109,11 @@ def algorithmic(wl):
     pairs = visible_pairs_fast(wl) * wl.B * wl.Hq
     flops = pairs * 2 * (wl.d_qk + wl.d_v)
     es = 2 if wl.dtype == "bf16" else 4
-    kv_bytes = sum(wl.lens()) * wl.B * wl.Hkv * (wl.d_qk + wl.d_v) * es
+    if wl.kv_dtype == "fp8":  # 1-byte codes plus one exponent byte per 64 tokens for K and for V
+        nblk = sum((n + 63) // 64 for n in wl.lens())
+        kv_bytes = sum(wl.lens()) * wl.B * wl.Hkv * (wl.d_qk + wl.d_v) + nblk * wl.B * wl.Hkv * 2
+    else:
+        kv_bytes = sum(wl.lens()) * wl.B * wl.Hkv * (wl.d_qk + wl.d_v) * es
     qo_bytes = wl.B * wl.Lq * wl.Hq * (wl.d_qk + wl.d_v) * es
     return flops, kv_bytes + qo_bytes
 
@@ -141,8 +145,8 @@ class WorkloadRun:
         ws = ra.ring_attn_workspace_size(self.x.q, self.chunks, wl.causal, wl.q_offset, self.flags)
         self.ws = torch.empty(max(ws, 1), device=device, dtype=torch.uint8)
         self.ctx = ra.RingAttnContext(torch.device(device).index or 0)
-        cls = ra.ring_attn_plan(wl.Lq, wl.q_offset, wl.causal, [s for (_, _, s) in self.chunks],
-                                [k.shape[1] for (k, _, _) in self.chunks])
+        cls = ra.ring_attn_plan(wl.Lq, wl.q_offset, wl.causal, [c[2] for c in self.chunks],
+                                [c[0].shape[1] for c in self.chunks])
         computed = sum(1 for c in cls if c != ra.RA_CHUNK_SKIP)
         # kernel launches of the dominant kernel per step
         self.launches = 1 if self.decode else computed
@@ -179,6 +183,8 @@ class WorkloadRun:
             roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name))
             metric, value, unit = "decode HBM GB/s at 1M KV", gbs, "GB/s"
+            if wl.kv_dtype == "fp8":
+                metric = "decode HBM GB/s at 1M KV (8-bit KV cache)"
         else:
             achieved = self.flops / self.launches / launch_s / 1e12
             peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS

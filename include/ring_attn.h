@@ -77,6 +77,16 @@ extern "C" {
 /* element types */
 #define RA_F32 0
 #define RA_BF16 1
+/* 8-bit KV cache (ra_desc.kv_dtype only): OCP FP8 E4M3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7f/0xff are
+ * NaN; largest finite 448).  Every RA_KV_SCALE_BLOCK consecutive tokens of
+ * one (batch, KV head) share the scale 2^(e - 127), e an 8-bit biased
+ * exponent in 1..254 (ra_kv_chunk.k_exp / v_exp): value = code x scale.
+ * The pages recommend an 8-bit KV cache for serving without fixing a
+ * format (page "billion-token context window engineering", production
+ * parameters; page "RingAttention与RAG技术对比及实战应用", §2.3). */
+#define RA_FP8_E4M3 2
+#define RA_KV_SCALE_BLOCK 64
 
 /* ring_attn_fwd flags */
 #define RA_FLAG_STAGE 1u      /* ring stand-in: copy each received chunk into a
@@ -97,12 +107,14 @@ typedef struct ra_desc {
     int32_t Hkv;   /* key/value heads; Hq % Hkv == 0                */
     int32_t d_qk;  /* query/key head size                           */
     int32_t d_v;   /* value/output head size                        */
-    int32_t dtype; /* RA_F32 or RA_BF16: q, k, v and out            */
+    int32_t dtype; /* RA_F32 or RA_BF16: q, out (and k, v)          */
     float scale;   /* logit scale; 0 selects 1/sqrt(d_qk)           */
-    int32_t reserved;
+    int32_t kv_dtype; /* element type of k and v: 0 (same as dtype) or
+                         RA_FP8_E4M3 (with dtype RA_BF16)            */
     int64_t q_strides[3]; /* q   [B, Lq, Hq, d_qk]: (batch, token, head) */
     int64_t k_strides[3]; /* k   [B, len, Hkv, d_qk], every chunk        */
     int64_t v_strides[3]; /* v   [B, len, Hkv, d_v],  every chunk        */
+    /* (all strides in elements: bytes for an 8-bit KV cache)             */
     int64_t o_strides[3]; /* out [B, Lq, Hq, d_v]                        */
 } ra_desc;
 
@@ -111,6 +123,10 @@ typedef struct ra_kv_chunk {
     const void *v;  /* device pointer to the chunk's values                */
     int64_t start;  /* absolute position of the chunk's first key          */
     int64_t len;    /* number of keys (ragged chunks allowed; 0 = empty)   */
+    /* 8-bit KV cache only (else NULL): device pointers to the biased scale
+     * exponents, dense [B, Hkv, ceil(len / RA_KV_SCALE_BLOCK)] uint8 */
+    const uint8_t *k_exp;
+    const uint8_t *v_exp;
 } ra_kv_chunk;
 
 typedef struct ra_ctx ra_ctx;
@@ -178,7 +194,10 @@ int ring_attn_workspace_size(const ra_desc *d, int64_t Lq,
  *   stream     hipStream_t
  * At least one of out / (m_out, l_out, O_out) must be given.
  * Supported: bf16 with d_qk == d_v in {64, 128, 512}; fp32 with d_qk == d_v
- * in {64, 128}; RA_ERR_UNSUPPORTED otherwise. */
+ * in {64, 128}; an 8-bit KV cache (kv_dtype RA_FP8_E4M3) with bf16 queries,
+ * d_qk == d_v == 128, on the split-KV schedule (incremental decoding, no
+ * STAGE); RA_ERR_UNSUPPORTED otherwise.  RA_ERR_INVALID_ARG if an 8-bit
+ * chunk with keys lacks k_exp or v_exp. */
 int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
                   const ra_kv_chunk *chunks, int P, int causal,
                   int64_t q_offset, uint32_t flags, void *out, float *m_out,

@@ -13,11 +13,18 @@ from .ring_attn import (  # noqa: F401
     RA_CHUNK_DIAG,
     RA_CHUNK_FULL,
     RA_CHUNK_SKIP,
+    RA_ERR_HIP,
+    RA_ERR_INVALID_ARG,
+    RA_ERR_UNSUPPORTED,
+    RA_ERR_WORKSPACE,
     RA_F32,
     RA_FLAG_ACCUMULATE,
     RA_FLAG_NO_SPLIT_KV,
     RA_FLAG_SPLIT_KV,
     RA_FLAG_STAGE,
+    RA_FP8_E4M3,
+    RA_KV_SCALE_BLOCK,
+    RA_OK,
     RingAttnContext,
     RingAttnError,
     ring_attn_fwd,

@@ -69,6 +69,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -851,6 +853,228 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
     write_results<D>(a, wt, row, g, hf * (D / 2), hf == 0, oacc, m_true, ltot);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 queries against an 8-bit KV cache (OCP FP8 E4M3 codes, one
+// power-of-two scale per 64 tokens of a (batch, KV head)), d = 128, split-KV
+// decoding.  Tiles of 128 keys go HBM -> LDS as raw bytes (16 KiB for K and
+// for V), so the cache is read at half the bytes of bf16.  Fragments are
+// widened to bf16 in registers with v_cvt_scalef32_pk_bf16_fp8, whose scale
+// operand applies the block's power of two exactly, and then feed the same
+// bf16 MFMAs, softmax and merge as the bf16 kernels.
+//  * LDS rows are keys (128 bytes = 8 units of 16 bytes); unit u of row r is
+//    stored at u ^ swz8(r), swz8(r) = 2((r>>1)&3) + ((r>>3)&1), which keeps
+//    both read patterns below free of bank conflicts.
+//  * K: one ds_read_b128 gives a lane 16 consecutive dimensions of its key,
+//    i.e. the A fragments of two MFMAs.  The contraction order is permuted to
+//    match: MFMA 2c+h takes dimensions 32c + 16g + 8h + j in lane group g,
+//    and the query fragments are loaded in that order.
+//  * V^T: one ds_read_b64_tr_b8 gives each lane 8 keys of one dimension.  In
+//    a group of 16 lanes, lane i receives byte i%8 of the 8-byte rows that
+//    lanes 2k + i/8 address (k = 0..7); lanes address the keys in the order
+//    of the probability fragments (keys 4g..4g+3, 8+4g..8+4g+3 of each 16).
+// ---------------------------------------------------------------------------
+namespace fp8kv {
+constexpr int D = 128;           // head size
+constexpr int BN = 128;          // keys per tile
+constexpr int ROWB = D;          // bytes per key row in LDS
+constexpr int TILE = BN * ROWB;  // bytes of one K (or V) tile
+constexpr int NW = 4;            // waves: 2 row blocks x 2 key halves
+constexpr int LOADS_PER_WAVE = TILE / 1024 / NW;
+constexpr int BLOCK = 64;        // tokens per scale exponent (= keys per wave per tile)
+using C = Cfg<D, BN, NW, 2>;     // row/key geometry: 64 rows, 64 keys per wave, KB = 2
+static_assert(C::KW == BLOCK, "each wave's keys of a tile share one scale block");
+
+__device__ inline int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+
+// Scale 2^(e-127) of a biased exponent e in 1..254, as a float.
+__device__ inline float exp_scale(unsigned e) { return __builtin_bit_cast(float, e << 23); }
+
+// 8 E4M3 codes (bytes of w) -> 8 bf16 values times the power-of-two scale.
+__device__ inline bf16x8 widen(u32x2 w, float scale) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], scale, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], scale, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], scale, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], scale, true);
+    const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline void load_tile(const uint8_t *base, int64_t stride, int64_t k0, int64_t kend, char *dst, int w,
+                                 int lane) {
+    const unsigned stride_b = (unsigned)stride;
+    const unsigned nvalid = (unsigned)(kend - k0 < BN ? kend - k0 : BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + k0 * stride), (short)0, (int)(nvalid * stride_b), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+        const int inst = j * NW + w;
+        const int pos = inst * 64 + lane;
+        const int r = pos / (ROWB / 16), u = (pos % (ROWB / 16)) ^ swz8(r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + inst * 1024), 16,
+                                                 (unsigned)r * stride_b + (unsigned)(u * 16), 0, 0, 0);
+    }
+}
+}  // namespace fp8kv
+
+template <int NS>
+__global__ __launch_bounds__(fp8kv::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8kv_kernel(const FwdArgs a) {
+    using namespace fp8kv;
+    constexpr int LPT = 2 * LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(NS, TILE)
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int wr = w % C::ROWW, wk = w / C::ROWW;
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;
+    token_range(a, wt.p0 + 32 * wr, wt.p0 + 32 * wr + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * wr + l32);
+
+    // query fragments in the permuted contraction order: qf[2c+h] holds
+    // dimensions 32c + 16g + 8h .. +8
+    bf16x8 qf[C::DS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + wt.b * a.q_sb + row.t * a.q_ss + row.h * a.q_sh + 16 * g;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row.ok) v = *(const u32x4 *)(qp + 32 * (ds / 2) + 8 * (ds % 2));
+            qf[ds] = to_bf16x8(v);
+        }
+    }
+    f32x16 oacc[C::DB];
+    float m_run, m_true, lsum;
+    load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+    const float c2 = a.scale_log2;
+
+    // per-lane LDS byte addresses (tile-relative)
+    int kaddr[D / 32];  // K: row wk*64 + l32, units 2c + g
+    {
+        const int r = wk * C::KW + l32;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kaddr[c] = r * ROWB + 16 * ((2 * c + g) ^ swz8(l32));
+    }
+    int vaddr[C::DB];  // V^T provider row wk*64 + keyofs, unit 2db + (G&1), half p&1
+    {
+        const int G = lane >> 4, p = lane & 15, kk = p >> 1;
+        const int keyofs = kk < 4 ? 4 * (G >> 1) + kk : 8 + 4 * (G >> 1) + (kk - 4);
+        const int r = wk * C::KW + keyofs;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+            vaddr[db] = r * ROWB + 16 * ((2 * db + (G & 1)) ^ swz8(keyofs)) + 8 * (p & 1);
+    }
+
+    int c_begin = 0, c_end = a.n_chunks, sub = 0;
+    if (a.split_mode) {
+        c_begin = wt.split / a.n_sub;
+        sub = wt.split % a.n_sub;
+        c_end = c_begin + 1;
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
+        const uint8_t *kbase = (const uint8_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint8_t *vbase = (const uint8_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        const int64_t nblk = (ch.len + BLOCK - 1) / BLOCK;
+        const uint8_t *kexp = ch.kexp + ((int64_t)wt.b * a.Hkv + wt.hk) * nblk;
+        const uint8_t *vexp = ch.vexp + ((int64_t)wt.b * a.Hkv + wt.hk) * nblk;
+        auto issue = [&](auto u, int t) {
+            const int64_t k0 = kbeg + (int64_t)t * BN;
+            load_tile(kbase, a.k_ss, k0, kend, kst(u), w, lane);
+            load_tile(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+        };
+        auto wait_for = [&](int need, int last) {
+            const int after = last - need;
+            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+        };
+
+        tile_barrier();  // the previous chunk's tiles are no longer read
+        const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
+        for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+        wait_for(0, pre - 1);
+        for_tiles<NS>(ntiles, [&](auto u, int it) {
+            constexpr int U = decltype(u)::value;
+            if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+            const int64_t k0 = kbeg + (int64_t)it * BN;
+            const int64_t wk0 = k0 + wk * C::KW;  // this wave's 64 keys: one scale block
+            const bool skip = (a.causal && ch.start + wk0 > a.q_offset + wv_thi) || wk0 >= kend;
+            const bool full = wk0 + C::KW <= kend &&
+                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
+            if (!skip) {
+                const int64_t blk = wk0 / BLOCK;
+                const float ks = exp_scale(kexp[blk]), vs = exp_scale(vexp[blk]);
+                const char *kt = kst(u);
+                const char *vt = vst(u);
+                f32x16 s[C::KB];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < D / 32; ++cc) {
+                        const u32x4 raw = *reinterpret_cast<const u32x4 *>(kt + kaddr[cc] + kb * 32 * ROWB);
+                        s[kb] = mfma(widen(u32x2{raw[0], raw[1]}, ks), qf[2 * cc], s[kb]);
+                        s[kb] = mfma(widen(u32x2{raw[2], raw[3]}, ks), qf[2 * cc + 1], s[kb]);
+                    }
+                }
+                if (!full) mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
+                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                bf16x8 pf[2 * C::KB];
+                probabilities<C>(s, c2, m_run, lsum, pf);
+#pragma unroll
+                for (int kss = 0; kss < 2 * C::KB; ++kss)
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        const u32x2 raw = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                       (__attribute__((address_space(3))) i32x2 *)(vt + vaddr[db] + kss * 16 * ROWB)));
+                        oacc[db] = mfma(widen(raw, vs), pf[kss], oacc[db]);
+                    }
+            }
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
+        });
+    }
+
+    renormalise(m_run, m_true, lsum, oacc);
+    // the key-half waves (wk = 1) hand their state to wave wk = 0 of the same rows
+    __syncthreads();
+    float *slot = reinterpret_cast<float *>(wr == 0 ? kv0 : kv1);  // (16 DB + 2) x 64 floats
+    if (wk == 1) {
+        slot[lane] = m_true;
+        slot[64 + lane] = lsum;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) slot[(2 + 16 * db + i) * 64 + lane] = oacc[db][i];
+    }
+    __syncthreads();
+    if (wk == 1) return;
+    {
+        const float m1 = slot[lane], l1 = slot[64 + lane];
+        const float mn = fmaxf(m_true, m1);
+        if (mn != kNegInf) {
+            const float a0 = m_true == kNegInf ? 0.f : exp2_fast(m_true - mn);
+            const float a1 = m1 == kNegInf ? 0.f : exp2_fast(m1 - mn);
+            lsum = a0 * lsum + a1 * l1;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] = a0 * oacc[db][i] + a1 * slot[(2 + 16 * db + i) * 64 + lane];
+            m_true = mn;
+        }
+    }
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    write_results<D>(a, wt, row, g, 0, true, oacc, m_true, ltot);
+}
+
 template <class C, class K>
 hipError_t launch(K kernel, const FwdArgs &a, hipStream_t s) {
     const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
@@ -873,6 +1097,12 @@ int fwd_bf16_row_tile(int d, bool split_mode) {
     if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, RA_TUNE_BN128, 4, 1>::BM;
     if (d == 512) return CfgHalf<512, 32, 2>::BM;
     return 0;
+}
+
+int fwd_fp8kv_row_tile() { return fp8kv::C::BM; }
+
+hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s) {
+    return launch<fp8kv::C>(fwd_fp8kv_kernel<2>, a, s);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s) {

@@ -15,6 +15,7 @@ struct ChunkArg {
     const void *v;
     int64_t start;  // absolute position of key 0
     int64_t len;    // keys in the chunk
+    const uint8_t *kexp, *vexp;  // 8-bit KV: biased scale exponents [B, Hkv, ceil(len/64)]
 };
 
 // Arguments of the forward kernels (bf16 MFMA and fp32 paths).
@@ -62,6 +63,9 @@ struct MergeArgs {
 // launch error; bm_out reports the row tile the kernel uses.
 int fwd_bf16_row_tile(int d, bool split_mode);
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s);
+// bf16 queries against an 8-bit (FP8 E4M3) KV cache, d = 128, split-KV only
+int fwd_fp8kv_row_tile();
+hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s);
 int fwd_f32_row_tile(int d);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);

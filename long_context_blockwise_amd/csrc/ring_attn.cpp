@@ -66,6 +66,15 @@ struct Strides {
 
 int elem_size(int dtype) { return dtype == RA_BF16 ? 2 : 4; }
 
+// 8-bit KV cache (bf16 queries, FP8 E4M3 keys/values with block exponents)
+bool kv_fp8(const ra_desc *d) { return d->kv_dtype == RA_FP8_E4M3; }
+
+// Query rows per workgroup of the kernel a schedule launches.
+int row_tile(const ra_desc *d, bool split) {
+    if (kv_fp8(d) && split) return ra::fwd_fp8kv_row_tile();
+    return d->dtype == RA_BF16 ? ra::fwd_bf16_row_tile(d->d_qk, split) : ra::fwd_f32_row_tile(d->d_qk);
+}
+
 bool supported_head(int dtype, int d) {
     if (dtype == RA_BF16) return d == 64 || d == 128 || d == 512;
     if (dtype == RA_F32) return d == 64 || d == 128;
@@ -82,8 +91,14 @@ int check_desc(const ra_desc *d, int64_t Lq, Strides *st) {
     if (Lq < 0) return fail(RA_ERR_INVALID_ARG, "Lq must be >= 0");
     if (d->d_qk != d->d_v || !supported_head(d->dtype, d->d_qk))
         return fail(RA_ERR_UNSUPPORTED, "head sizes d_qk=%d d_v=%d not built for dtype %d", d->d_qk, d->d_v, d->dtype);
-    const int align = d->dtype == RA_BF16 ? 8 : 4;
+    if (d->kv_dtype != 0 && d->kv_dtype != d->dtype && d->kv_dtype != RA_FP8_E4M3)
+        return fail(RA_ERR_INVALID_ARG, "kv_dtype %d unknown", d->kv_dtype);
+    if (kv_fp8(d) && (d->dtype != RA_BF16 || d->d_qk != 128))
+        return fail(RA_ERR_UNSUPPORTED, "an 8-bit KV cache is built for bf16 queries with d = 128");
+    const int qalign = d->dtype == RA_BF16 ? 8 : 4;  // elements of 16-byte units
+    const int kvalign = kv_fp8(d) ? 16 : qalign;
     auto fill = [&](const int64_t *in, int64_t *out, int64_t S, int64_t H, int64_t D, const char *name) -> int {
+        const int align = name[0] == 'k' || name[0] == 'v' ? kvalign : qalign;
         if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
             out[2] = D;
             out[1] = H * D;
@@ -205,7 +220,13 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
     pl->rows = (int64_t)d->B * Lq * d->Hq;
     pl->stage = (flags & RA_FLAG_STAGE) != 0;
     pl->split = !pl->stage && !(flags & RA_FLAG_NO_SPLIT_KV) &&
-                ((flags & RA_FLAG_SPLIT_KV) || (Lq > 0 && Lq <= kSplitMaxLq));
+                ((flags & RA_FLAG_SPLIT_KV) || (Lq > 0 && Lq <= kSplitMaxLq) || kv_fp8(d));
+    if (kv_fp8(d)) {  // the 8-bit cache is read in place by the split-KV schedule only
+        if (!pl->split) return fail(RA_ERR_UNSUPPORTED, "an 8-bit KV cache needs the split-KV schedule (no STAGE / NO_SPLIT_KV)");
+        for (int c = 0; c < P; ++c)
+            if (chunks[c].len > 0 && (!chunks[c].k_exp || !chunks[c].v_exp))
+                return fail(RA_ERR_INVALID_ARG, "chunk %d: an 8-bit KV chunk needs k_exp and v_exp", c);
+    }
     for (int c = 0; c < P; ++c)
         if (classify(Lq, q_offset, causal, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP) pl->steps.push_back(c);
 
@@ -228,7 +249,7 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
     }
     if (pl->split) {
         // sub-ranges per chunk: enough workgroups to fill the GPU, whole key tiles
-        const int bm = d->dtype == RA_BF16 ? ra::fwd_bf16_row_tile(d->d_qk, true) : ra::fwd_f32_row_tile(d->d_qk);
+        const int bm = row_tile(d, true);
         const int64_t rowtiles = (pl->G * Lq + bm - 1) / bm;
         const int64_t base_wg = (int64_t)d->B * d->Hkv * rowtiles * (int64_t)std::max<size_t>(pl->steps.size(), 1);
         int64_t maxlen = 1;
@@ -272,7 +293,7 @@ FwdArgs base_args(const ra_desc *d, const Strides &st, const void *q, int64_t Lq
 
 // Row tiling: prefill keeps each row tile inside one head; decode packs heads.
 void set_rows(FwdArgs &a, const ra_desc *d, bool split) {
-    const int bm = d->dtype == RA_BF16 ? ra::fwd_bf16_row_tile(d->d_qk, split) : ra::fwd_f32_row_tile(d->d_qk);
+    const int bm = row_tile(d, split);
     if (split || a.Lq * a.G <= bm) {
         a.Lq_pad = a.Lq;  // packed
     } else {
@@ -282,6 +303,7 @@ void set_rows(FwdArgs &a, const ra_desc *d, bool split) {
 }
 
 hipError_t launch_fwd(const FwdArgs &a, const ra_desc *d, bool split, hipStream_t s) {
+    if (kv_fp8(d) && split) return ra::launch_fwd_fp8kv(a, s);
     return d->dtype == RA_BF16 ? ra::launch_fwd_bf16(a, d->d_qk, split, s) : ra::launch_fwd_f32(a, d->d_qk, s);
 }
 
@@ -310,7 +332,7 @@ struct DeviceGuard {
 
 extern "C" {
 
-const char *ring_attn_version(void) { return "ringattn 0.1 (gfx950)"; }
+const char *ring_attn_version(void) { return "ringattn 0.2 (gfx950)"; }
 
 const char *ring_attn_last_error(void) { return g_err.c_str(); }
 
@@ -453,7 +475,7 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
                 if (nsub != nsub0) break;
                 if (dense_kv(d->k_strides) || dense_kv(d->v_strides))
                     if (ch.len != len0) break;  // dense strides depend on the length
-                a.chunks[a.n_chunks++] = ChunkArg{ch.k, ch.v, ch.start, ch.len};
+                a.chunks[a.n_chunks++] = ChunkArg{ch.k, ch.v, ch.start, ch.len, ch.k_exp, ch.v_exp};
                 ++j;
             }
             set_chunk_strides(a, d, len0);

@@ -21,6 +21,17 @@ Workloads (one device's share of the ring, shapes from the pages' settings):
 * ``decode_b4_gqa32x8_cache1m``: 4 sequences, 32 query / 8 KV heads, d=128,
   bf16, a 1,048,576-token KV cache in 64 chunks of 16384; 16 new query tokens
   at cache_idx = 1,048,560 (their K/V are the cache's last 16 slots), causal.
+* ``decode_b4_gqa32x8_cache1m_fp8``: the same decode with the KV cache held
+  in 8 bits (OCP FP8 E4M3, one power-of-two scale per 64 tokens of a
+  (batch, KV head)); queries stay bf16.
+
+8-bit KV caches are drawn like the others and then quantised block by block
+(input preparation, not the method): each block of 64 tokens x d values of
+one (batch, KV head) gets the scale 2^e with the smallest e for which its
+largest magnitude fits under 448, and the values divided by the scale are
+rounded to E4M3 (round to nearest even).  Chunks of such workloads are
+``(k, v, start, k_exp, v_exp)`` with k, v ``torch.float8_e4m3fn`` and the
+biased exponents e + 127 as ``uint8 [B, Hkv, ceil(len/64)]``.
 """
 from __future__ import annotations
 
@@ -50,6 +61,7 @@ class Workload:
     seed: int
     # explicit per-chunk lengths (ragged tails); None means all chunk_len
     chunk_lens: Optional[Tuple[int, ...]] = field(default=None)
+    kv_dtype: Optional[str] = None  # None: same as dtype; "fp8": 8-bit KV cache
 
     @property
     def torch_dtype(self):
@@ -90,7 +102,33 @@ WORKLOADS = {
                                           chunk_len=16384, P=64, Lq=16,
                                           q_offset=1048560, causal=True, std=0.5,
                                           seed=5),
+    "decode_b4_gqa32x8_cache1m_fp8": Workload("decode_b4_gqa32x8_cache1m_fp8", B=4, Hq=32,
+                                              Hkv=8, d_qk=128, d_v=128, dtype="bf16",
+                                              chunk_len=16384, P=64, Lq=16,
+                                              q_offset=1048560, causal=True, std=0.5,
+                                              seed=5, kv_dtype="fp8"),
 }
+
+KV_SCALE_BLOCK = 64  # tokens per shared exponent of an 8-bit KV cache
+FP8_MAX = 448.0      # largest finite OCP FP8 E4M3 value
+
+
+def quantize_fp8(x: torch.Tensor, block: int = KV_SCALE_BLOCK):
+    """``x [B, n, H, d]`` -> (E4M3 codes as ``torch.float8_e4m3fn`` [B, n, H, d],
+    biased exponents ``uint8 [B, H, ceil(n/block)]``)."""
+    B, n, H, d = x.shape
+    nb = (n + block - 1) // block
+    xf = x.float()
+    pad = torch.zeros((B, nb * block - n, H, d), dtype=xf.dtype, device=xf.device)
+    blocks = torch.cat([xf, pad], 1).view(B, nb, block, H, d)
+    amax = blocks.abs().amax(dim=(2, 4))  # [B, nb, H]
+    e = torch.ceil(torch.log2(torch.clamp(amax, min=2.0 ** -100) / FP8_MAX))
+    e = torch.clamp(e, -126, 127)
+    scale = torch.pow(2.0, e)  # exact powers of two
+    per_token = scale.repeat_interleave(block, dim=1)[:, :n].unsqueeze(-1)  # [B, n, H, 1]
+    codes = (xf / per_token).to(torch.float8_e4m3fn)
+    exps = (e + 127).to(torch.uint8).permute(0, 2, 1).contiguous()  # [B, H, nb]
+    return codes, exps
 
 
 def _generator(device, seed: int, tensor: int, chunk: int) -> torch.Generator:
@@ -116,10 +154,15 @@ class Inputs:
     ks: List[torch.Tensor]  # chunk c: [B, len_c, Hkv, d_qk]
     vs: List[torch.Tensor]  # chunk c: [B, len_c, Hkv, d_v]
     starts: List[int]
+    k_exps: Optional[List[torch.Tensor]] = None  # 8-bit KV: [B, Hkv, ceil(len_c/64)]
+    v_exps: Optional[List[torch.Tensor]] = None
 
     def chunks(self, order=None):
-        """``[(k, v, start)]`` in ``order`` (default: chunk index order)."""
+        """``[(k, v, start)]`` (8-bit KV: ``(k, v, start, k_exp, v_exp)``) in
+        ``order`` (default: chunk index order)."""
         idx = range(len(self.ks)) if order is None else order
+        if self.k_exps is not None:
+            return [(self.ks[c], self.vs[c], self.starts[c], self.k_exps[c], self.v_exps[c]) for c in idx]
         return [(self.ks[c], self.vs[c], self.starts[c]) for c in idx]
 
 
@@ -129,12 +172,18 @@ def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:
     q = draw((wl.B, wl.Lq, wl.Hq, wl.d_qk), wl.std if q_std is None else q_std, dt,
              device, wl.seed, _TENSOR_Q)
     ks, vs = [], []
+    kes, ves = ([], []) if wl.kv_dtype == "fp8" else (None, None)
     for c, n in enumerate(wl.lens()):
-        ks.append(draw((wl.B, n, wl.Hkv, wl.d_qk), wl.std, dt, device, wl.seed,
-                       _TENSOR_K, c))
-        vs.append(draw((wl.B, n, wl.Hkv, wl.d_v), wl.std, dt, device, wl.seed,
-                       _TENSOR_V, c))
-    return Inputs(wl, q, ks, vs, wl.starts())
+        k = draw((wl.B, n, wl.Hkv, wl.d_qk), wl.std, dt, device, wl.seed, _TENSOR_K, c)
+        v = draw((wl.B, n, wl.Hkv, wl.d_v), wl.std, dt, device, wl.seed, _TENSOR_V, c)
+        if kes is not None:
+            k, ke = quantize_fp8(k)
+            v, ve = quantize_fp8(v)
+            kes.append(ke)
+            ves.append(ve)
+        ks.append(k)
+        vs.append(v)
+    return Inputs(wl, q, ks, vs, wl.starts(), kes, ves)
 
 
 def sample_rows(Lq: int, tile: int = 128, seed: int = 0, extra=()) -> List[int]:

@@ -24,6 +24,8 @@ RA_ERR_UNSUPPORTED = -2
 RA_ERR_WORKSPACE = -3
 RA_ERR_HIP = -4
 RA_F32, RA_BF16 = 0, 1
+RA_FP8_E4M3 = 2          # kv_dtype: 8-bit KV cache (OCP FP8 E4M3 + block exponents)
+RA_KV_SCALE_BLOCK = 64   # tokens per scale exponent of an 8-bit KV cache
 RA_FLAG_STAGE = 1
 RA_FLAG_SPLIT_KV = 2
 RA_FLAG_NO_SPLIT_KV = 4
@@ -44,14 +46,14 @@ class RingAttnError(RuntimeError):
 class ra_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
                 ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3)]
 
 
 class ra_kv_chunk(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("start", ctypes.c_int64),
-                ("len", ctypes.c_int64)]
+                ("len", ctypes.c_int64), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
 
 
 _lib = None
@@ -177,7 +179,11 @@ def _strides(t) -> Tuple[int, int, int]:
 
 
 def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]:
-    """ra_desc and the ra_kv_chunk array for a query tensor and (k, v, start) chunks."""
+    """ra_desc and the ra_kv_chunk array for a query tensor and chunks
+    ``(k, v, start)``, or ``(k, v, start, k_exp, v_exp)`` for an 8-bit KV cache
+    (k, v ``torch.float8_e4m3fn``; exponents ``uint8 [B, Hkv, ceil(len/64)]``)."""
+    import torch
+
     B, Lq, Hq, dqk = q.shape
     if not chunks:
         raise RingAttnError(RA_ERR_INVALID_ARG, "at least one chunk is needed to know Hkv/d_v")
@@ -189,22 +195,36 @@ def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]
     d.q_strides[:] = _strides(q)
     if out is not None:
         d.o_strides[:] = _strides(out)
-    dense = all(k.is_contiguous() and v.is_contiguous() for (k, v, _) in chunks)
+    fp8 = k0.dtype == torch.float8_e4m3fn
+    d.kv_dtype = RA_FP8_E4M3 if fp8 else 0
+    dense = all(c[0].is_contiguous() and c[1].is_contiguous() for c in chunks)
     if not dense:
         ks, vs = _strides(k0), _strides(v0)
-        for (k, v, _) in chunks:
+        for (k, v) in ((c[0], c[1]) for c in chunks):
             if _strides(k) != ks or _strides(v) != vs:
                 raise RingAttnError(RA_ERR_INVALID_ARG, "non-contiguous chunks must share strides")
         d.k_strides[:] = ks
         d.v_strides[:] = vs
     arr = (ra_kv_chunk * len(chunks))()
-    for i, (k, v, start) in enumerate(chunks):
-        if k.dtype != q.dtype or v.dtype != q.dtype:
-            raise RingAttnError(RA_ERR_INVALID_ARG, "q, k and v must share a dtype")
+    for i, c in enumerate(chunks):
+        k, v, start = c[0], c[1], c[2]
+        kv_dt = torch.float8_e4m3fn if fp8 else q.dtype
+        if k.dtype != kv_dt or v.dtype != kv_dt:
+            raise RingAttnError(RA_ERR_INVALID_ARG, "k and v must share one dtype (q's, or float8_e4m3fn)")
         arr[i].k = k.data_ptr()
         arr[i].v = v.data_ptr()
         arr[i].start = int(start)
         arr[i].len = int(k.shape[1])
+        if fp8:
+            if len(c) != 5:
+                raise RingAttnError(RA_ERR_INVALID_ARG, "8-bit chunks are (k, v, start, k_exp, v_exp)")
+            ke, ve = c[3], c[4]
+            nb = (int(k.shape[1]) + RA_KV_SCALE_BLOCK - 1) // RA_KV_SCALE_BLOCK
+            for e in (ke, ve):
+                if e.dtype != torch.uint8 or not e.is_contiguous() or tuple(e.shape) != (B, d.Hkv, nb):
+                    raise RingAttnError(RA_ERR_INVALID_ARG, f"exponents must be contiguous uint8 [{B}, {d.Hkv}, {nb}]")
+            arr[i].k_exp = ke.data_ptr()
+            arr[i].v_exp = ve.data_ptr()
     return d, arr
 
 

@@ -45,7 +45,8 @@ def check(got, ref, dtype: str, what: str = "", rel_l2=True):
 
 
 def to_host(chunks):
-    return [(k.cpu(), v.cpu(), s) for (k, v, s) in chunks]
+    """Chunks with their tensors on the host (8-bit chunks keep their exponents)."""
+    return [tuple(t.cpu() if hasattr(t, "cpu") else t for t in c) for c in chunks]
 
 
 def oracle_out(q, chunks, q_offset, causal, rows=None, scale=None):
@@ -79,8 +80,13 @@ def sampled_reference(q, chunks, q_offset, causal, rows, kv_heads, batches=None)
     for b in (range(B) if batches is None else batches):
         for hk in kv_heads:
             qs = q[b:b + 1, :, hk * G:(hk + 1) * G].cpu().contiguous()
-            cs = [(k[b:b + 1, :, hk:hk + 1].cpu().contiguous(), v[b:b + 1, :, hk:hk + 1].cpu().contiguous(), s)
-                  for (k, v, s) in chunks]
+            cs = []
+            for c in chunks:
+                k, v, s = c[0], c[1], c[2]
+                cut = (k[b:b + 1, :, hk:hk + 1].cpu().contiguous(), v[b:b + 1, :, hk:hk + 1].cpu().contiguous(), s)
+                if len(c) == 5:  # 8-bit chunk: exponents [B, Hkv, nblk] of the same (batch, head)
+                    cut += (c[3][b:b + 1, hk:hk + 1].cpu().contiguous(), c[4][b:b + 1, hk:hk + 1].cpu().contiguous())
+                cs.append(cut)
             out, _ = oracle.attention(qs, cs, q_offset, causal, rows=rows)
             res[(b, hk)] = out
     return res

@@ -193,3 +193,50 @@ def test_context_needs_a_device(lib):
         pytest.skip("a GPU is present")
     h = ctypes.c_void_p()
     assert lib.ring_attn_ctx_create(0, ctypes.byref(h)) == rb.RA_ERR_HIP
+
+
+def test_struct_layouts_match_the_header():
+    assert ctypes.sizeof(rb.ra_desc) == 8 * 4 + 12 * 8
+    assert ctypes.sizeof(rb.ra_kv_chunk) == 6 * 8
+    assert rb.ra_desc.kv_dtype.offset == 7 * 4
+    assert rb.ra_kv_chunk.k_exp.offset == 32 and rb.ra_kv_chunk.v_exp.offset == 40
+
+
+def test_fp8_kv_validation(lib):
+    def fp8_desc(**kw):
+        d = _desc(**kw)
+        d.kv_dtype = rb.RA_FP8_E4M3
+        return d
+
+    def fp8_chunks(lens, start=0):
+        arr = _chunks(lens, start)
+        for i in range(len(lens)):
+            arr[i].k_exp = arr[i].v_exp = 1 << 12
+        return arr
+
+    d, arr = fp8_desc(), fp8_chunks([256, 100])
+    # decode-sized and longer query blocks both take the split-KV schedule: partial states
+    for Lq in (4, 64):
+        rc, n = _ws(lib, d, Lq, arr, 2, 1, 300, 0, 1)
+        assert rc == 0 and n > 0 and n % (2 * Lq * 4 * (128 + 2) * 4) == 0
+    # the 8-bit cache is read in place by split-KV only
+    for flags in (ra.RA_FLAG_STAGE, ra.RA_FLAG_NO_SPLIT_KV):
+        assert _ws(lib, d, 4, arr, 2, 1, 300, flags, 1)[0] == rb.RA_ERR_UNSUPPORTED
+    # both exponent arrays are required for chunks with keys
+    arr[1].v_exp = None
+    assert _ws(lib, d, 4, arr, 2, 1, 300, 0, 1)[0] == rb.RA_ERR_INVALID_ARG
+    empty = fp8_chunks([256, 0])
+    empty[1].k_exp = empty[1].v_exp = None
+    assert _ws(lib, d, 4, empty, 2, 1, 300, 0, 1)[0] == 0
+    # built for bf16 queries with d = 128
+    assert _ws(lib, fp8_desc(d=64), 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_UNSUPPORTED
+    assert _ws(lib, fp8_desc(dtype=ra.RA_F32), 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_UNSUPPORTED
+    # unknown kv dtypes; 8-bit strides are whole 16-byte units
+    bad = fp8_desc()
+    bad.kv_dtype = 9
+    assert _ws(lib, bad, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_INVALID_ARG
+    st = fp8_desc()
+    st.k_strides[:] = (64 * 2 * 136, 2 * 136, 136)
+    assert _ws(lib, st, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_INVALID_ARG
+    st.k_strides[:] = (64 * 2 * 144, 2 * 144, 144)
+    assert _ws(lib, st, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == 0

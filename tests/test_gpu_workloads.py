@@ -1,4 +1,4 @@
-"""The five workloads at full size, in the launch configuration bench.py
+"""The workloads at full size, in the launch configuration bench.py
 times (bench.WorkloadRun: staged ring for prefill shares, split-KV + merge
 for decoding), checked against the oracle on sampled outputs the oracle
 computes row by row: stratified query rows (one per tile plus tile and
@@ -27,6 +27,7 @@ CASES = {
     "ring_1m_gqa32x8_d128": (4096, [0, 5], None),
     "mla_h16_d512": (1024, [0], None),
     "decode_b4_gqa32x8_cache1m": (1, [0, 7], [0, 3]),
+    "decode_b4_gqa32x8_cache1m_fp8": (1, [0, 7], [0, 3]),
 }
 
 
