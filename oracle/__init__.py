@@ -66,10 +66,10 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_threads.restype = i32
     lib.oracle_attention.restype = i32
     lib.oracle_attention.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64,
-                                     i32, vp, vp, vp, vp, i32, dbl, i64, vp, vp, vp]
+                                     i32, vp, vp, vp, vp, i32, i64, dbl, i64, vp, vp, vp]
     lib.oracle_ring_step.restype = i32
     lib.oracle_ring_step.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64,
-                                     vp, vp, i64, i64, i32, dbl, i64, vp, vp, vp, vp]
+                                     vp, vp, i64, i64, i32, i64, dbl, i64, vp, vp, vp, vp]
     lib.oracle_state_init.restype = None
     lib.oracle_state_init.argtypes = [i64, i32, vp, vp, vp]
     lib.oracle_merge.restype = None
@@ -211,14 +211,16 @@ def _scale(scale, dqk):
 # entry points
 # --------------------------------------------------------------------------- #
 def attention(q, chunks, q_offset=0, causal=False, scale=None, rows=None,
-              dtype=None, Hkv=None, dv=None):
+              dtype=None, Hkv=None, dv=None, window=0):
     """Plain attention of the query rows ``rows`` against all keys of ``chunks``.
 
     ``chunks`` is a list of ``(k, v, start)``: k ``[B, len, Hkv, d_qk]``, v
     ``[B, len, Hkv, d_v]`` holding the keys at absolute positions
     ``start .. start+len-1``.  Query row r sits at position ``q_offset + r``.
-    Returns ``(out [B, n_rows, Hq, d_v], lse [B, Hq, n_rows])`` in float64;
-    a row that sees no key gets out = 0 and lse = -inf.
+    ``window > 0`` limits a query at p to keys at distance <= window (keys
+    p - window .. p when causal).  Returns ``(out [B, n_rows, Hq, d_v], lse
+    [B, Hq, n_rows])`` in float64; a row that sees no key gets out = 0 and
+    lse = -inf.
     """
     lib = _get_lib()
     p = _Problem(q, chunks, dtype, rows)
@@ -235,7 +237,7 @@ def attention(q, chunks, q_offset=0, causal=False, scale=None, rows=None,
     ln = np.asarray(p.lens if n else [0], dtype=np.int64)
     rc = lib.oracle_attention(p.B, p.Hq, Hkv, p.dqk, dv, p.code, _ptr(p.q), p.Lq,
                               int(q_offset), n, kp, vp, _ptr(st), _ptr(ln),
-                              int(bool(causal)), _scale(scale, p.dqk), p.nr,
+                              int(bool(causal)), int(window), _scale(scale, p.dqk), p.nr,
                               _ptr(p.rows), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attention failed ({rc})")
@@ -260,7 +262,7 @@ class State:
 
 
 def ring_step(state: State, q, chunk, q_offset=0, causal=False, scale=None,
-              rows=None, dtype=None) -> State:
+              rows=None, dtype=None, window=0) -> State:
     """Fold one KV chunk ``(k, v, start)`` into ``state`` in place."""
     lib = _get_lib()
     p = _Problem(q, [chunk], dtype, rows)
@@ -268,7 +270,7 @@ def ring_step(state: State, q, chunk, q_offset=0, causal=False, scale=None,
         raise ValueError("state shape does not match the problem")
     rc = lib.oracle_ring_step(p.B, p.Hq, p.Hkv, p.dqk, p.dv, p.code, _ptr(p.q),
                               p.Lq, int(q_offset), _ptr(p.ks[0]), _ptr(p.vs[0]),
-                              p.starts[0], p.lens[0], int(bool(causal)),
+                              p.starts[0], p.lens[0], int(bool(causal)), int(window),
                               _scale(scale, p.dqk), p.nr, _ptr(p.rows),
                               _ptr(state.m), _ptr(state.l), _ptr(state.O))
     if rc != 0:
@@ -277,7 +279,7 @@ def ring_step(state: State, q, chunk, q_offset=0, causal=False, scale=None,
 
 
 def ring(q, chunks, order=None, q_offset=0, causal=False, scale=None, rows=None,
-         dtype=None) -> State:
+         dtype=None, window=0) -> State:
     """One device's share of the ring: fold the chunks in ``order`` (default:
     list order) into a fresh state and return it."""
     qa, _ = _to_numpy(q, dtype)
@@ -286,7 +288,7 @@ def ring(q, chunks, order=None, q_offset=0, causal=False, scale=None, rows=None,
     dv = int(chunks[0][1].shape[3])
     st = State(B, Hq, nr, dv)
     for c in (range(len(chunks)) if order is None else order):
-        ring_step(st, q, chunks[c], q_offset, causal, scale, rows, dtype)
+        ring_step(st, q, chunks[c], q_offset, causal, scale, rows, dtype, window)
     return st
 
 

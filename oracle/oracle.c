@@ -36,7 +36,14 @@
  *        "系统架构设计", item 4 注意力融合层.
  *
  * Causal masking is token level with the diagonal included: a query at
- * absolute position p sees a key at position t iff t <= p.  The query row r
+ * absolute position p sees a key at position t iff t <= p.  A local window
+ * w > 0 further limits it to keys at distance <= w: t >= p - w (and, without
+ * causal masking, t <= p + w); w <= 0 means no window.  Sparse local
+ * attention over the last w tokens is the window of page "Ring Attention：
+ * 百万 Token 上下文的秘密", §4.3 稀疏注意力掩码 (query i sees keys
+ * i - w .. i); page "billion-token context window engineering" describes
+ * the sliding window as keys within a range before and after the query,
+ * the reading taken without causal masking.  The query row r
  * sits at absolute position q_offset + r (q_offset = chunk index * chunk
  * length in a prefill ring, or cache_idx in incremental decoding:
  *   page "RingAttention推理优化：cache_idx参数使用与千万级上下文高效推理实践",
@@ -133,17 +140,21 @@ static double score(const void *q, const void *kc, int dtype, int64_t Lq,
     return dot * scale;
 }
 
-static int visible(int causal, int64_t qpos, int64_t kpos)
+static int visible(int causal, int64_t window, int64_t qpos, int64_t kpos)
 {
-    return !causal || kpos <= qpos;
+    if (causal && kpos > qpos)
+        return 0;
+    if (window > 0 && (kpos < qpos - window || kpos > qpos + window))
+        return 0;
+    return 1;
 }
 
 int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
                      const void *q, int64_t Lq, int64_t q_offset, int n_chunks,
                      const void *const *k, const void *const *v,
                      const int64_t *start, const int64_t *len, int causal,
-                     double scale, int64_t n_rows, const int64_t *rows,
-                     double *out, double *lse)
+                     int64_t window, double scale, int64_t n_rows,
+                     const int64_t *rows, double *out, double *lse)
 {
     if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, n_chunks, len, n_rows,
                      rows))
@@ -178,7 +189,7 @@ int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             int64_t t = 0;
             for (int c = 0; c < n_chunks; ++c)
                 for (int64_t j = 0; j < len[c]; ++j, ++t) {
-                    if (!visible(causal, qpos, start[c] + j)) {
+                    if (!visible(causal, window, qpos, start[c] + j)) {
                         s[t] = -INFINITY;
                         continue;
                     }
@@ -224,8 +235,9 @@ int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
 int oracle_ring_step(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
                      const void *q, int64_t Lq, int64_t q_offset,
                      const void *kc, const void *vc, int64_t start,
-                     int64_t len, int causal, double scale, int64_t n_rows,
-                     const int64_t *rows, double *m, double *l, double *O)
+                     int64_t len, int causal, int64_t window, double scale,
+                     int64_t n_rows, const int64_t *rows, double *m,
+                     double *l, double *O)
 {
     if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, 1, &len, n_rows, rows))
         return -1;
@@ -254,7 +266,7 @@ int oracle_ring_step(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             /* largest score of this chunk's visible keys */
             double cmax = -INFINITY;
             for (int64_t j = 0; j < len; ++j) {
-                if (!visible(causal, qpos, start + j)) {
+                if (!visible(causal, window, qpos, start + j)) {
                     s[j] = -INFINITY;
                     continue;
                 }

@@ -461,6 +461,79 @@ def pin_fp8_attention_equals_decoded():
     _close(o, ref, 1e-12, "fp8 ring")
 
 
+# --------------------------------------------------------------------------- #
+# local windows (page "Ring Attention：百万 Token 上下文的秘密", §4.3)
+# --------------------------------------------------------------------------- #
+def _window_mask(qpos, kpos, causal, window):
+    m = np.ones((len(qpos), len(kpos)), dtype=bool)
+    if causal:
+        m &= kpos[None, :] <= qpos[:, None]
+    if window > 0:
+        m &= np.abs(kpos[None, :] - qpos[:, None]) <= window
+    return m
+
+
+def pin_window_library_sdpa():
+    """Windowed attention against float64 SDPA with the window written as an
+    explicit boolean mask over absolute positions (causal one-sided windows,
+    two-sided windows without causal masking, GQA, ragged chunks, and rows
+    whose window holds no key, which must give 0)."""
+    rng = np.random.default_rng(202)
+    cases = [
+        # B, Lq, Hq, Hkv, d, lens, q_offset, causal, window
+        (1, 9, 2, 1, 6, [5, 9, 3], 4, True, 3),
+        (2, 7, 4, 2, 5, [8, 8, 8], 16, True, 1),
+        (1, 6, 3, 3, 8, [4, 11], 0, False, 2),
+        (1, 5, 2, 2, 4, [7, 7], 30, True, 4),     # query positions past every key: empty rows
+        (2, 8, 4, 1, 7, [6, 1, 9], 10, False, 5),
+        (1, 10, 2, 2, 6, [10, 10], 10, True, 9),  # query chunk = last chunk
+    ]
+    for (B, Lq, Hq, Hkv, d, lens, q_off, causal, w) in cases:
+        q, chunks = _rand(rng, B, Lq, Hq, Hkv, d, d, lens)
+        out, _ = oracle.attention(q, chunks, q_off, causal, window=w)
+        qpos = q_off + np.arange(Lq)
+        mask = _window_mask(qpos, _positions(chunks), causal, w)
+        seen = mask.any(1)
+        K = torch.from_numpy(np.concatenate([c[0] for c in chunks], axis=1)).permute(0, 2, 1, 3)
+        V = torch.from_numpy(np.concatenate([c[1] for c in chunks], axis=1)).permute(0, 2, 1, 3)
+        Q = torch.from_numpy(q).permute(0, 2, 1, 3)
+        if seen.any():
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, :, seen], K, V, attn_mask=torch.from_numpy(mask[seen]), scale=1.0 / math.sqrt(d),
+                enable_gqa=True).permute(0, 2, 1, 3).numpy()
+            _close(out[:, seen], ref, 1e-12, f"window sdpa {lens} q_off={q_off} causal={causal} w={w}")
+        assert np.all(out[:, ~seen] == 0.0), "rows with an empty window must be 0"
+
+
+def pin_window_of_one_is_two_keys():
+    """A causal window of 1 leaves each query its own key and the one before:
+    the two-key logistic closed form."""
+    d = 4
+    q = np.array([[[[2.0, 0.0, 1.0, 0.0]]]])
+    keys = np.array([[[[5.0, 1.0, 0.0, 2.0]], [[1.0, 0.0, 0.0, 0.0]], [[0.0, 0.0, 3.0, 0.0]]]])  # positions 0,1,2
+    vals = np.array([[[[9.0, 9.0]], [[1.0, 2.0]], [[-1.0, 5.0]]]])
+    out, _ = oracle.attention(q, [(keys, vals, 0)], 2, True, window=1)  # query at position 2
+    s1, s2 = 2.0 / math.sqrt(d), 3.0 / math.sqrt(d)
+    sig = 1.0 / (1.0 + math.exp(-(s2 - s1)))
+    _close(out[0, 0, 0], vals[0, 1, 0] + (vals[0, 2, 0] - vals[0, 1, 0]) * sig, 1e-15, "window of one")
+
+
+def pin_window_wider_than_keys_and_ring():
+    """A window wider than the key span changes nothing; with a window the
+    ring recurrence in any chunk order still equals windowed attention."""
+    rng = np.random.default_rng(303)
+    q, chunks = _rand(rng, 2, 6, 4, 2, 8, 8, [9, 4, 12])
+    for causal in (True, False):
+        a, _ = oracle.attention(q, chunks, 7, causal)
+        b, _ = oracle.attention(q, chunks, 7, causal, window=100)
+        _close(a, b, 0.0, f"wide window causal={causal}")
+    for w, order in ((3, [2, 0, 1]), (6, [1, 2, 0]), (13, [0, 1, 2])):
+        full, _ = oracle.attention(q, chunks, 7, True, window=w)
+        st = oracle.ring(q, chunks, order=order, q_offset=7, causal=True, window=w)
+        o, _ = oracle.finalize(st)
+        _close(o, full, 1e-12, f"windowed ring w={w} order={order}")
+
+
 ALL_PINS = [
     pin_library_sdpa,
     pin_zero_query_mean,
@@ -477,4 +550,7 @@ ALL_PINS = [
     pin_input_types,
     pin_fp8_decode_library,
     pin_fp8_attention_equals_decoded,
+    pin_window_library_sdpa,
+    pin_window_of_one_is_two_keys,
+    pin_window_wider_than_keys_and_ring,
 ]

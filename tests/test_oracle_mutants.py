@@ -19,8 +19,10 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = [
     ("no_rescale_of_O", "o[e] *= alpha;", "(void)alpha;", 1),
     ("no_rescale_of_l", "l[st] = alpha * l[st] + psum;", "l[st] = l[st] + psum;", 1),
-    ("strict_causal_diagonal", "return !causal || kpos <= qpos;",
-     "return !causal || kpos < qpos;", 1),
+    ("strict_causal_diagonal", "if (causal && kpos > qpos)", "if (causal && kpos >= qpos)", 1),
+    ("window_excludes_its_edge", "kpos < qpos - window", "kpos <= qpos - window", 1),
+    ("window_one_sided_without_causal", " || kpos > qpos + window", "", 1),
+    ("window_ignored", "if (window > 0 && (", "if (0 && (", 1),
     ("interleaved_gqa_heads", "int hk = h / (Hq / Hkv);", "int hk = h % Hkv;", "all"),
     ("q_offset_floored_to_512_chunk", "int64_t qpos = q_offset + r;",
      "int64_t qpos = (q_offset / 512) * 512 + r;", "all"),
