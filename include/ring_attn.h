@@ -116,6 +116,13 @@ typedef struct ra_desc {
     int64_t v_strides[3]; /* v   [B, len, Hkv, d_v],  every chunk        */
     /* (all strides in elements: bytes for an 8-bit KV cache)             */
     int64_t o_strides[3]; /* out [B, Lq, Hq, d_v]                        */
+    /* Local window: with window > 0 a query at position p sees only keys
+     * at distance <= window: p - window .. p under causal masking, p -
+     * window .. p + window without it (page "Ring Attention：百万 Token
+     * 上下文的秘密", §4.3 稀疏注意力掩码: query i sees keys i - w .. i).
+     * window <= 0: no window.  Tiles and chunks outside every window of a
+     * workgroup are not read. */
+    int64_t window;
 } ra_desc;
 
 typedef struct ra_kv_chunk {
@@ -151,10 +158,12 @@ int ring_attn_ctx_destroy(ra_ctx *ctx);
 int ring_attn_ring_order(int device_index, int P, int32_t *order);
 
 /* Chunk classes for a query chunk of Lq rows at absolute positions
- * q_offset .. q_offset+Lq-1 (host only): cls[c] = RA_CHUNK_SKIP / FULL /
- * DIAG for the chunk at starts[c] with lens[c] keys.  Non-causal: all FULL
- * (empty chunks: SKIP). */
-int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int P,
+ * q_offset .. q_offset+Lq-1 (host only): cls[c] = RA_CHUNK_SKIP (no key
+ * visible to any query) / FULL (every key visible to every query) / DIAG
+ * for the chunk at starts[c] with lens[c] keys, under causal masking and
+ * the local window (as ra_desc.window; <= 0: none).  Non-causal without a
+ * window: all FULL (empty chunks: SKIP). */
+int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window, int P,
                    const int64_t *starts, const int64_t *lens, int32_t *cls);
 
 /* Bytes of device workspace ring_attn_fwd needs for these arguments

@@ -344,33 +344,69 @@ __device__ inline void load_tile(const uint16_t *base, int64_t stride, int64_t k
     }
 }
 
-// Keys of a chunk a lane's row may see, counted from the chunk's first
-// processed key kbeg: keys kbeg .. kbeg + n - 1 exist (below kend) and, for
-// causal attention, sit at absolute positions <= the row's position.  Clamped
-// to [0, 2^30] so that per-tile offsets stay in 32 bits.
-__device__ inline int visible_keys(const FwdArgs &a, const LaneRow &r, int64_t cstart, int64_t kbeg, int64_t kend) {
-    int64_t n = kend - kbeg;
-    if (a.causal) {
-        const int64_t vis = r.qpos - cstart - kbeg + 1;
-        n = vis < n ? vis : n;
+// Keys of a chunk a lane's row may see, as a range [lo, hi) of key indices
+// counted from the chunk's first processed key kbeg: below kend, not after
+// the row's position under causal masking, and within the local window.
+// Clamped to +-2^30 so that per-tile offsets stay in 32 bits.
+struct VisRange {
+    int lo, hi;
+};
+
+__device__ inline VisRange visible_range(const FwdArgs &a, const LaneRow &r, int64_t cstart, int64_t kbeg,
+                                         int64_t kend) {
+    const int64_t rel = r.qpos - cstart - kbeg;  // the row's own key index
+    int64_t lo = -(1 << 30), hi = kend - kbeg;
+    if (a.causal) hi = rel + 1 < hi ? rel + 1 : hi;
+    if (a.window > 0) {
+        lo = rel - a.window;
+        if (!a.causal) hi = rel + a.window + 1 < hi ? rel + a.window + 1 : hi;
     }
-    n = n < 0 ? 0 : n;
-    return (int)(n < (1 << 30) ? n : (1 << 30));
+    const int64_t big = 1 << 30;
+    lo = lo < -big ? -big : (lo > big ? big : lo);
+    hi = hi < -big ? -big : (hi > big ? big : hi);
+    return VisRange{(int)lo, (int)hi};
 }
 
 // Mask the keys a lane's row must not see in a tile whose first key is
 // `rel` keys after kbeg: element i of block kb is key 32kb + 8(i/4) + 4g +
-// i%4 of the tile, visible iff it is below vis - rel.
+// i%4 of the tile, visible iff it lies in [lo - rel, hi - rel).
 template <class C>
-__device__ inline void mask_scores(f32x16 (&s)[C::KB], int vis, int rel, int g) {
-    const int lim = vis - rel - 4 * g;  // compare against the lane-independent part of the key
+__device__ inline void mask_scores(f32x16 (&s)[C::KB], VisRange v, int rel, int g) {
+    const int hi = v.hi - rel - 4 * g;  // compare against the lane-independent part of the key
+    const int lo = v.lo - rel - 4 * g;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
-            if (key >= lim) s[kb][i] = kNegInf;
+            if (key >= hi || key < lo) s[kb][i] = kNegInf;
         }
+}
+
+// Keys k0 .. k0+n-1 of a chunk (absolute k0 + cstart) against the rows of
+// positions q_offset + tlo .. q_offset + thi: none visible to any row
+// (skipped) / all visible to all rows (no mask needed).
+__device__ inline bool keys_unseen(const FwdArgs &a, int64_t cstart, int64_t k0, int64_t n, int64_t tlo,
+                                   int64_t thi) {
+    const int64_t first = cstart + k0, last = first + n - 1;
+    if (a.causal && first > a.q_offset + thi) return true;
+    if (a.window > 0) {
+        if (last < a.q_offset + tlo - a.window) return true;
+        if (!a.causal && first > a.q_offset + thi + a.window) return true;
+    }
+    return false;
+}
+
+__device__ inline bool keys_all_seen(const FwdArgs &a, int64_t cstart, int64_t k0, int64_t n, int64_t kend,
+                                     int64_t tlo, int64_t thi) {
+    const int64_t first = cstart + k0, last = first + n - 1;
+    if (k0 + n > kend) return false;
+    if (a.causal && last > a.q_offset + tlo) return false;
+    if (a.window > 0) {
+        if (first < a.q_offset + thi - a.window) return false;
+        if (!a.causal && last > a.q_offset + tlo + a.window) return false;
+    }
+    return true;
 }
 
 // New tile maximum: update the true max, and move the reference (rescaling O
@@ -514,7 +550,10 @@ __device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const
     }
 }
 
-// Key range of chunk c for this workgroup; returns false when nothing is visible.
+// Key range of chunk c for this workgroup; returns false when nothing is
+// visible.  With a local window the first tile is the one holding the
+// earliest key any of the workgroup's rows may see (kbeg moves by whole
+// tiles, so tiles stay aligned to the chunk or sub-range start).
 __device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, int sub, int64_t &kbeg,
                                    int64_t &kend, int &ntiles, int bn) {
     const ChunkArg &ch = a.chunks[c];
@@ -525,9 +564,14 @@ __device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, 
         kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
     }
     int64_t kstop = kend;
-    if (a.causal) {
-        const int64_t vis = a.q_offset + wt.wg_thi - ch.start + 1;  // keys < vis can be visible
+    if (a.causal || a.window > 0) {
+        // keys < vis can be visible to the last row
+        const int64_t vis = a.q_offset + wt.wg_thi - ch.start + 1 + (a.causal ? 0 : a.window);
         kstop = vis < kstop ? vis : kstop;
+    }
+    if (a.window > 0) {
+        const int64_t lo = a.q_offset + wt.wg_tlo - a.window - ch.start;  // first key the first row may see
+        if (lo > kbeg) kbeg += (lo - kbeg) / bn * bn;
     }
     if (kstop <= kbeg) return false;
     ntiles = (int)((kstop - kbeg + bn - 1) / bn);
@@ -638,7 +682,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
         int ntiles;
         if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         const ChunkArg ch = a.chunks[c];
-        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto issue = [&](auto u, int t) {
@@ -661,9 +705,8 @@ void fwd_bf16_kernel(const FwdArgs a) {
             // this wave's keys k0 + wk*KW .. + KW-1
             const int64_t k0 = kbeg + (int64_t)it * BN;
             const int64_t wk0 = k0 + wk * C::KW;
-            const bool skip = a.causal && ch.start + wk0 > a.q_offset + wv_thi;
-            const bool full = wk0 + C::KW <= kend &&
-                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
+            const bool skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
+            const bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
             if (!skip) {
                 if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
                 f32x16 s[C::KB];
@@ -790,7 +833,7 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
         int ntiles;
         if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         const ChunkArg ch = a.chunks[c];
-        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto issue = [&](auto u, int t) {
@@ -812,8 +855,8 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
             if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
             const int64_t k0 = kbeg + (int64_t)it * BN;
             // both waves of a row block take the same branch
-            const bool skip = a.causal && ch.start + k0 > a.q_offset + wv_thi;
-            const bool full = k0 + BN <= kend && (!a.causal || ch.start + k0 + BN - 1 <= a.q_offset + wv_tlo);
+            const bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
+            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
             f32x16 s[1];
             if (!skip) {
                 if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -977,7 +1020,7 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
         int ntiles;
         if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         const ChunkArg ch = a.chunks[c];
-        const int vis = visible_keys(a, row, ch.start, kbeg, kend);
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         const uint8_t *kbase = (const uint8_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint8_t *vbase = (const uint8_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         const int64_t nblk = (ch.len + BLOCK - 1) / BLOCK;
@@ -1002,9 +1045,8 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
             if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
             const int64_t k0 = kbeg + (int64_t)it * BN;
             const int64_t wk0 = k0 + wk * C::KW;  // this wave's 64 keys: one scale block
-            const bool skip = (a.causal && ch.start + wk0 > a.q_offset + wv_thi) || wk0 >= kend;
-            const bool full = wk0 + C::KW <= kend &&
-                              (!a.causal || ch.start + wk0 + C::KW - 1 <= a.q_offset + wv_tlo);
+            const bool skip = wk0 >= kend || keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
+            const bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
             if (!skip) {
                 const int64_t blk = wk0 / BLOCK;
                 const float ks = exp_scale(kexp[blk]), vs = exp_scale(vexp[blk]);

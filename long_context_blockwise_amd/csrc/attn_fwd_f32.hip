@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
     const bool row_ok = gq < a.G && t < Lq;
     const int h = hk * a.G + gq;
     const int64_t qpos = a.q_offset + t;
-    // last query position among this workgroup's rows (for skipping keys)
-    int64_t pos_hi;
+    // first and last query positions among this workgroup's rows (for skipping keys)
+    int64_t pos_lo, pos_hi;
     {
         const int64_t pa = (int64_t)rt * RB;
         int64_t pb = pa + RB;
@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
         int64_t thi = (pa / Lq_pad == pb / Lq_pad) ? pb % Lq_pad : Lq - 1;
         thi = thi < Lq - 1 ? thi : Lq - 1;
         pos_hi = a.q_offset + thi;
+        pos_lo = a.q_offset + ((pa / Lq_pad == pb / Lq_pad) ? pa % Lq_pad : 0);
     }
 
     float q[64], o[64];
@@ -94,9 +95,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
             kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
         }
         int64_t kstop = kend;
-        if (a.causal) {
-            const int64_t vis = pos_hi - ch.start + 1;
+        if (a.causal || a.window > 0) {
+            const int64_t vis = pos_hi - ch.start + 1 + (a.causal ? 0 : a.window);
             kstop = vis < kstop ? vis : kstop;
+        }
+        if (a.window > 0) {  // start at the tile of the first key the first row may see
+            const int64_t lo = pos_lo - a.window - ch.start;
+            if (lo > kbeg) kbeg += (lo - kbeg) / kKeys * kKeys;
         }
         const float *kbase = (const float *)ch.k + b * a.k_sb + hk * a.k_sh;
         const float *vbase = (const float *)ch.v + b * a.v_sb + hk * a.v_sh;
@@ -126,7 +131,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
                         for (int x = 1; x < TPR; x <<= 1) acc += __shfl_xor(acc, x);
                     }
                     const int64_t key = k0 + j0 + j;
-                    const bool vis = key < kend && (!a.causal || ch.start + key <= qpos);
+                    const int64_t kpos = ch.start + key;
+                    const bool vis = key < kend && (!a.causal || kpos <= qpos) &&
+                                     (a.window <= 0 ||
+                                      (kpos >= qpos - a.window && (a.causal || kpos <= qpos + a.window)));
                     s[j] = vis ? acc * c2 : kNegInf;
                     smax = fmaxf(smax, s[j]);
                 }

@@ -35,6 +35,7 @@ struct FwdArgs {
     int64_t o_sb, o_ss, o_sh;
     int64_t Lq, Lq_pad, q_offset;
     int64_t sub_len;           // split mode: keys per sub-range of a chunk
+    int64_t window;            // local window (> 0), or 0: none
     int B, Hq, Hkv, G;
     int causal;
     int load_state;            // start from (m, l, O) instead of empty

@@ -145,13 +145,19 @@ void chunk_strides(const int64_t *given, int64_t len, int Hkv, int dd, int64_t *
     }
 }
 
-int classify(int64_t Lq, int64_t q_offset, int causal, int64_t start, int64_t len) {
+// Chunk class of keys start .. start+len-1 for queries q_offset .. q_offset+Lq-1.
+int classify(int64_t Lq, int64_t q_offset, int causal, int64_t window, int64_t start, int64_t len) {
     if (len <= 0 || Lq <= 0) return RA_CHUNK_SKIP;
-    if (!causal) return RA_CHUNK_FULL;
-    const int64_t first_q = q_offset, last_q = q_offset + Lq - 1;
-    if (start > last_q) return RA_CHUNK_SKIP;
-    if (start + len - 1 <= first_q) return RA_CHUNK_FULL;
-    return RA_CHUNK_DIAG;
+    const int64_t first_q = q_offset, last_q = q_offset + Lq - 1, last_k = start + len - 1;
+    const bool win = window > 0;
+    // keys any query may see: [first_q - window, last_q (+ window)]
+    if (causal && start > last_q) return RA_CHUNK_SKIP;
+    if (win && (last_k < first_q - window || (!causal && start > last_q + window))) return RA_CHUNK_SKIP;
+    // keys every query sees
+    bool full = true;
+    if (causal && last_k > first_q) full = false;
+    if (win && (start < last_q - window || (!causal && last_k > first_q + window))) full = false;
+    return full ? RA_CHUNK_FULL : RA_CHUNK_DIAG;
 }
 
 // Launches of the ring schedule: one chunk per launch when staged, else up to
@@ -228,7 +234,8 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
                 return fail(RA_ERR_INVALID_ARG, "chunk %d: an 8-bit KV chunk needs k_exp and v_exp", c);
     }
     for (int c = 0; c < P; ++c)
-        if (classify(Lq, q_offset, causal, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP) pl->steps.push_back(c);
+        if (classify(Lq, q_offset, causal, d->window, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
+            pl->steps.push_back(c);
 
     const int es = elem_size(d->dtype);
     size_t off = 0;
@@ -286,6 +293,7 @@ FwdArgs base_args(const ra_desc *d, const Strides &st, const void *q, int64_t Lq
     a.q_offset = q_offset;
     a.B = d->B, a.Hq = d->Hq, a.Hkv = d->Hkv, a.G = d->Hq / d->Hkv;
     a.causal = causal ? 1 : 0;
+    a.window = d->window > 0 ? d->window : 0;
     const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->d_qk);
     a.scale_log2 = scale * 1.4426950408889634f;
     return a;
@@ -332,7 +340,7 @@ struct DeviceGuard {
 
 extern "C" {
 
-const char *ring_attn_version(void) { return "ringattn 0.2 (gfx950)"; }
+const char *ring_attn_version(void) { return "ringattn 0.3 (gfx950)"; }
 
 const char *ring_attn_last_error(void) { return g_err.c_str(); }
 
@@ -381,13 +389,13 @@ int ring_attn_ring_order(int device_index, int P, int32_t *order) {
     return RA_OK;
 }
 
-int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int P, const int64_t *starts, const int64_t *lens,
-                   int32_t *cls) {
+int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window, int P, const int64_t *starts,
+                   const int64_t *lens, int32_t *cls) {
     if (P < 0 || Lq < 0 || q_offset < 0) return fail(RA_ERR_INVALID_ARG, "negative argument");
     if (P > 0 && (!starts || !lens || !cls)) return fail(RA_ERR_INVALID_ARG, "NULL array");
     for (int c = 0; c < P; ++c) {
         if (starts[c] < 0 || lens[c] < 0) return fail(RA_ERR_INVALID_ARG, "chunk %d: negative start/len", c);
-        cls[c] = classify(Lq, q_offset, causal, starts[c], lens[c]);
+        cls[c] = classify(Lq, q_offset, causal, window, starts[c], lens[c]);
     }
     return RA_OK;
 }

@@ -48,7 +48,8 @@ class ra_desc(ctypes.Structure):
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
-                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3)]
+                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
+                ("window", ctypes.c_int64)]
 
 
 class ra_kv_chunk(ctypes.Structure):
@@ -83,7 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ring_attn_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
         lib.ring_attn_ctx_destroy.argtypes = [vp]
         lib.ring_attn_ring_order.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i32)]
-        lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64),
+        lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, i64, ctypes.c_int, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i32)]
         lib.ring_attn_workspace_size.argtypes = [ctypes.POINTER(ra_desc), i64, ctypes.POINTER(ra_kv_chunk),
                                                  ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32,
@@ -120,12 +121,12 @@ def ring_attn_ring_order(device_index: int, P: int) -> List[int]:
 
 
 def ring_attn_plan(Lq: int, q_offset: int, causal: bool, starts: Sequence[int],
-                   lens: Sequence[int]) -> List[int]:
+                   lens: Sequence[int], window: int = 0) -> List[int]:
     P = len(starts)
     st = (ctypes.c_int64 * max(P, 1))(*starts)
     ln = (ctypes.c_int64 * max(P, 1))(*lens)
     cls = (ctypes.c_int32 * max(P, 1))()
-    _check(load().ring_attn_plan(Lq, q_offset, int(bool(causal)), P, st, ln, cls))
+    _check(load().ring_attn_plan(Lq, q_offset, int(bool(causal)), int(window), P, st, ln, cls))
     return list(cls)[:P]
 
 
@@ -178,7 +179,7 @@ def _strides(t) -> Tuple[int, int, int]:
     return t.stride(0), t.stride(1), t.stride(2)
 
 
-def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]:
+def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0) -> Tuple[ra_desc, object]:
     """ra_desc and the ra_kv_chunk array for a query tensor and chunks
     ``(k, v, start)``, or ``(k, v, start, k_exp, v_exp)`` for an 8-bit KV cache
     (k, v ``torch.float8_e4m3fn``; exponents ``uint8 [B, Hkv, ceil(len/64)]``)."""
@@ -192,6 +193,7 @@ def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]
     d.B, d.Hq, d.Hkv, d.d_qk, d.d_v = B, Hq, k0.shape[2], dqk, v0.shape[3]
     d.dtype = _dtype_code(q)
     d.scale = float(scale)
+    d.window = int(window)
     d.q_strides[:] = _strides(q)
     if out is not None:
         d.o_strides[:] = _strides(out)
@@ -229,8 +231,8 @@ def make_desc(q, chunks, scale: float = 0.0, out=None) -> Tuple[ra_desc, object]
 
 
 def ring_attn_workspace_size(q, chunks, causal: bool = False, q_offset: int = 0, flags: int = 0,
-                             want_state: bool = False, scale: float = 0.0) -> int:
-    d, arr = make_desc(q, chunks, scale)
+                             want_state: bool = False, scale: float = 0.0, window: int = 0) -> int:
+    d, arr = make_desc(q, chunks, scale, window=window)
     n = ctypes.c_size_t()
     _check(load().ring_attn_workspace_size(ctypes.byref(d), q.shape[1], arr, len(chunks),
                                            int(bool(causal)), int(q_offset), int(flags),
@@ -241,8 +243,11 @@ def ring_attn_workspace_size(q, chunks, causal: bool = False, q_offset: int = 0,
 def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: int = 0,
                   out=None, state=None, want_out: bool = True, want_state: bool = False,
                   scale: float = 0.0, ctx: Optional[RingAttnContext] = None, workspace=None,
-                  stream=None):
+                  stream=None, window: int = 0):
     """One device's share of ring attention; returns ``(out, state)``.
+
+    ``window > 0`` limits each query to keys at distance <= window (a local
+    window; under causal masking keys p - window .. p of a query at p).
 
     ``state`` (if given) is a tuple ``(m, l, O)`` of fp32 tensors ``[B, Lq, Hq]``,
     ``[B, Lq, Hq]``, ``[B, Lq, Hq, d_v]`` that receives the softmax state (and
@@ -260,7 +265,7 @@ def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: 
         state = (torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
                  torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
                  torch.empty((B, Lq, Hq, dv), device=q.device, dtype=torch.float32))
-    d, arr = make_desc(q, chunks, scale, out)
+    d, arr = make_desc(q, chunks, scale, out, window)
     lib = load()
     n = ctypes.c_size_t()
     _check(lib.ring_attn_workspace_size(ctypes.byref(d), Lq, arr, len(chunks), int(bool(causal)),

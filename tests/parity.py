@@ -49,14 +49,16 @@ def to_host(chunks):
     return [tuple(t.cpu() if hasattr(t, "cpu") else t for t in c) for c in chunks]
 
 
-def oracle_out(q, chunks, q_offset, causal, rows=None, scale=None):
+def oracle_out(q, chunks, q_offset, causal, rows=None, scale=None, window=0):
     """Oracle output [B, n_rows, Hq, d_v] and lse for device tensors."""
-    return oracle.attention(q.cpu(), to_host(chunks), q_offset, causal, scale=scale, rows=rows)
+    return oracle.attention(q.cpu(), to_host(chunks), q_offset, causal, scale=scale, rows=rows,
+                            window=window)
 
 
-def oracle_state(q, chunks, q_offset, causal, order=None, rows=None):
+def oracle_state(q, chunks, q_offset, causal, order=None, rows=None, window=0):
     """Oracle ring state (m, l, O) in the ABI layout [B, Lq, Hq](, d_v)."""
-    st = oracle.ring(q.cpu(), to_host(chunks), order=order, q_offset=q_offset, causal=causal, rows=rows)
+    st = oracle.ring(q.cpu(), to_host(chunks), order=order, q_offset=q_offset, causal=causal, rows=rows,
+                     window=window)
     return (st.m.transpose(0, 2, 1), st.l.transpose(0, 2, 1), st.O.transpose(0, 2, 1, 3))
 
 

@@ -62,10 +62,16 @@ def test_ring_order_rejects_bad_args(lib):
         ra.ring_attn_ring_order(0, 0)
 
 
-def _brute_class(Lq, q_off, causal, start, n):
+def _brute_class(Lq, q_off, causal, start, n, window=0):
     if n == 0 or Lq == 0:
         return ra.RA_CHUNK_SKIP
-    vis = [[(not causal) or (start + j <= q_off + r) for j in range(n)] for r in range(Lq)]
+
+    def seen(qp, kp):
+        if causal and kp > qp:
+            return False
+        return window <= 0 or abs(kp - qp) <= window
+
+    vis = [[seen(q_off + r, start + j) for j in range(n)] for r in range(Lq)]
     if not any(any(row) for row in vis):
         return ra.RA_CHUNK_SKIP
     if all(all(row) for row in vis):
@@ -74,14 +80,15 @@ def _brute_class(Lq, q_off, causal, start, n):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_plan_matches_brute_force(lib, causal):
+@pytest.mark.parametrize("window", [0, 1, 3, 7, 40])
+def test_plan_matches_brute_force(lib, causal, window):
     starts = [0, 5, 9, 20, 21, 30]
     lens = [5, 4, 11, 1, 9, 0]
     for Lq in (1, 3, 8):
         for q_off in (0, 4, 5, 8, 9, 19, 20, 29, 35):
-            got = ra.ring_attn_plan(Lq, q_off, causal, starts, lens)
-            want = [_brute_class(Lq, q_off, causal, s, n) for s, n in zip(starts, lens)]
-            assert got == want, (Lq, q_off)
+            got = ra.ring_attn_plan(Lq, q_off, causal, starts, lens, window=window)
+            want = [_brute_class(Lq, q_off, causal, s, n, window) for s, n in zip(starts, lens)]
+            assert got == want, (Lq, q_off, window)
 
 
 def test_plan_of_the_prefill_share():
@@ -196,7 +203,8 @@ def test_context_needs_a_device(lib):
 
 
 def test_struct_layouts_match_the_header():
-    assert ctypes.sizeof(rb.ra_desc) == 8 * 4 + 12 * 8
+    assert ctypes.sizeof(rb.ra_desc) == 8 * 4 + 13 * 8
+    assert rb.ra_desc.window.offset == 8 * 4 + 12 * 8
     assert ctypes.sizeof(rb.ra_kv_chunk) == 6 * 8
     assert rb.ra_desc.kv_dtype.offset == 7 * 4
     assert rb.ra_kv_chunk.k_exp.offset == 32 and rb.ra_kv_chunk.v_exp.offset == 40
