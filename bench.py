@@ -43,9 +43,10 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "b369380149888499",
-    "prefill_bf16_h32_d128": 6.5798e8,
+    "digest": "ad45dbde0a622d7d",
+    "prefill_bf16_h32_d128": 6.5269e8,
     "decode_b4_gqa32x8_cache1m": 1.7250e10,
+    "decode_b4_gqa32x8_cache1m_fp8": 8.6619e9,
 }
 
 HEADLINE = "prefill_bf16_h32_d128"
