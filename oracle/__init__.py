@@ -21,6 +21,9 @@ each routine follows:
 * :func:`merge` / :func:`finalize` -- combining partial (m, l, O) states and
   normalising them (page "从百毫秒到百万Token", section "系统架构设计",
   注意力融合层).
+* :func:`attention_bwd` -- dQ, dK, dV of sum(dO * attention(...)): the
+  derivative of the definition above, for the training use the pages
+  describe (page "Ring Attention：百万 Token 上下文的秘密", §5.1 训练效率).
 
 Inputs are numpy arrays of float64, float32, or bfloat16 carried as raw
 ``uint16`` bit patterns (pass ``dtype="bf16"``); torch CPU tensors of those
@@ -78,6 +81,9 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_finalize.argtypes = [i64, i32, vp, vp, vp, vp, vp]
     lib.oracle_dequant_fp8.restype = i32
     lib.oracle_dequant_fp8.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp]
+    lib.oracle_attention_bwd.restype = i32
+    lib.oracle_attention_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp, vp,
+                                         vp, vp, i32, i64, dbl, vp, vp, vp, vp]
     return lib
 
 
@@ -242,6 +248,36 @@ def attention(q, chunks, q_offset=0, causal=False, scale=None, rows=None,
     if rc != 0:
         raise ValueError(f"oracle_attention failed ({rc})")
     return out, lse
+
+
+def attention_bwd(q, chunks, dout, q_offset=0, causal=False, scale=None, dtype=None, window=0):
+    """Gradients of ``sum(dout * attention(q, chunks, ...))``: returns
+    ``(dq [B, Lq, Hq, d_qk], [dk_c [B, len_c, Hkv, d_qk]], [dv_c [B, len_c, Hkv, d_v]])``
+    in float64.  ``dout [B, Lq, Hq, d_v]`` has q's element type; masking
+    (causal, window, q_offset) is as in :func:`attention`."""
+    lib = _get_lib()
+    p = _Problem(q, chunks, dtype, None)
+    if not p.ks:
+        raise ValueError("attention_bwd needs at least one chunk")
+    do, code = _to_numpy(dout, dtype)
+    if code != p.code or do.shape != (p.B, p.Lq, p.Hq, p.dv):
+        raise ValueError("dout must have q's element type and shape [B, Lq, Hq, d_v]")
+    dq = np.zeros((p.B, p.Lq, p.Hq, p.dqk), dtype=np.float64)
+    dks = [np.zeros(k.shape, dtype=np.float64) for k in p.ks]
+    dvs = [np.zeros(v.shape, dtype=np.float64) for v in p.vs]
+    n = len(p.ks)
+    kp = (ctypes.c_void_p * n)(*[_ptr(a) for a in p.ks])
+    vp = (ctypes.c_void_p * n)(*[_ptr(a) for a in p.vs])
+    dkp = (ctypes.c_void_p * n)(*[_ptr(a) for a in dks])
+    dvp = (ctypes.c_void_p * n)(*[_ptr(a) for a in dvs])
+    st = np.asarray(p.starts, dtype=np.int64)
+    ln = np.asarray(p.lens, dtype=np.int64)
+    rc = lib.oracle_attention_bwd(p.B, p.Hq, p.Hkv, p.dqk, p.dv, p.code, _ptr(p.q), p.Lq,
+                                  int(q_offset), n, kp, vp, _ptr(st), _ptr(ln), int(bool(causal)),
+                                  int(window), _scale(scale, p.dqk), _ptr(do), _ptr(dq), dkp, dvp)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_bwd failed ({rc})")
+    return dq, dks, dvs
 
 
 class State:

@@ -72,6 +72,23 @@
  *    of 64 consecutive tokens of one (batch, KV head) sharing a power-of-two
  *    scale 2^(e - 127) given by an 8-bit biased exponent e (1 .. 254).
  *    The attention itself is then oracle_attention on the decoded values.
+ *
+ *  - oracle_attention_bwd: the gradients dQ, dK, dV of L = sum(dO * out),
+ *    out = oracle_attention(...), for a given output gradient dO.  The pages
+ *    use ring attention for training (page "Ring Attention：百万 Token
+ *    上下文的秘密", §5.1 训练效率; page "billion-token context window
+ *    engineering", training with ring attention and FSDP) but print no
+ *    backward algorithm, so this is the derivative of the definition,
+ *    written out.  With P = softmax(S) over the visible keys of a row and
+ *    S = scale * q k^T:
+ *        dV_j = sum_i P_ij dO_i                     (out is linear in V)
+ *        dP_ij = dO_i . v_j
+ *        dS_ij = P_ij (dP_ij - sum_t P_it dP_it)    (softmax Jacobian)
+ *        dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+ *    with sums over visible (i, j) only, and every query head of a KV head's
+ *    group adding into that head's dK and dV.  Rows that see no key get
+ *    dQ = 0 and add nothing.  It runs as a per-row pass (softmax, dQ) and
+ *    a per-key pass (dK, dV), so no two threads write one element.
  */
 #include <math.h>
 #include <stdint.h>
@@ -381,5 +398,165 @@ int oracle_dequant_fp8(int B, int64_t len, int H, int d, int block,
                 for (int i = 0; i < d; ++i)
                     out[base + i] = fp8_e4m3_value(codes[base + i]) * scale;
             }
+    return 0;
+}
+
+/* Gradients of L = sum(dout * attention(q, k, v)).  dout has q's element
+ * type and layout [B][Lq][Hq][dv]; dq [B][Lq][Hq][dqk], dk[c]
+ * [B][len[c]][Hkv][dqk] and dvv[c] [B][len[c]][Hkv][dv] are written (double).
+ * Returns 0, -1 on an argument error, -2 if out of memory. */
+int oracle_attention_bwd(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
+                         const void *q, int64_t Lq, int64_t q_offset,
+                         int n_chunks, const void *const *k,
+                         const void *const *v, const int64_t *start,
+                         const int64_t *len, int causal, int64_t window,
+                         double scale, const void *dout, double *dq,
+                         double *const *dk, double *const *dvv)
+{
+    if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, n_chunks, len, 0, NULL))
+        return -1;
+    const int G = Hq / Hkv;
+    int64_t nkeys = 0;
+    for (int c = 0; c < n_chunks; ++c)
+        nkeys += len[c];
+    int64_t units = (int64_t)B * Hq * Lq;
+    /* per row: log-sum-exp of its visible scores, and sum_t P_t dP_t */
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(units ? units : 1));
+    double *Dsum = (double *)malloc(sizeof(double) * (size_t)(units ? units : 1));
+    if (!lse || !Dsum) {
+        free(lse);
+        free(Dsum);
+        return -2;
+    }
+    int err = 0;
+
+    /* pass 1, per query row: softmax weights, D, and dQ */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nkeys ? nkeys : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(nkeys ? nkeys : 1));
+        if (!s || !dp) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !dp)
+                continue;
+            int b = (int)(u / ((int64_t)Hq * Lq));
+            int h = (int)((u / Lq) % Hq);
+            int64_t r = u % Lq;
+            int64_t qpos = q_offset + r;
+            int hk = h / G;
+            int64_t row = ((int64_t)b * Hq + h) * Lq + r;
+            double *g = dq + (((int64_t)b * Lq + r) * Hq + h) * dqk;
+            int64_t ob = (((int64_t)b * Lq + r) * Hq + h) * dv;
+            for (int e = 0; e < dqk; ++e)
+                g[e] = 0.0;
+
+            double mx = -INFINITY;
+            int64_t t = 0;
+            for (int c = 0; c < n_chunks; ++c)
+                for (int64_t j = 0; j < len[c]; ++j, ++t) {
+                    if (!visible(causal, window, qpos, start[c] + j)) {
+                        s[t] = -INFINITY;
+                        continue;
+                    }
+                    s[t] = score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale);
+                    if (s[t] > mx)
+                        mx = s[t];
+                }
+            if (mx == -INFINITY) { /* no visible key */
+                lse[row] = -INFINITY;
+                Dsum[row] = 0.0;
+                continue;
+            }
+            double sum = 0.0;
+            for (t = 0; t < nkeys; ++t)
+                if (s[t] != -INFINITY)
+                    sum += exp(s[t] - mx);
+            double ls = mx + log(sum);
+            lse[row] = ls;
+
+            /* dP_t = dO . v_t and D = sum_t P_t dP_t */
+            double D = 0.0;
+            t = 0;
+            for (int c = 0; c < n_chunks; ++c)
+                for (int64_t j = 0; j < len[c]; ++j, ++t) {
+                    if (s[t] == -INFINITY)
+                        continue;
+                    int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;
+                    double acc = 0.0;
+                    for (int e = 0; e < dv; ++e)
+                        acc += elem(dout, dtype, ob + e) * elem(v[c], dtype, vb + e);
+                    dp[t] = acc;
+                    D += exp(s[t] - ls) * acc;
+                }
+            Dsum[row] = D;
+
+            /* dQ = scale sum_t P_t (dP_t - D) k_t */
+            t = 0;
+            for (int c = 0; c < n_chunks; ++c)
+                for (int64_t j = 0; j < len[c]; ++j, ++t) {
+                    if (s[t] == -INFINITY)
+                        continue;
+                    double ds = exp(s[t] - ls) * (dp[t] - D);
+                    int64_t kb = (((int64_t)b * len[c] + j) * Hkv + hk) * dqk;
+                    for (int e = 0; e < dqk; ++e)
+                        g[e] += scale * ds * elem(k[c], dtype, kb + e);
+                }
+        }
+        free(s);
+        free(dp);
+    }
+    if (err) {
+        free(lse);
+        free(Dsum);
+        return err;
+    }
+
+    /* pass 2, per key: dK and dV summed over every row of every query head
+     * in the key's group */
+    int64_t kunits = (int64_t)B * Hkv * nkeys;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t u = 0; u < kunits; ++u) {
+        int b = (int)(u / ((int64_t)Hkv * nkeys));
+        int hk = (int)((u / nkeys) % Hkv);
+        int64_t t = u % nkeys;
+        int c = 0;
+        while (t >= len[c]) { /* chunk c and index j of global key t */
+            t -= len[c];
+            ++c;
+        }
+        int64_t j = t;
+        int64_t kb = (((int64_t)b * len[c] + j) * Hkv + hk) * dqk;
+        int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;
+        double *gk = dk[c] + kb, *gv = dvv[c] + vb;
+        for (int e = 0; e < dqk; ++e)
+            gk[e] = 0.0;
+        for (int e = 0; e < dv; ++e)
+            gv[e] = 0.0;
+        for (int h = hk * G; h < (hk + 1) * G; ++h)
+            for (int64_t r = 0; r < Lq; ++r) {
+                if (!visible(causal, window, q_offset + r, start[c] + j))
+                    continue;
+                int64_t row = ((int64_t)b * Hq + h) * Lq + r;
+                if (lse[row] == -INFINITY)
+                    continue;
+                double p = exp(score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale) - lse[row]);
+                int64_t ob = (((int64_t)b * Lq + r) * Hq + h) * dv;
+                int64_t qb = (((int64_t)b * Lq + r) * Hq + h) * dqk;
+                double dpv = 0.0;
+                for (int e = 0; e < dv; ++e)
+                    dpv += elem(dout, dtype, ob + e) * elem(v[c], dtype, vb + e);
+                double ds = p * (dpv - Dsum[row]);
+                for (int e = 0; e < dqk; ++e)
+                    gk[e] += scale * ds * elem(q, dtype, qb + e);
+                for (int e = 0; e < dv; ++e)
+                    gv[e] += p * elem(dout, dtype, ob + e);
+            }
+    }
+    free(lse);
+    free(Dsum);
     return 0;
 }

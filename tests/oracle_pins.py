@@ -534,6 +534,135 @@ def pin_window_wider_than_keys_and_ring():
         _close(o, full, 1e-12, f"windowed ring w={w} order={order}")
 
 
+# --------------------------------------------------------------------------- #
+# backward: gradients of sum(dO * out)
+# --------------------------------------------------------------------------- #
+def _mask(q_off, Lq, chunks, causal, w):
+    return _window_mask(q_off + np.arange(Lq), _positions(chunks), causal, w)
+
+
+def pin_bwd_library_autograd():
+    """dQ, dK, dV against float64 autograd through library SDPA with an
+    explicit position mask: causal, windows, two-sided windows, GQA, ragged
+    chunks, d_qk != d_v, and rows that see no key (dropped from the library
+    call: they must get dQ = 0 and add nothing to dK, dV)."""
+    rng = np.random.default_rng(404)
+    cases = [
+        # B, Lq, Hq, Hkv, dqk, dv, lens, q_offset, causal, window
+        (1, 7, 2, 1, 6, 6, [5, 9, 3], 6, True, 0),
+        (2, 6, 4, 2, 5, 3, [8, 8], 8, True, 0),
+        (1, 5, 3, 3, 4, 4, [6, 2], 0, False, 0),
+        (2, 8, 4, 1, 7, 7, [6, 1, 9], 5, True, 3),
+        (1, 6, 2, 2, 5, 5, [7, 7], 3, False, 2),
+        (1, 5, 2, 1, 4, 4, [6, 6], 20, False, 4),  # the last rows' windows hold no key
+    ]
+    for (B, Lq, Hq, Hkv, dqk, dv, lens, q_off, causal, w) in cases:
+        q, chunks = _rand(rng, B, Lq, Hq, Hkv, dqk, dv, lens)
+        do = rng.standard_normal((B, Lq, Hq, dv))
+        dq, dks, dvs = oracle.attention_bwd(q, chunks, do, q_off, causal, window=w)
+        mask = _mask(q_off, Lq, chunks, causal, w)
+        seen = mask.any(1)
+        Q = torch.from_numpy(q).requires_grad_()
+        K = torch.from_numpy(np.concatenate([c[0] for c in chunks], axis=1)).requires_grad_()
+        V = torch.from_numpy(np.concatenate([c[1] for c in chunks], axis=1)).requires_grad_()
+        out = torch.nn.functional.scaled_dot_product_attention(
+            Q[:, seen].permute(0, 2, 1, 3), K.permute(0, 2, 1, 3), V.permute(0, 2, 1, 3),
+            attn_mask=torch.from_numpy(mask[seen]), scale=1.0 / math.sqrt(dqk), enable_gqa=True)
+        (out.permute(0, 2, 1, 3) * torch.from_numpy(do[:, seen])).sum().backward()
+        what = f"bwd autograd {lens} q_off={q_off} causal={causal} w={w}"
+        _close(dq, Q.grad.numpy(), 1e-11, what + " dQ")
+        _close(np.concatenate(dks, 1), K.grad.numpy(), 1e-11, what + " dK")
+        _close(np.concatenate(dvs, 1), V.grad.numpy(), 1e-11, what + " dV")
+        assert np.all(dq[:, ~seen] == 0.0), what + ": rows with no key must get dQ = 0"
+
+
+def pin_bwd_finite_differences():
+    """Every gradient element against central differences of the forward
+    oracle's sum(dO * out): brute force, no derivative code involved."""
+    rng = np.random.default_rng(505)
+    for (Hq, Hkv, lens, q_off, causal, w) in ((2, 1, [2, 3], 2, True, 0), (2, 2, [3, 2], 1, False, 2),
+                                              (2, 1, [4, 1], 3, True, 2)):
+        q, chunks = _rand(rng, 1, 3, Hq, Hkv, 3, 2, lens)
+        do = rng.standard_normal((1, 3, Hq, 2))
+        dq, dks, dvs = oracle.attention_bwd(q, chunks, do, q_off, causal, window=w)
+
+        def loss(qq, cc):
+            out, _ = oracle.attention(qq, cc, q_off, causal, window=w)
+            return float((out * do).sum())
+
+        eps = 1e-6
+        arrays = [("q", q, dq)] + [(f"k{c}", chunks[c][0], dks[c]) for c in range(len(chunks))] + \
+                 [(f"v{c}", chunks[c][1], dvs[c]) for c in range(len(chunks))]
+        for name, a, g in arrays:
+            for idx in np.ndindex(a.shape):
+                old = a[idx]
+                a[idx] = old + eps
+                lp = loss(q, chunks)
+                a[idx] = old - eps
+                lm = loss(q, chunks)
+                a[idx] = old
+                num = (lp - lm) / (2 * eps)
+                assert abs(num - g[idx]) <= 1e-7 * (1 + abs(num)), \
+                    f"bwd finite difference {name}{idx}: {num} vs {g[idx]} (lens {lens} causal={causal} w={w})"
+
+
+def pin_bwd_invariants_and_closed_forms():
+    """Softmax shift invariance: the dK of all keys of a (batch, KV head) sum
+    to 0; the dV sum to the summed dO of the rows that see a key (each row's
+    weights sum to 1).  Closed forms: constant values give dQ = dK = 0; a
+    row seeing one key gets dQ = 0; two keys give the logistic derivative."""
+    rng = np.random.default_rng(606)
+    q, chunks = _rand(rng, 2, 9, 4, 2, 6, 5, [7, 4, 10])
+    do = rng.standard_normal((2, 9, 4, 5))
+    for causal, w, q_off in ((True, 0, 12), (False, 3, 4), (True, 2, 14), (False, 0, 0)):
+        dq, dks, dvs = oracle.attention_bwd(q, chunks, do, q_off, causal, window=w)
+        _close(np.concatenate(dks, 1).sum(1), np.zeros((2, 2, 6)), 1e-12, f"sum dK causal={causal} w={w}")
+        seen = _mask(q_off, 9, chunks, causal, w).any(1)
+        want = do[:, seen].reshape(2, -1, 2, 2, 5).sum(1).sum(2)  # rows, then the 2 heads of each group
+        _close(np.concatenate(dvs, 1).sum(1), want, 1e-12, f"sum dV causal={causal} w={w}")
+    # constant values: out does not depend on the scores
+    const = [(k, np.broadcast_to(np.arange(5.0), v.shape).copy(), s) for (k, v, s) in chunks]
+    dq, dks, _ = oracle.attention_bwd(q, const, do, 12, True)
+    _close(dq, np.zeros_like(dq), 1e-12, "constant V: dQ")
+    _close(np.concatenate(dks, 1), np.zeros((2, 21, 2, 6)), 1e-12, "constant V: dK")
+    # causal row 0 at position 0 sees key 0 only
+    dq, _, _ = oracle.attention_bwd(q, chunks, do, 0, True)
+    _close(dq[:, 0], np.zeros((2, 4, 6)), 0.0, "single visible key: dQ")
+    # window of one: keys t-1, t; out = v1 + (v2 - v1) sig(s2 - s1)
+    d = 4
+    qq = np.array([[[[2.0, 0.5, 1.0, -1.0]]]])
+    keys = np.array([[[[5.0, 1.0, 0.0, 2.0]], [[1.0, 0.0, -2.0, 0.0]], [[0.0, 1.0, 3.0, 0.0]]]])
+    vals = np.array([[[[9.0, 9.0]], [[1.0, 2.0]], [[-1.0, 5.0]]]])
+    g = np.array([[[[0.7, -1.3]]]])
+    dq, dks, dvs = oracle.attention_bwd(qq, [(keys, vals, 0)], g, 2, True, window=1)
+    sc = 1.0 / math.sqrt(d)
+    s1, s2 = sc * qq[0, 0, 0] @ keys[0, 1, 0], sc * qq[0, 0, 0] @ keys[0, 2, 0]
+    sig = 1.0 / (1.0 + math.exp(-(s2 - s1)))
+    c = float(g[0, 0, 0] @ (vals[0, 2, 0] - vals[0, 1, 0])) * sig * (1 - sig)
+    _close(dq[0, 0, 0], c * sc * (keys[0, 2, 0] - keys[0, 1, 0]), 1e-14, "two keys: dQ")
+    _close(dks[0][0, 2, 0], c * sc * qq[0, 0, 0], 1e-14, "two keys: dK of the later key")
+    _close(dks[0][0, 1, 0], -c * sc * qq[0, 0, 0], 1e-14, "two keys: dK of the earlier key")
+    _close(dvs[0][0, 1, 0], (1 - sig) * g[0, 0, 0], 1e-14, "two keys: dV of the earlier key")
+    _close(dks[0][0, 0, 0], np.zeros(d), 0.0, "key outside the window: dK")
+
+
+def pin_bwd_chunking_invariance():
+    """Gradients do not depend on how the keys are cut into chunks or in
+    which order the chunks are listed (the ring's equivalence, page "Ring
+    Attention：百万 Token 上下文的秘密", §2.3)."""
+    rng = np.random.default_rng(707)
+    q, chunks = _rand(rng, 1, 6, 2, 1, 5, 5, [12])
+    do = rng.standard_normal((1, 6, 2, 5))
+    k, v, _ = chunks[0]
+    dq0, dk0, dv0 = oracle.attention_bwd(q, chunks, do, 6, True, window=4)
+    cut = [(k[:, :5], v[:, :5], 0), (k[:, 5:7], v[:, 5:7], 5), (k[:, 7:], v[:, 7:], 7)]
+    perm = [cut[2], cut[0], cut[1]]
+    dq1, dk1, dv1 = oracle.attention_bwd(q, perm, do, 6, True, window=4)
+    _close(dq1, dq0, 1e-13, "chunked dQ")
+    _close(np.concatenate([dk1[1], dk1[2], dk1[0]], 1), dk0[0], 1e-13, "chunked dK")
+    _close(np.concatenate([dv1[1], dv1[2], dv1[0]], 1), dv0[0], 1e-13, "chunked dV")
+
+
 ALL_PINS = [
     pin_library_sdpa,
     pin_zero_query_mean,
@@ -553,4 +682,8 @@ ALL_PINS = [
     pin_window_library_sdpa,
     pin_window_of_one_is_two_keys,
     pin_window_wider_than_keys_and_ring,
+    pin_bwd_library_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_invariants_and_closed_forms,
+    pin_bwd_chunking_invariance,
 ]

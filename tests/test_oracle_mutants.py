@@ -56,6 +56,19 @@ MUTANTS = [
     ("fp8_scale_bias", "double scale = ldexp(1.0, e - 127);", "double scale = ldexp(1.0, e - 128);", 1),
     ("fp8_scale_block_of_next_token", "exps[((int64_t)b * H + h) * nblk + t / block]",
      "exps[((int64_t)b * H + h) * nblk + (t + 1) / block]", 1),
+    ("bwd_D_unweighted", "D += exp(s[t] - ls) * acc;", "D += acc;", 1),
+    ("bwd_dq_without_D", "double ds = exp(s[t] - ls) * (dp[t] - D);", "double ds = exp(s[t] - ls) * dp[t];", 1),
+    ("bwd_dk_without_D", "double ds = p * (dpv - Dsum[row]);", "double ds = p * dpv;", 1),
+    ("bwd_dv_from_dS", "gv[e] += p * elem(dout, dtype, ob + e);", "gv[e] += ds * elem(dout, dtype, ob + e);", 1),
+    ("bwd_dk_unscaled", "gk[e] += scale * ds * elem(q, dtype, qb + e);", "gk[e] += ds * elem(q, dtype, qb + e);", 1),
+    ("bwd_dq_sign", "g[e] += scale * ds * elem(k[c], dtype, kb + e);", "g[e] -= scale * ds * elem(k[c], dtype, kb + e);", 1),
+    ("bwd_first_head_of_group_only", "for (int h = hk * G; h < (hk + 1) * G; ++h)", "for (int h = hk * G; h < hk * G + 1; ++h)", 1),
+    ("bwd_dkdv_ignore_mask", "if (!visible(causal, window, q_offset + r, start[c] + j))\n                    continue;",
+     "if (0)\n                    continue;", 1),
+    ("bwd_unnormalised_weights", "double p = exp(score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale) - lse[row]);",
+     "double p = exp(score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale) - lse[row] + 0.01);", 1),
+    ("bwd_dv_of_wrong_row", "int64_t ob = (((int64_t)b * Lq + r) * Hq + h) * dv;\n                int64_t qb",
+     "int64_t ob = (((int64_t)b * Lq + (r + 1) % Lq) * Hq + h) * dv;\n                int64_t qb", 1),
 ]
 
 
