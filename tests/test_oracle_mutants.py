@@ -29,15 +29,16 @@ MUTANTS = [
     ("scale_dropped", "return dot * scale;", "return dot;", 1),
     ("no_max_shift", "double w = exp(s[t] - mx);", "double w = exp(s[t]);", 1),
     ("lse_without_max", "*ls = mx + log(sum);", "*ls = log(sum);", 1),
-    ("wrong_query_head", "int64_t qb = (((int64_t)b * Lq + r) * Hq + h) * dqk;",
-     "int64_t qb = (((int64_t)b * Lq + r) * Hq + 0) * dqk;", 1),
+    ("wrong_query_head", "int hk = h / (Hq / Hkv);\n    int64_t qb = (((int64_t)b * Lq + r) * Hq + h) * dqk;",
+     "int hk = h / (Hq / Hkv);\n    int64_t qb = (((int64_t)b * Lq + r) * Hq + 0) * dqk;", 1),
     ("key_index_transposed", "int64_t kb = (((int64_t)b * lenc + j) * Hkv + hk) * dqk;",
      "int64_t kb = (((int64_t)b * lenc + (lenc - 1 - j)) * Hkv + hk) * dqk;", 1),
     ("value_of_wrong_chunk_key",
-     "int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;",
-     "int64_t vb = (((int64_t)b * len[c] + (j ? j - 1 : 0)) * Hkv + hk) * dv;", 1),
-    ("only_two_chunks_seen", "for (int c = 0; c < n_chunks; ++c)\n                for (int64_t j = 0; j < len[c]; ++j, ++t) {\n                    if (!visible",
-     "for (int c = 0; c < n_chunks && c < 2; ++c)\n                for (int64_t j = 0; j < len[c]; ++j, ++t) {\n                    if (!visible", 1),
+     "sum += w;\n                    int64_t vb = (((int64_t)b * len[c] + j) * Hkv + hk) * dv;",
+     "sum += w;\n                    int64_t vb = (((int64_t)b * len[c] + (j ? j - 1 : 0)) * Hkv + hk) * dv;", 1),
+    ("only_two_chunks_seen",
+     "/* pass 1: scores of all visible keys and their maximum */\n            double mx = -INFINITY;\n            int64_t t = 0;\n            for (int c = 0; c < n_chunks; ++c)",
+     "/* pass 1: scores of all visible keys and their maximum */\n            double mx = -INFINITY;\n            int64_t t = 0;\n            for (int c = 0; c < n_chunks && c < 2; ++c)", 1),
     ("merge_weight_sign", "double a2 = m2[i] == -INFINITY ? 0.0 : exp(m2[i] - mx);",
      "double a2 = m2[i] == -INFINITY ? 0.0 : exp(mx - m2[i]);", 1),
     ("merge_drops_second_l", "l[i] = a1 * l1[i] + a2 * l2[i];", "l[i] = a1 * l1[i] + l2[i];", 1),
