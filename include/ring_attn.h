@@ -213,6 +213,48 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
                   float *l_out, float *O_out, void *workspace,
                   size_t ws_bytes, void *stream);
 
+/* Gradients of one KV chunk (fp32, dense [B, len, Hkv, d], device). */
+typedef struct ra_kv_grad {
+    float *dk; /* [B, len, Hkv, d_qk] */
+    float *dv; /* [B, len, Hkv, d_v]  */
+} ra_kv_grad;
+
+/* Bytes of device workspace ring_attn_bwd needs (host only). */
+int ring_attn_bwd_workspace_size(const ra_desc *d, int64_t Lq, size_t *bytes);
+
+/* Gradients of one device's share of ring attention, for training with it
+ * (page "Ring Attention：百万 Token 上下文的秘密", §5.1 训练效率, which uses
+ * it to train; the pages give no backward algorithm, so this is the
+ * derivative of softmax(Q K^T * scale) V over the visible keys).  With
+ * P = softmax(S), dO the gradient of out and D = rowsum(dO * out):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q
+ * summed over the query heads of each KV head's group.
+ *
+ *   q, chunks, P, causal, q_offset, d->window: as for ring_attn_fwd (the same
+ *              masks; d->o_strides also describe dout)
+ *   out        [B, Lq, Hq, d_v] bf16: the forward output
+ *   dout       [B, Lq, Hq, d_v] bf16: the gradient of out
+ *   m, l       [B, Lq, Hq] fp32: the forward state after all the key chunks
+ *              the output attended (m_out and l_out of ring_attn_fwd)
+ *   dq         [B, Lq, Hq, d_qk] fp32, dense (device)
+ *   grads      P entries: dK and dV of chunk c go to grads[c] (entries of
+ *              empty chunks are not touched)
+ *   flags      0 or RA_FLAG_ACCUMULATE: add into dq, dk and dv instead of
+ *              overwriting them (the dK/dV of a chunk travelling the ring
+ *              collect each device's share this way)
+ *   workspace, ws_bytes   ring_attn_bwd_workspace_size bytes, 256-aligned
+ * The chunks given may be a subset of those the forward saw (one ring step
+ * at a time, say): m and l carry the softmax normalisation over all of them.
+ * Rows with l = 0 (no visible key) have zero gradients.  Supported: bf16
+ * with d_qk == d_v in {64, 128}, bf16 keys and values; RA_ERR_UNSUPPORTED
+ * otherwise.  The call is deterministic (no atomics). */
+int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
+                  const ra_kv_chunk *chunks, int P, int causal,
+                  int64_t q_offset, uint32_t flags, const void *out,
+                  const void *dout, const float *m, const float *l, float *dq,
+                  const ra_kv_grad *grads, void *workspace, size_t ws_bytes,
+                  void *stream);
+
 /* Merge n_parts partial softmax states over disjoint key sets into one (the
  * fusion layer's global normalisation, page "从百毫秒到百万Token", 系统架构设计,
  * 注意力融合层):

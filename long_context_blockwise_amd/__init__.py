@@ -27,6 +27,8 @@ from .ring_attn import (  # noqa: F401
     RA_OK,
     RingAttnContext,
     RingAttnError,
+    ring_attn_bwd,
+    ring_attn_bwd_workspace_size,
     ring_attn_fwd,
     ring_attn_last_error,
     ring_attn_merge,

@@ -1,0 +1,447 @@
+// attn_bwd_bf16.hip - gradients of blockwise attention (dQ, dK, dV) for bf16
+// inputs on CDNA4 (gfx950) MFMA, fp32 accumulation.
+//
+// For L = sum(dO * out), out = softmax(S) V with S = scale * Q K^T over the
+// visible keys, and P = exp(S - lse) the forward's probabilities:
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D = rowsum(dO * out),
+//     dQ = scale * dS K,   dK = scale * dS^T Q,
+// with every query head of a KV group adding into that KV head's dK and dV.
+// This is what training with ring attention needs per ring step (page "Ring
+// Attention：百万 Token 上下文的秘密", §5.1 训练效率): dQ stays with the
+// device's query chunk, dK and dV travel with the KV chunk they belong to.
+//
+// Three kernels.  bwd_pre turns the forward's final state into the per-row
+// log-sum-exp (log2 units) and computes D.  bwd_dq keeps a tile of query rows
+// resident and walks the key tiles like the forward kernel: with S^T = K Q^T
+// in the lane-per-row layout, P^T needs only the lane's own lse, dP^T = V dO^T
+// reads V exactly as the forward reads K, and dS^T is the B operand of
+// dQ^T += K^T dS^T (K read transposed, as the forward reads V).  bwd_dkdv
+// keeps 32 keys per wave resident (their K and V fragments in registers, their
+// dK^T and dV^T accumulators in the matrix-core result layout) and walks the
+// query rows that can see them in tiles of 32: S = Q K^T puts the keys on the
+// lanes, so P and dS are directly the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS, whose A operands are transposed reads of the Q and dO tiles.
+// Neither kernel needs atomics, and both are deterministic.
+#include "tile_common.h"
+
+namespace ra {
+namespace {
+
+constexpr float kPosInf = __builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Row statistics: 16 lanes per row
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A) {
+    const FwdArgs &a = A.f;
+    constexpr int EPL = D / 16;  // elements per lane
+    const int64_t rows = (int64_t)a.B * a.Lq * a.Hq;
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // (b * Lq + t) * Hq + h
+    const int sub = threadIdx.x & 15;
+    float acc = 0.f;
+    int64_t b = 0, t = 0;
+    int h = 0;
+    if (row < rows) {
+        h = (int)(row % a.Hq);
+        t = (row / a.Hq) % a.Lq;
+        b = row / ((int64_t)a.Hq * a.Lq);
+        const int64_t off = b * a.o_sb + t * a.o_ss + h * a.o_sh + sub * EPL;
+        const uint16_t *o = (const uint16_t *)A.out + off;
+        const uint16_t *g = (const uint16_t *)A.dout + off;
+        uint16_t ov[EPL], gv[EPL];
+        if constexpr (EPL == 8) {
+            *(u32x4 *)ov = *(const u32x4 *)o;
+            *(u32x4 *)gv = *(const u32x4 *)g;
+        } else {
+            *(u32x2 *)ov = *(const u32x2 *)o;
+            *(u32x2 *)gv = *(const u32x2 *)g;
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc = __builtin_fmaf(__builtin_bit_cast(float, (unsigned)ov[e] << 16),
+                                 __builtin_bit_cast(float, (unsigned)gv[e] << 16), acc);
+    }
+#pragma unroll
+    for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
+    if (row < rows && sub == 0) {
+        const float l = A.l[row];
+        const int64_t idx = ((b * a.Hq + h) * a.Lq + t) * 2;
+        A.ld[idx] = l > 0.f ? (A.m[row] + logf(l)) * kLog2e : kPosInf;
+        A.ld[idx + 1] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query rows resident, key tiles streamed (the forward's structure)
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const BwdArgs A) {
+    const FwdArgs &a = A.f;
+    using C = Cfg<D, BN, NW, 1>;
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(NS, C::TILE)
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;
+    token_range(a, wt.p0 + 32 * w, wt.p0 + 32 * w + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * w + l32);
+
+    // resident B operands: the row's queries and output gradients
+    bf16x8 qf[C::DS], gf[C::DS];
+    load_q(a, wt, row, g, 0, qf);
+    {
+        const uint16_t *gp = (const uint16_t *)A.dout + wt.b * a.o_sb + row.t * a.o_ss + row.h * a.o_sh + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row.ok) v = *(const u32x4 *)(gp + 16 * ds);
+            gf[ds] = to_bf16x8(v);
+        }
+    }
+    float lse2 = kPosInf, Drow = 0.f;  // rows past Lq get P = 0
+    if (row.ok) {
+        const int64_t idx = (((int64_t)wt.b * a.Hq + row.h) * a.Lq + row.t) * 2;
+        lse2 = A.ld[idx];
+        Drow = A.ld[idx + 1];
+    }
+    const float c2 = a.scale_log2;
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+
+    for (int c = 0; c < a.n_chunks; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, 0, kbeg, kend, ntiles, BN)) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto issue = [&](auto u, int t) {
+            const int64_t k0 = kbeg + (int64_t)t * BN;
+            load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
+            load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+        };
+        auto wait_for = [&](int need, int last) {
+            const int after = last - need;
+            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+        };
+
+        tile_barrier();  // the previous chunk's tiles are no longer read
+        const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
+        for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+        wait_for(0, pre - 1);
+        for_tiles<NS>(ntiles, [&](auto u, int it) {
+            constexpr int U = decltype(u)::value;
+            if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+            const int64_t k0 = kbeg + (int64_t)it * BN;
+            const bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
+            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
+            if (!skip) {
+                f32x16 s[C::KB], dp[C::KB];
+                scores<C>(kst(u), kaddr, qf, s);   // S^T = K Q^T
+                scores<C>(vst(u), kaddr, gf, dp);  // dP^T = V dO^T
+                if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
+                bf16x8 pf[2 * C::KB];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u32x4 pk;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int i0 = 8 * hh + 2 * j, i1 = i0 + 1;
+                            const float p0 = exp2_fast(__builtin_fmaf(s[kb][i0], c2, -lse2));
+                            const float p1 = exp2_fast(__builtin_fmaf(s[kb][i1], c2, -lse2));
+                            pk[j] = pack_bf16(p0 * (dp[kb][i0] - Drow), p1 * (dp[kb][i1] - Drow));
+                        }
+                        pf[2 * kb + hh] = to_bf16x8(pk);
+                    }
+                accumulate_pv<C>(kst(u), vaddr, pf, acc);
+            }
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
+        });
+    }
+
+    if (!row.ok) return;
+    // dQ element i of block db in lane l is d = 32db + 8(i/4) + 4g + i%4
+    float *dq = A.dq + row.srow * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            f32x4 v;
+            if (A.accumulate) v = *(const f32x4 *)(dq + 32 * db + 8 * i4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = A.scale * acc[db][4 * i4 + j];
+                v[j] = A.accumulate ? v[j] + x : x;
+            }
+            *(f32x4 *)(dq + 32 * db + 8 * i4) = v;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: keys resident (32 per wave), query-row tiles of 32 streamed
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
+
+// Stage u holds the Q tile (rows t0 .. t0+31, row-major, swizzled), then each
+// wave's copy of the rows' (lse2, D) pairs (256 bytes per wave), then the dO
+// tile; RA_STAGE_ARRAYS(NS, TILE + 1024) gives 2 * TILE + 2048 bytes a stage.
+template <int D, int NS>
+__global__ __launch_bounds__(kKvWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(const BwdArgs A) {
+    const FwdArgs &a = A.f;
+    using C = Cfg<D, 32, kKvWaves, 1>;  // 32-row tiles: TILE bytes each for Q and dO
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + 1;
+    RA_STAGE_ARRAYS(NS, C::TILE + 1024)
+    auto qtile = [&](auto u) { return kst(u); };
+    auto ldtile = [&](auto u) { return kst(u) + C::TILE; };
+    auto gtile = [&](auto u) { return vst(u); };
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int l32 = lane & 31, g = lane >> 5;
+    const ChunkArg ch = a.chunks[A.chunk];
+    const int64_t len = ch.len;
+    const int nkt = (int)((len + kKvKeys - 1) / kKvKeys);
+    int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = lid % nkt;  // earliest keys (most rows under causal masking) first
+    lid /= nkt;
+    const int hk = lid % a.Hkv;
+    const int b = lid / a.Hkv;
+    const int64_t kt0 = (int64_t)kt * kKvKeys;
+    const int64_t wk0 = kt0 + 32 * w;       // this wave's first key
+    const int64_t key = wk0 + l32;          // this lane's key
+    const bool key_ok = key < len;
+
+    // resident B operands: K^T and V^T fragments of the lane's key
+    bf16x8 kf[C::DS], vf[C::DS];
+    {
+        const uint16_t *kp = (const uint16_t *)ch.k + b * a.k_sb + key * a.k_ss + hk * a.k_sh + 8 * g;
+        const uint16_t *vp = (const uint16_t *)ch.v + b * a.v_sb + key * a.v_ss + hk * a.v_sh + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            if (key_ok) {
+                x = *(const u32x4 *)(kp + 16 * ds);
+                y = *(const u32x4 *)(vp + 16 * ds);
+            }
+            kf[ds] = to_bf16x8(x);
+            vf[ds] = to_bf16x8(y);
+        }
+    }
+    f32x16 dk[C::DB], dv[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+
+    // query rows that can see any key of the workgroup
+    const int64_t kp_lo = ch.start + kt0;
+    const int64_t kp_hi = ch.start + (kt0 + kKvKeys < len ? kt0 + kKvKeys : len) - 1;
+    int64_t t_lo = 0, t_hi = a.Lq - 1;
+    if (a.causal) t_lo = kp_lo - a.q_offset > t_lo ? kp_lo - a.q_offset : t_lo;
+    if (a.window > 0) {
+        const int64_t hi = kp_hi + a.window - a.q_offset;
+        t_hi = hi < t_hi ? hi : t_hi;
+        if (!a.causal) {
+            const int64_t lo = kp_lo - a.window - a.q_offset;
+            t_lo = lo > t_lo ? lo : t_lo;
+        }
+    }
+    t_lo &= ~(int64_t)31;
+    const int nrt = t_hi >= t_lo ? (int)((t_hi - t_lo) / 32 + 1) : 0;
+    const int ntiles = nrt * a.G;
+
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+    const float c2 = a.scale_log2;
+    const int64_t kpos = ch.start + key;
+
+    auto tile_of = [&](int it, int &h, int64_t &t0) {
+        const int gq = it / nrt;
+        h = hk * a.G + gq;
+        t0 = t_lo + 32 * (int64_t)(it % nrt);
+    };
+    auto issue = [&](auto u, int it) {
+        int h;
+        int64_t t0;
+        tile_of(it, h, t0);
+        const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
+        const uint16_t *gb = (const uint16_t *)A.dout + b * a.o_sb + h * a.o_sh;
+        load_tile<C>(qb, a.q_ss, t0, a.Lq, qtile(u), w, lane);
+        load_tile<C>(gb, a.o_ss, t0, a.Lq, gtile(u), w, lane);
+        // (lse2, D) of rows t0 .. t0+31: one dword per lane into the wave's own copy
+        const int64_t nrows = a.Lq - t0 < 32 ? a.Lq - t0 : 32;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(A.ld + (((int64_t)b * a.Hq + h) * a.Lq + t0) * 2), (short)0, (int)(nrows * 8), kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(ldtile(u) + 256 * w), 4, (unsigned)lane * 4u, 0, 0,
+                                                 0);
+    };
+    auto wait_for = [&](int need, int last) {
+        const int after = last - need;
+        wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+    };
+
+    const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
+    for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+    wait_for(0, pre - 1);
+    for_tiles<NS>(ntiles, [&](auto u, int it) {
+        constexpr int U = decltype(u)::value;
+        if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+        int h;
+        int64_t t0;
+        tile_of(it, h, t0);
+        const int64_t thi = t0 + 31 < a.Lq - 1 ? t0 + 31 : a.Lq - 1;
+        const bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
+        const bool full = t0 + 31 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
+        if (!skip) {
+            const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + 256 * w;
+            // S = Q K^T and dP = dO V^T: rows on M, this wave's keys on N
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds) {
+                s = mfma(kfrag<C>(qt, kaddr, ds, 0), kf[ds], s);
+                dp = mfma(kfrag<C>(gt, kaddr, ds, 0), vf[ds], dp);
+            }
+            // element i is row t0 + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
+            if (!full) {
+                const int64_t big = 1 << 30;
+                const int64_t base = a.q_offset + t0 + 4 * g - kpos;  // qpos - kpos at ro = 0
+                int64_t lo = -big, hi = a.Lq - t0 - 4 * g;
+                if (a.causal) lo = -base;
+                if (a.window > 0) {
+                    hi = a.window - base + 1 < hi ? a.window - base + 1 : hi;
+                    if (!a.causal) lo = -a.window - base;
+                }
+                if (!key_ok) lo = big;
+                lo = lo < -big ? -big : (lo > big ? big : lo);
+                hi = hi < -big ? -big : (hi > big ? big : hi);
+                const int lo32 = (int)lo, hi32 = (int)hi;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int ro = 8 * (i >> 2) + (i & 3);
+                    if (ro < lo32 || ro >= hi32) s[i] = kNegInf;
+                }
+            }
+            // P and dS of the 16 rows, packed as B operands (k-steps of 16 rows)
+            bf16x8 pp[2], pd[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4 a4, b4;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    // rows 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
+                    const f32x4 x = *(const f32x4 *)(lt + 8 * (16 * hh + 8 * jj + 4 * g));
+                    const f32x4 y = *(const f32x4 *)(lt + 8 * (16 * hh + 8 * jj + 4 * g) + 16);
+                    const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
+#pragma unroll
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
+                        const float p0 = exp2_fast(__builtin_fmaf(s[i0], c2, -l4[2 * r2]));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[i1], c2, -l4[2 * r2 + 1]));
+                        a4[2 * jj + r2] = pack_bf16(p0, p1);
+                        b4[2 * jj + r2] = pack_bf16(p0 * (dp[i0] - d4[2 * r2]), p1 * (dp[i1] - d4[2 * r2 + 1]));
+                    }
+                }
+                pp[hh] = to_bf16x8(a4);
+                pd[hh] = to_bf16x8(b4);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    dv[db] = mfma(vfrag<C>(gt, vaddr, ks, db), pp[ks], dv[db]);
+                    dk[db] = mfma(vfrag<C>(qt, vaddr, ks, db), pd[ks], dk[db]);
+                }
+        }
+        if (it + 1 < ntiles) {
+            const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+            wait_for(it + 1, last);
+        }
+    });
+
+    if (!key_ok) return;
+    // element i of block db in lane l is d = 32db + 8(i/4) + 4g + i%4 of the lane's key
+    const int64_t off = ((b * len + key) * a.Hkv + hk) * D + 4 * g;
+    float *pk = A.dk + off, *pv = A.dv + off;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int e = 32 * db + 8 * i4;
+            f32x4 x, y;
+            if (A.accumulate) {
+                x = *(const f32x4 *)(pk + e);
+                y = *(const f32x4 *)(pv + e);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float gk = A.scale * dk[db][4 * i4 + j], gv = dv[db][4 * i4 + j];
+                x[j] = A.accumulate ? x[j] + gk : gk;
+                y[j] = A.accumulate ? y[j] + gv : gv;
+            }
+            *(f32x4 *)(pk + e) = x;
+            *(f32x4 *)(pv + e) = y;
+        }
+}
+
+}  // namespace
+
+int bwd_dq_row_tile() { return 128; }
+
+hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s) {
+    const int64_t rows = (int64_t)a.f.B * a.f.Lq * a.f.Hq;
+    if (rows == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((rows * 16 + 255) / 256);
+    if (d == 128)
+        hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s) {
+    const unsigned grid = (unsigned)((int64_t)a.f.n_rowtiles * a.f.Hkv * a.f.B);
+    if (grid == 0) return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s) {
+    const int64_t len = a.f.chunks[a.chunk].len;
+    const int64_t nkt = (len + kKvKeys - 1) / kKvKeys;
+    const unsigned grid = (unsigned)(nkt * a.f.Hkv * a.f.B);
+    if (grid == 0) return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace ra

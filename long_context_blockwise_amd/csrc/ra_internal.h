@@ -50,6 +50,20 @@ struct FwdArgs {
     ChunkArg chunks[kMaxChunks];
 };
 
+// Arguments of the backward kernels.  The query rows, chunks, strides and
+// masks are those of the forward (f); out and dout share f's o strides.
+struct BwdArgs {
+    FwdArgs f;
+    const void *out, *dout;  // [B, Lq, Hq, d_v] in the input dtype
+    const float *m, *l;      // forward state after all chunks [B, Lq, Hq]
+    float *ld;               // workspace [B, Hq, Lq][2]: (m + ln l) log2(e), rowsum(dO * out)
+    float *dq;               // [B, Lq, Hq, d_qk] fp32, dense
+    float *dk, *dv;          // dK/dV kernel: the launch's chunk, [B, len, Hkv, d] fp32, dense
+    int chunk;               // dK/dV kernel: index into f.chunks
+    int accumulate;          // add into dq / dk / dv instead of overwriting them
+    float scale;             // logit scale
+};
+
 struct MergeArgs {
     const float *pm, *pl, *pO;  // [n, rows](, d_v)
     float *m, *l, *O;           // merged state or null
@@ -70,5 +84,12 @@ hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s);
 int fwd_f32_row_tile(int d);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+// Backward, bf16 with d = 64 or 128: row statistics, dQ over the chunks of
+// a.f (rows tiled like the forward, bwd_dq_row_tile rows per workgroup), and
+// dK/dV of chunk a.chunk.
+int bwd_dq_row_tile();
+hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s);
 
 }  // namespace ra

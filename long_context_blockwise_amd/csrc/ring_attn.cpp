@@ -21,9 +21,12 @@
 #include "../../include/ring_attn.h"
 #include "ra_internal.h"
 
+using ra::BwdArgs;
 using ra::ChunkArg;
 using ra::FwdArgs;
 using ra::MergeArgs;
+
+static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct ra_ctx {
     int device;
@@ -596,6 +599,115 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     if (pl.stage && nl > 1) {
         if ((e = hipEventRecord(ctx->join, ctx->side)) != hipSuccess) return hip_fail(e, "event record");
         if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess) return hip_fail(e, "join");
+    }
+    return RA_OK;
+}
+
+// Row statistics of the backward: (lse2, D) per (b, h, t).
+static size_t bwd_ld_bytes(const ra_desc *d, int64_t Lq) { return align_up((size_t)d->B * d->Hq * Lq * 8); }
+
+static int check_bwd(const ra_desc *d, int64_t Lq, Strides *st) {
+    int rc = check_desc(d, Lq, st);
+    if (rc) return rc;
+    if (d->dtype != RA_BF16 || (d->d_qk != 64 && d->d_qk != 128))
+        return fail(RA_ERR_UNSUPPORTED, "the backward is built for bf16 with d_qk = d_v in {64, 128}");
+    if (kv_fp8(d)) return fail(RA_ERR_UNSUPPORTED, "the backward takes bf16 keys and values");
+    for (int i = 0; i < 3; ++i)
+        if (st->q[i] >= ((int64_t)1 << 24) || st->o[i] >= ((int64_t)1 << 24))
+            return fail(RA_ERR_UNSUPPORTED, "q/out strides must be below 2^24 elements");
+    return RA_OK;
+}
+
+int ring_attn_bwd_workspace_size(const ra_desc *d, int64_t Lq, size_t *bytes) {
+    if (!bytes) return fail(RA_ERR_INVALID_ARG, "bytes is NULL");
+    Strides st;
+    int rc = check_bwd(d, Lq, &st);
+    if (rc) return rc;
+    *bytes = bwd_ld_bytes(d, Lq);
+    return RA_OK;
+}
+
+int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, const ra_kv_chunk *chunks, int P,
+                  int causal, int64_t q_offset, uint32_t flags, const void *out, const void *dout, const float *m,
+                  const float *l, float *dq, const ra_kv_grad *grads, void *workspace, size_t ws_bytes,
+                  void *stream) {
+    if (!ctx) return fail(RA_ERR_INVALID_ARG, "ctx is NULL");
+    Strides st;
+    int rc = check_bwd(d, Lq, &st);
+    if (rc) return rc;
+    if (P < 0 || P > ra::kMaxChunks) return fail(RA_ERR_INVALID_ARG, "P must be in 0..%d", ra::kMaxChunks);
+    if (P > 0 && (!chunks || !grads)) return fail(RA_ERR_INVALID_ARG, "chunks and grads must be given");
+    if ((flags & ~RA_FLAG_ACCUMULATE) != 0) return fail(RA_ERR_INVALID_ARG, "the backward takes only ACCUMULATE");
+    const bool accumulate = (flags & RA_FLAG_ACCUMULATE) != 0;
+    auto misaligned = [](const void *p) { return ((uintptr_t)p & 15) != 0; };
+    for (int c = 0; c < P; ++c) {
+        if (chunks[c].len < 0) return fail(RA_ERR_INVALID_ARG, "chunk %d: negative length", c);
+        if (chunks[c].len == 0) continue;
+        if (!chunks[c].k || !chunks[c].v || !grads[c].dk || !grads[c].dv)
+            return fail(RA_ERR_INVALID_ARG, "chunk %d: k, v, dk and dv must be given", c);
+        if (misaligned(chunks[c].k) || misaligned(chunks[c].v) || misaligned(grads[c].dk) ||
+            misaligned(grads[c].dv))
+            return fail(RA_ERR_INVALID_ARG, "chunk %d: k, v, dk and dv must be 16-byte aligned", c);
+    }
+    if (Lq > 0) {
+        if (!q || !out || !dout || !m || !l || !dq)
+            return fail(RA_ERR_INVALID_ARG, "q, out, dout, m, l and dq must be given");
+        if (misaligned(q) || misaligned(out) || misaligned(dout) || misaligned(dq))
+            return fail(RA_ERR_INVALID_ARG, "q, out, dout and dq must be 16-byte aligned");
+    }
+    const size_t need = Lq > 0 ? bwd_ld_bytes(d, Lq) : 0;
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (need > 0 && ((uintptr_t)workspace % kAlign) != 0)
+        return fail(RA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return fail(RA_ERR_HIP, "hipSetDevice(%d) failed", ctx->device);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    BwdArgs A;
+    std::memset(&A, 0, sizeof A);
+    A.f = base_args(d, st, q, Lq, causal, q_offset, nullptr);
+    A.out = out, A.dout = dout, A.m = m, A.l = l;
+    A.ld = (float *)workspace;
+    A.dq = dq;
+    A.scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->d_qk);
+    const int bm = ra::bwd_dq_row_tile();
+    A.f.Lq_pad = A.f.Lq * A.f.G <= bm ? A.f.Lq : (A.f.Lq + bm - 1) / bm * bm;
+    A.f.n_rowtiles = (int)(((int64_t)A.f.G * A.f.Lq_pad + bm - 1) / bm);
+
+    if (Lq > 0) {
+        if ((e = ra::launch_bwd_pre(A, d->d_qk, s)) != hipSuccess) return hip_fail(e, "backward row statistics");
+        // dQ: chunks that share k/v strides go in one launch; later launches add
+        std::vector<int> steps;
+        for (int c = 0; c < P; ++c)
+            if (classify(Lq, q_offset, causal, d->window, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
+                steps.push_back(c);
+        std::vector<std::vector<int>> launches = group_ring_launches(d, chunks, steps, false);
+        bool first = true;
+        for (const std::vector<int> &grp : launches) {
+            A.accumulate = accumulate || !first;
+            A.f.n_chunks = (int)grp.size();
+            for (size_t i = 0; i < grp.size(); ++i) {
+                const ra_kv_chunk &c = chunks[grp[i]];
+                A.f.chunks[i] = ChunkArg{c.k, c.v, c.start, c.len, nullptr, nullptr};
+            }
+            if (!grp.empty()) set_chunk_strides(A.f, d, chunks[grp[0]].len);
+            // with no chunk to walk, the launch writes dQ = 0 (or leaves the sum)
+            if ((e = ra::launch_bwd_dq(A, d->d_qk, s)) != hipSuccess) return hip_fail(e, "backward dQ launch");
+            first = false;
+        }
+    }
+    // dK, dV of every chunk (zero, or unchanged when accumulating, where no row sees it)
+    A.accumulate = accumulate;
+    A.f.n_chunks = 1;
+    A.chunk = 0;
+    for (int c = 0; c < P; ++c) {
+        if (chunks[c].len == 0) continue;
+        A.f.chunks[0] = ChunkArg{chunks[c].k, chunks[c].v, chunks[c].start, chunks[c].len, nullptr, nullptr};
+        set_chunk_strides(A.f, d, chunks[c].len);
+        A.dk = grads[c].dk, A.dv = grads[c].dv;
+        if ((e = ra::launch_bwd_dkdv(A, d->d_qk, s)) != hipSuccess) return hip_fail(e, "backward dK/dV launch");
     }
     return RA_OK;
 }

@@ -1,0 +1,480 @@
+// tile_common.h - CDNA4 (gfx950) building blocks shared by the attention
+// kernels of libringattn: vector types, MFMA and LDS-transpose wrappers,
+// the XOR-swizzled row-major LDS tile layout and its fragment reads, the
+// HBM->LDS tile loads, query-row geometry, the causal / local-window masks,
+// and the statically named stage buffers with their waits.
+//
+// Everything here has internal linkage (anonymous namespace); each kernel
+// source includes it once.
+#pragma once
+
+#include <type_traits>
+
+#include "ra_internal.h"
+
+// Tuning knobs (compile-time): LDS fragments read ahead of the MFMAs (0 lets
+// the compiler schedule them) and whether waves raise their issue priority
+// while they feed the matrix cores.
+#ifndef RA_TUNE_PF
+#define RA_TUNE_PF 4
+#endif
+#ifndef RA_TUNE_SETPRIO
+#define RA_TUNE_SETPRIO 1
+#endif
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+// The softmax reference moves when a tile max exceeds it by more than this
+// (log2 units): p = exp2(s*c - m_ref) <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+// gfx9 buffer descriptor word 3 for raw (untyped) dword access
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of x over lanes l and l^32 (the two lanes that share a query row).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second; with both holding x, one holds the low half twice and
+// the other the high half twice, so their max is the pair max in every lane.
+// It is written as inline asm because the compiler's builtin returns the same
+// register for both results.  The s_nops cover the VALU-write -> permlane and
+// permlane -> VALU-read wait states, which the compiler does not see inside asm.
+__device__ inline float max_pair(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
+
+// Index of the calling wave in its workgroup, as a scalar: the compiler
+// cannot see that threadIdx.x >> 6 is uniform across a wave, and would keep
+// everything derived from it (row ranges, branch conditions) in vector
+// registers and exec-masked branches.
+__device__ inline int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
+// each XCD runs a contiguous range of logical tiles (tiles that share K/V then
+// share that XCD's L2).
+__device__ inline int xcd_remap(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, s = bid >> 3;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
+}
+
+// Swizzle of the 16-byte units of LDS row r (key r of a tile): unit u is
+// stored at u ^ swz<D>(r).  gfx950's LDS serves 256 bytes (64 banks) per
+// cycle: 16 lanes of a ds_read_b128, 32 lanes of a ds_read_b64_tr_b16.  A K
+// fragment read touches 16 consecutive rows at one unit; a transposed V read
+// touches 4 consecutive rows x 4 units.  With rows of >= 256 bytes both land on
+// 16 distinct units of a 256-byte window when swz(r) = 4(r&3) + ((r>>2)&3).
+// 128-byte rows (d=64) pair up in a window, so the row-pair index r>>1 is used.
+template <int D>
+__device__ inline int swz(int r) {
+    if constexpr (D >= 128)
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ inline bf16x8 to_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ inline unsigned pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ inline bf16x8 lds_read_b128(const char *lds, int byte) {
+    return *reinterpret_cast<const bf16x8 *>(lds + byte);
+}
+
+// Two transposed 4-key reads make one V^T A-operand fragment.
+__device__ inline bf16x8 lds_read_vt(const char *lds, int byte0, int byte1) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + byte0));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + byte1));
+    const s16x8 xy = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, xy);
+}
+
+__device__ inline f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int BN, int NW, int KSPLIT>
+struct Cfg {
+    static constexpr int NT = NW * 64;           // threads
+    static constexpr int ROWW = NW / KSPLIT;     // waves along rows
+    static constexpr int BM = 32 * ROWW;         // query rows per workgroup
+    static constexpr int KW = BN / KSPLIT;       // keys per wave per tile
+    static constexpr int KB = KW / 32;           // 32-key blocks per wave
+    static constexpr int DS = D / 16;            // reduction steps of S^T
+    static constexpr int DB = D / 32;            // 32-wide blocks of O^T
+    static constexpr int ROWB = D * 2;           // bytes per K/V row in LDS
+    static constexpr int UPR = D / 8;            // 16-byte units per row
+    static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
+    static constexpr int LOADS = TILE / 1024;    // 1 KiB wave loads per K (or V) tile
+    static constexpr int LOADS_PER_WAVE = LOADS / NW;
+    static constexpr int PF = RA_TUNE_PF;        // LDS fragments read ahead of the MFMAs
+    static constexpr int SWB = D >= 128 ? 16 : 8;  // units covered by the swizzle
+    static constexpr int NKA = SWB / 2;            // per-lane K address patterns
+    static constexpr int NVD = SWB / 4;            // per-lane V^T address patterns per read
+    static_assert(KW % 32 == 0, "each wave needs whole 32-key blocks");
+    static_assert(D % 64 == 0, "head size must be a multiple of 64");
+    static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+};
+
+// ---------------------------------------------------------------------------
+// Pieces shared by both kernels
+// ---------------------------------------------------------------------------
+
+// Rows and key range of one workgroup.
+struct WorkTile {
+    int b, hk, split;
+    int64_t p0;              // first packed row
+    int64_t wg_tlo, wg_thi;  // token range of the workgroup's rows
+};
+
+__device__ inline void token_range(const FwdArgs &a, int64_t pa, int64_t pb, int64_t &lo, int64_t &hi) {
+    const int64_t pend = (int64_t)a.G * a.Lq_pad;
+    pb = (pb < pend ? pb : pend) - 1;
+    if (pa / a.Lq_pad == pb / a.Lq_pad) {
+        lo = pa % a.Lq_pad;
+        hi = pb % a.Lq_pad;
+        hi = hi < a.Lq - 1 ? hi : a.Lq - 1;
+    } else {
+        lo = 0;
+        hi = a.Lq - 1;
+    }
+}
+
+template <class C>
+__device__ inline WorkTile work_tile(const FwdArgs &a) {
+    WorkTile wt;
+    const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
+    int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int rt = lid % a.n_rowtiles;
+    lid /= a.n_rowtiles;
+    wt.split = lid % nsplit;
+    lid /= nsplit;
+    wt.hk = lid % a.Hkv;
+    wt.b = lid / a.Hkv;
+    if (a.Lq_pad % C::BM == 0) {  // one head per tile; heaviest (latest) rows first
+        const int64_t ntt = a.Lq_pad / C::BM;
+        const int gq = rt % a.G;
+        const int64_t tt = ntt - 1 - rt / a.G;
+        wt.p0 = gq * a.Lq_pad + tt * C::BM;
+    } else {
+        wt.p0 = (int64_t)rt * C::BM;
+    }
+    token_range(a, wt.p0, wt.p0 + C::BM, wt.wg_tlo, wt.wg_thi);
+    return wt;
+}
+
+// The query row a lane owns.
+struct LaneRow {
+    int64_t t, qpos, srow;
+    int h;
+    bool ok;
+};
+
+__device__ inline LaneRow lane_row(const FwdArgs &a, const WorkTile &wt, int64_t prow) {
+    LaneRow r;
+    const int gq = (int)(prow / a.Lq_pad);
+    r.t = prow % a.Lq_pad;
+    r.ok = prow < (int64_t)a.G * a.Lq_pad && r.t < a.Lq;
+    r.h = wt.hk * a.G + gq;
+    r.qpos = a.q_offset + r.t;
+    r.srow = ((int64_t)wt.b * a.Lq + r.t) * a.Hq + r.h;  // state row index
+    return r;
+}
+
+// Resident query fragments (B operand of S^T = K Q^T) for dimensions d0 ..
+// d0 + 16*NDS - 1: fragment ds of a lane holds d = d0 + 16ds + 8g .. +8.
+template <int NDS>
+__device__ inline void load_q(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0,
+                              bf16x8 (&qf)[NDS]) {
+    const uint16_t *qp = (const uint16_t *)a.q + wt.b * a.q_sb + r.t * a.q_ss + r.h * a.q_sh + d0 + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r.ok) v = *(const u32x4 *)(qp + 16 * ds);
+        qf[ds] = to_bf16x8(v);
+    }
+}
+
+// Per-lane LDS byte addresses.  The swizzle only touches the low 4 bits of a
+// unit index (3 for d=64), so every read is a per-lane base plus a
+// compile-time offset.
+// K fragment (kb, ds): row r0 + 32kb + l32, unit u = 2ds+g, stored at u ^ swz(row)
+// (r0 and 32kb keep the low 4 bits of the row).
+template <class C>
+__device__ inline void k_addrs(int r0, int l32, int g, int (&kaddr)[C::NKA]) {
+    const int sw = swz<C::DB * 32>(l32);
+    const int rowb = (r0 + l32) * C::ROWB;
+#pragma unroll
+    for (int x = 0; x < C::NKA; ++x) kaddr[x] = rowb + (((2 * x + g) ^ sw) << 4);
+}
+// V^T fragment (ks, db), read hh of 2: lane = 16G + 4k + q provides V[key][d]
+// with key = r0 + 16ks + 4(G>>1) + 8hh + k and d = 32db + 16(G&1) + 4q,
+// i.e. unit u = 4db + 2(G&1) + (q>>1), half q&1.
+template <class C>
+__device__ inline void v_addrs(int r0, int lane, int (&vaddr)[2][C::NVD]) {
+    const int G = lane >> 4, k = (lane >> 2) & 3, q = lane & 3;
+    const int gi = G & 1, gk = G >> 1;
+    const int c = 2 * gi + (q >> 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int row = r0 + 4 * gk + 8 * hh + k;
+        const int sw = swz<C::DB * 32>(row);
+#pragma unroll
+        for (int dbl = 0; dbl < C::NVD; ++dbl)
+            vaddr[hh][dbl] = row * C::ROWB + (((4 * dbl + c) ^ sw) << 4) + ((q & 1) << 3);
+    }
+}
+
+template <class C>
+__device__ inline bf16x8 kfrag(const char *kt, const int (&kaddr)[C::NKA], int ds, int kb) {
+    return lds_read_b128(kt, kaddr[ds % C::NKA] + 16 * C::SWB * (ds / C::NKA) + 32 * kb * C::ROWB);
+}
+
+template <class C>
+__device__ inline bf16x8 vfrag(const char *vt, const int (&vaddr)[2][C::NVD], int ks, int db) {
+    const int off = 16 * C::SWB * (db / C::NVD) + 16 * ks * C::ROWB;
+    return lds_read_vt(vt, vaddr[0][db % C::NVD] + off, vaddr[1][db % C::NVD] + off);
+}
+
+// One K (or V) tile, keys k0 .. k0+BN-1 of a chunk, HBM -> LDS; keys >= kend
+// are zero-filled by the descriptor.  Each wave issues LOADS_PER_WAVE loads.
+// The host keeps token strides below 2^24 elements, so the byte offsets
+// within a tile (< BN x stride x 2 < 2^31) are computed in 32 bits.
+template <class C>
+__device__ inline void load_tile(const uint16_t *base, int64_t stride, int64_t k0, int64_t kend, char *dst,
+                                 int w, int lane) {
+    constexpr int BN = C::TILE / C::ROWB;
+    const unsigned stride_b = (unsigned)stride * 2u;
+    const unsigned nvalid = (unsigned)(kend - k0 < BN ? kend - k0 : BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + k0 * stride), (short)0, (int)(nvalid * stride_b), kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
+        const int inst = j * (C::NT / 64) + w;
+        const int pos = inst * 64 + lane;
+        const int r = pos / C::UPR, u = (pos % C::UPR) ^ swz<C::DB * 32>(r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + inst * 1024), 16,
+                                                 (unsigned)r * stride_b + (unsigned)(u * 16), 0, 0, 0);
+    }
+}
+
+// Keys of a chunk a lane's row may see, as a range [lo, hi) of key indices
+// counted from the chunk's first processed key kbeg: below kend, not after
+// the row's position under causal masking, and within the local window.
+// Clamped to +-2^30 so that per-tile offsets stay in 32 bits.
+struct VisRange {
+    int lo, hi;
+};
+
+__device__ inline VisRange visible_range(const FwdArgs &a, const LaneRow &r, int64_t cstart, int64_t kbeg,
+                                         int64_t kend) {
+    const int64_t rel = r.qpos - cstart - kbeg;  // the row's own key index
+    int64_t lo = -(1 << 30), hi = kend - kbeg;
+    if (a.causal) hi = rel + 1 < hi ? rel + 1 : hi;
+    if (a.window > 0) {
+        lo = rel - a.window;
+        if (!a.causal) hi = rel + a.window + 1 < hi ? rel + a.window + 1 : hi;
+    }
+    const int64_t big = 1 << 30;
+    lo = lo < -big ? -big : (lo > big ? big : lo);
+    hi = hi < -big ? -big : (hi > big ? big : hi);
+    return VisRange{(int)lo, (int)hi};
+}
+
+// Mask the keys a lane's row must not see in a tile whose first key is
+// `rel` keys after kbeg: element i of block kb is key 32kb + 8(i/4) + 4g +
+// i%4 of the tile, visible iff it lies in [lo - rel, hi - rel).
+template <class C>
+__device__ inline void mask_scores(f32x16 (&s)[C::KB], VisRange v, int rel, int g) {
+    const int hi = v.hi - rel - 4 * g;  // compare against the lane-independent part of the key
+    const int lo = v.lo - rel - 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
+            if (key >= hi || key < lo) s[kb][i] = kNegInf;
+        }
+}
+
+// Keys k0 .. k0+n-1 of a chunk (absolute k0 + cstart) against the rows of
+// positions q_offset + tlo .. q_offset + thi: none visible to any row
+// (skipped) / all visible to all rows (no mask needed).
+__device__ inline bool keys_unseen(const FwdArgs &a, int64_t cstart, int64_t k0, int64_t n, int64_t tlo,
+                                   int64_t thi) {
+    const int64_t first = cstart + k0, last = first + n - 1;
+    if (a.causal && first > a.q_offset + thi) return true;
+    if (a.window > 0) {
+        if (last < a.q_offset + tlo - a.window) return true;
+        if (!a.causal && first > a.q_offset + thi + a.window) return true;
+    }
+    return false;
+}
+
+__device__ inline bool keys_all_seen(const FwdArgs &a, int64_t cstart, int64_t k0, int64_t n, int64_t kend,
+                                     int64_t tlo, int64_t thi) {
+    const int64_t first = cstart + k0, last = first + n - 1;
+    if (k0 + n > kend) return false;
+    if (a.causal && last > a.q_offset + tlo) return false;
+    if (a.window > 0) {
+        if (first < a.q_offset + thi - a.window) return false;
+        if (!a.causal && last > a.q_offset + tlo + a.window) return false;
+    }
+    return true;
+}
+
+// S^T (KB 32-key blocks) = K Q^T from an LDS tile over the NDS reduction
+// steps whose K units start at kt, PF fragments in flight.
+template <class C, int NDS>
+__device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[NDS],
+                              f32x16 (&s)[C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    constexpr int N = NDS * C::KB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = kfrag<C>(kt, kaddr, n / C::KB, n % C::KB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        s[n % C::KB] = mfma(fr[n % PF], qf[n / C::KB], s[n % C::KB]);
+        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, (n + PF) / C::KB, (n + PF) % C::KB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// O^T += V^T P^T over the wave's keys of an LDS tile, for the NDB output
+// blocks whose V units start at vt, PF fragments in flight.  (Any product
+// X^T += T^T Y^T of an LDS tile T with B operands Y^T in the P^T layout.)
+template <class C, int NDB>
+__device__ inline void accumulate_pv(const char *vt, const int (&vaddr)[2][C::NVD], const bf16x8 (&pf)[2 * C::KB],
+                                     f32x16 (&o)[NDB]) {
+    constexpr int N = 2 * C::KB * NDB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = vfrag<C>(vt, vaddr, n / NDB, n % NDB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        o[n % NDB] = mfma(fr[n % PF], pf[n / NDB], o[n % NDB]);
+        if (n + PF < N) fr[n % PF] = vfrag<C>(vt, vaddr, (n + PF) / NDB, (n + PF) % NDB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Key range of chunk c for this workgroup; returns false when nothing is
+// visible.  With a local window the first tile is the one holding the
+// earliest key any of the workgroup's rows may see (kbeg moves by whole
+// tiles, so tiles stay aligned to the chunk or sub-range start).
+__device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, int sub, int64_t &kbeg,
+                                   int64_t &kend, int &ntiles, int bn) {
+    const ChunkArg &ch = a.chunks[c];
+    kbeg = 0;
+    kend = ch.len;
+    if (a.split_mode) {
+        kbeg = sub * a.sub_len;
+        kend = kbeg + a.sub_len < ch.len ? kbeg + a.sub_len : ch.len;
+    }
+    int64_t kstop = kend;
+    if (a.causal || a.window > 0) {
+        // keys < vis can be visible to the last row
+        const int64_t vis = a.q_offset + wt.wg_thi - ch.start + 1 + (a.causal ? 0 : a.window);
+        kstop = vis < kstop ? vis : kstop;
+    }
+    if (a.window > 0) {
+        const int64_t lo = a.q_offset + wt.wg_tlo - a.window - ch.start;  // first key the first row may see
+        if (lo > kbeg) kbeg += (lo - kbeg) / bn * bn;
+    }
+    if (kstop <= kbeg) return false;
+    ntiles = (int)((kstop - kbeg + bn - 1) / bn);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Tile stages: NS statically named K and V buffers per workgroup.  Tile t
+// lives in stage t % NS; loads run NS-1 tiles ahead of the compute, and each
+// wait lets the loads of later tiles stay in flight.
+// ---------------------------------------------------------------------------
+// K and V of a tile share one array (K first, V at +TILE); the compiler
+// tracks in-flight HBM->LDS loads per array, and a handful of arrays stays
+// within what it can tell apart.
+#define RA_STAGE_ARRAYS(NS, TILE)                                                      \
+    __shared__ __attribute__((aligned(1024))) char kv0[2 * (TILE)];                   \
+    __shared__ __attribute__((aligned(1024))) char kv1[2 * (TILE)];                   \
+    __shared__ __attribute__((aligned(1024))) char kv2[(NS) > 2 ? 2 * (TILE) : 16];   \
+    __shared__ __attribute__((aligned(1024))) char kv3[(NS) > 3 ? 2 * (TILE) : 16];   \
+    __shared__ __attribute__((aligned(1024))) char kv4[(NS) > 4 ? 2 * (TILE) : 16];   \
+    auto kst = [&](auto u) -> char * {                                                \
+        constexpr int U = decltype(u)::value % (NS);                                  \
+        if constexpr (U == 0) return kv0;                                             \
+        else if constexpr (U == 1) return kv1;                                        \
+        else if constexpr (U == 2) return kv2;                                        \
+        else if constexpr (U == 3) return kv3;                                        \
+        else return kv4;                                                              \
+    };                                                                                \
+    auto vst = [&](auto u) -> char * { return kst(u) + (TILE); };
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// Workgroup barrier for the tile buffers: each wave's own LDS reads and
+// writes have completed (lgkmcnt 0) and the compiler may not move memory
+// operations across it.  Unlike __syncthreads() it does not wait for the
+// wave's in-flight HBM->LDS tile loads (that fence would drain vmcnt and
+// serialise the prefetch); their completion is waited for explicitly.
+__device__ inline void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most `tiles` tiles' loads (LPT load instructions each) of
+// this wave are still in flight, then synchronise the workgroup.
+template <int LPT>
+__device__ inline void wait_tiles_in_flight(int tiles) {
+    switch (tiles) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory"); break;
+    }
+    tile_barrier();
+}
+
+// Run f(ic<t % NS>{}, t) for tiles t = 0 .. n-1: the stage of every call is a
+// compile-time constant, so each call names its LDS buffers statically.
+template <int NS, class F>
+__device__ inline void for_tiles(int n, F &&f) {
+    static_assert(NS >= 2 && NS <= 5, "2..5 stages");
+    for (int t = 0; t < n; t += NS) {
+        f(ic<0>{}, t);
+        if (t + 1 < n) f(ic<1>{}, t + 1);
+        if constexpr (NS > 2) if (t + 2 < n) f(ic<2 % NS>{}, t + 2);
+        if constexpr (NS > 3) if (t + 3 < n) f(ic<3 % NS>{}, t + 3);
+        if constexpr (NS > 4) if (t + 4 < n) f(ic<4 % NS>{}, t + 4);
+    }
+}
+
+}  // namespace
+}  // namespace ra

@@ -40,7 +40,7 @@ from typing import List, Optional, Tuple
 
 import torch
 
-_TENSOR_Q, _TENSOR_K, _TENSOR_V = 0, 1, 2
+_TENSOR_Q, _TENSOR_K, _TENSOR_V, _TENSOR_DO = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
@@ -164,6 +164,12 @@ class Inputs:
         if self.k_exps is not None:
             return [(self.ks[c], self.vs[c], self.starts[c], self.k_exps[c], self.v_exps[c]) for c in idx]
         return [(self.ks[c], self.vs[c], self.starts[c]) for c in idx]
+
+
+def output_grad(wl: Workload, device="cpu", std: float = 1.0) -> torch.Tensor:
+    """A seeded gradient of the attention output, ``[B, Lq, Hq, d_v]`` in the
+    workload dtype (N(0,1)*std), for the backward pass."""
+    return draw((wl.B, wl.Lq, wl.Hq, wl.d_v), std, wl.torch_dtype, device, wl.seed, _TENSOR_DO)
 
 
 def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:

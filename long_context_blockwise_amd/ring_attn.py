@@ -34,7 +34,8 @@ RA_CHUNK_SKIP, RA_CHUNK_FULL, RA_CHUNK_DIAG = 0, 1, 2
 
 EXPORTS = ("ring_attn_version", "ring_attn_last_error", "ring_attn_ctx_create",
            "ring_attn_ctx_destroy", "ring_attn_ring_order", "ring_attn_plan",
-           "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge")
+           "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge",
+           "ring_attn_bwd_workspace_size", "ring_attn_bwd")
 
 
 class RingAttnError(RuntimeError):
@@ -55,6 +56,10 @@ class ra_desc(ctypes.Structure):
 class ra_kv_chunk(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("start", ctypes.c_int64),
                 ("len", ctypes.c_int64), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
+
+
+class ra_kv_grad(ctypes.Structure):
+    _fields_ = [("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,8 +99,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, sz, vp]
         lib.ring_attn_merge.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_int, vp]
+        lib.ring_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(ra_desc), i64, ctypes.POINTER(sz)]
+        lib.ring_attn_bwd.argtypes = [vp, ctypes.POINTER(ra_desc), vp, i64, ctypes.POINTER(ra_kv_chunk),
+                                      ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp, vp,
+                                      ctypes.POINTER(ra_kv_grad), vp, sz, vp]
         for name in ("ring_attn_ctx_create", "ring_attn_ctx_destroy", "ring_attn_ring_order",
-                     "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge"):
+                     "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge",
+                     "ring_attn_bwd_workspace_size", "ring_attn_bwd"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -313,3 +323,66 @@ def ring_attn_merge(m_parts, l_parts, O_parts, out_dtype=None, *, out=None, stat
                                   O_parts.data_ptr(), ptr(m), ptr(l), ptr(O), ptr(out), code,
                                   stream.cuda_stream))
     return out, state
+
+
+def ring_attn_bwd_workspace_size(q, chunks, scale: float = 0.0, window: int = 0) -> int:
+    d, _ = make_desc(q, chunks, scale, window=window)
+    n = ctypes.c_size_t()
+    _check(load().ring_attn_bwd_workspace_size(ctypes.byref(d), q.shape[1], ctypes.byref(n)))
+    return int(n.value)
+
+
+def ring_attn_bwd(q, chunks, out, dout, state, causal: bool = False, q_offset: int = 0, *, flags: int = 0,
+                  dq=None, grads=None, scale: float = 0.0, window: int = 0,
+                  ctx: Optional[RingAttnContext] = None, workspace=None, stream=None):
+    """Gradients of one device's share of ring attention; returns ``(dq, [(dk, dv), ...])``.
+
+    ``out``/``dout`` ``[B, Lq, Hq, d_v]`` are the forward output and its
+    gradient (same strides); ``state`` is ``(m, l)`` or ``(m, l, O)`` from the
+    forward after all chunks.  ``dq`` ``[B, Lq, Hq, d_qk]`` and the per-chunk
+    ``(dk, dv)`` are contiguous fp32 tensors, allocated when not given; with
+    ``RA_FLAG_ACCUMULATE`` the call adds into them.
+    """
+    import torch
+
+    B, Lq, Hq, dqk = q.shape
+    same_strides = all(a == b or n == 1 for a, b, n in zip(out.stride(), dout.stride(), out.shape))
+    if tuple(out.shape) != tuple(dout.shape) or not same_strides or out.dtype != dout.dtype:
+        raise RingAttnError(RA_ERR_INVALID_ARG, "out and dout must share shape, strides and dtype")
+    m, l = state[0], state[1]
+    for t in (m, l):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, Lq, Hq):
+            raise RingAttnError(RA_ERR_INVALID_ARG, "m and l must be contiguous fp32 [B, Lq, Hq]")
+    d, arr = make_desc(q, chunks, scale, out, window)
+    if dq is None:
+        dq = torch.empty((B, Lq, Hq, dqk), device=q.device, dtype=torch.float32)
+    if grads is None:
+        grads = [(torch.empty(c[0].shape, device=q.device, dtype=torch.float32),
+                  torch.empty(c[1].shape, device=q.device, dtype=torch.float32)) for c in chunks]
+    if len(grads) != len(chunks):
+        raise RingAttnError(RA_ERR_INVALID_ARG, "one (dk, dv) pair per chunk")
+    for t in [dq] + [g for pair in grads for g in pair]:
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise RingAttnError(RA_ERR_INVALID_ARG, "dq, dk and dv must be contiguous fp32")
+    garr = (ra_kv_grad * max(len(chunks), 1))()
+    for i, (gk, gv) in enumerate(grads):
+        if tuple(gk.shape) != tuple(chunks[i][0].shape) or tuple(gv.shape) != tuple(chunks[i][1].shape):
+            raise RingAttnError(RA_ERR_INVALID_ARG, f"grads[{i}] must match the chunk's k and v shapes")
+        garr[i].dk = gk.data_ptr()
+        garr[i].dv = gv.data_ptr()
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.ring_attn_bwd_workspace_size(ctypes.byref(d), Lq, ctypes.byref(n)))
+    ws_bytes = int(n.value)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if ctx is None:
+        ctx = default_context(dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(lib.ring_attn_bwd(ctx.handle, ctypes.byref(d), q.data_ptr(), Lq, arr, len(chunks),
+                             int(bool(causal)), int(q_offset), int(flags), out.data_ptr(), dout.data_ptr(),
+                             m.data_ptr(), l.data_ptr(), dq.data_ptr(), garr,
+                             workspace.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream))
+    return dq, grads

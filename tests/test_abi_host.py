@@ -248,3 +248,44 @@ def test_fp8_kv_validation(lib):
     assert _ws(lib, st, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == rb.RA_ERR_INVALID_ARG
     st.k_strides[:] = (64 * 2 * 144, 2 * 144, 144)
     assert _ws(lib, st, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == 0
+
+
+def test_bwd_workspace_and_validation(lib):
+    """Backward: workspace = the rows' (lse, D) pairs; what is not built is
+    rejected; bad arguments are rejected before anything touches the device
+    (a dummy context is safe because validation comes first)."""
+    n = ctypes.c_size_t()
+    assert lib.ring_attn_bwd_workspace_size(ctypes.byref(_desc(B=2, Hq=4, d=128)), 100, ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * 100 * 8  # 6400, already a multiple of 256
+    assert lib.ring_attn_bwd_workspace_size(ctypes.byref(_desc(B=1, Hq=3, Hkv=3, d=64)), 5, ctypes.byref(n)) == 0
+    assert n.value == 256
+    for bad in (_desc(dtype=ra.RA_F32), _desc(d=512)):
+        assert lib.ring_attn_bwd_workspace_size(ctypes.byref(bad), 8, ctypes.byref(n)) == rb.RA_ERR_UNSUPPORTED
+    f8 = _desc()
+    f8.kv_dtype = rb.RA_FP8_E4M3
+    assert lib.ring_attn_bwd_workspace_size(ctypes.byref(f8), 8, ctypes.byref(n)) == rb.RA_ERR_UNSUPPORTED
+
+    ctx = ctypes.create_string_buffer(256)  # never dereferenced on these paths
+    d, arr = _desc(B=1, Hq=4, Hkv=2, d=128), _chunks([64, 64])
+    grads = (rb.ra_kv_grad * 2)()
+    for i in range(2):
+        grads[i].dk = grads[i].dv = 1 << 16
+    buf = 1 << 20  # 16-byte aligned stand-in device addresses
+
+    def bwd(flags=0, P=2, g=grads, dq=buf, ws=buf, ws_bytes=1 << 20, c=ctx):
+        return lib.ring_attn_bwd(c, ctypes.byref(d), buf, 64, arr, P, 1, 64, flags, buf, buf, buf, buf, dq, g,
+                                 ws, ws_bytes, None)
+
+    assert bwd(c=None) == rb.RA_ERR_INVALID_ARG
+    assert bwd(flags=ra.RA_FLAG_STAGE) == rb.RA_ERR_INVALID_ARG
+    assert bwd(flags=ra.RA_FLAG_SPLIT_KV) == rb.RA_ERR_INVALID_ARG
+    assert bwd(P=65) == rb.RA_ERR_INVALID_ARG
+    assert bwd(g=None) == rb.RA_ERR_INVALID_ARG
+    assert bwd(dq=None) == rb.RA_ERR_INVALID_ARG
+    assert bwd(dq=buf + 4) == rb.RA_ERR_INVALID_ARG
+    assert bwd(ws=None) == rb.RA_ERR_WORKSPACE
+    assert bwd(ws_bytes=100) == rb.RA_ERR_WORKSPACE
+    assert bwd(ws=buf + 16) == rb.RA_ERR_WORKSPACE
+    grads[1].dv = None
+    assert bwd() == rb.RA_ERR_INVALID_ARG
+    assert ctypes.sizeof(rb.ra_kv_grad) == 16
