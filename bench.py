@@ -50,7 +50,7 @@ MEASURED_TRAFFIC = {
 }
 
 HEADLINE = "prefill_bf16_h32_d128"
-SECONDARY = "decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8"
+SECONDARY = "decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,bwd:prefill_bf16_h32_d128"
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -199,6 +199,46 @@ class WorkloadRun:
                     launches_per_step=self.launches, roofline=roof)
 
 
+class BackwardRun(WorkloadRun):
+    """The gradients (dQ, dK, dV) of a prefill workload's ring share: one
+    ring_attn_bwd call over all chunks in ring order (in place), with the
+    forward's output, state and a seeded output gradient resident."""
+
+    def __init__(self, name, device="cuda:0"):
+        super().__init__(name, device)
+        torch, ra, wl = self.torch, self.ra, self.wl
+        from long_context_blockwise_amd import inputs
+
+        self.out, self.state = ra.ring_attn_fwd(self.x.q, self.chunks, wl.causal, wl.q_offset,
+                                                flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True, ctx=self.ctx)
+        self.dout = inputs.output_grad(wl, device)
+        self.dq = torch.empty((wl.B, wl.Lq, wl.Hq, wl.d_qk), device=device, dtype=torch.float32)
+        self.grads = [(torch.empty(c[0].shape, device=device, dtype=torch.float32),
+                       torch.empty(c[1].shape, device=device, dtype=torch.float32)) for c in self.chunks]
+        self.bws = torch.empty(max(ra.ring_attn_bwd_workspace_size(self.x.q, self.chunks), 1), device=device,
+                               dtype=torch.uint8)
+        pairs = visible_pairs_fast(wl) * wl.B * wl.Hq
+        # S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q per visible pair
+        self.flops = pairs * 2 * (3 * wl.d_qk + 2 * wl.d_v)
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.ra.ring_attn_bwd(self.x.q, self.chunks, self.out, self.dout, self.state, self.wl.causal,
+                              self.wl.q_offset, dq=self.dq, grads=self.grads, ctx=self.ctx, workspace=self.bws)
+
+    def result(self, sec_per_step, ev_ms):
+        wl = self.wl
+        tflops = self.flops / sec_per_step / 1e12
+        achieved = self.flops / (ev_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    kernels="bwd_pre + bwd_dq + bwd_dkdv per step")
+        return dict(workload="bwd:" + wl.name, metric="causal attn bwd TFLOP/s (dQ, dK, dV) per GPU",
+                    value=round(tflops, 2), unit="TFLOP/s", ms_per_step=round(sec_per_step * 1e3, 4),
+                    tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1), tflops=round(tflops, 2),
+                    launches_per_step=2 + len(self.chunks), roofline=roof)
+
+
 def cpu_baseline(name, budget_s=20.0):
     """Time the CPU oracle on a bounded, stratified row sample of a workload
     (all heads and batches of the sampled rows) and scale to TFLOP/s."""
@@ -270,7 +310,7 @@ def main():
 
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = WorkloadRun(name)
+        r = BackwardRun(name[4:]) if name.startswith("bwd:") else WorkloadRun(name)
         s2, e2 = r.time(max(3, args.steps // 2), max(1, args.warmup))
         res = r.result(s2, e2)
         print(f"[bench] {res}", file=sys.stderr, flush=True)

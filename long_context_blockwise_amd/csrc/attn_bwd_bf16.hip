@@ -196,21 +196,29 @@ void bwd_dq_kernel(const BwdArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: keys resident (32 per wave), query-row tiles of 32 streamed
+// dK, dV: keys resident (32 per wave), query-row tiles of 32 * RB streamed
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
+#ifndef RA_TUNE_KV_RB
+#define RA_TUNE_KV_RB 2
+#endif
 
-// Stage u holds the Q tile (rows t0 .. t0+31, row-major, swizzled), then each
-// wave's copy of the rows' (lse2, D) pairs (256 bytes per wave), then the dO
-// tile; RA_STAGE_ARRAYS(NS, TILE + 1024) gives 2 * TILE + 2048 bytes a stage.
-template <int D, int NS>
+// A tile is RB blocks of 32 query rows.  Stage u holds the Q tile (row-major,
+// swizzled), then each wave's copy of the rows' (lse2, D) pairs (256 bytes
+// per 32 rows per wave), then the dO tile: RA_STAGE_ARRAYS(NS, TILE + 1024 RB)
+// gives 2 TILE + 2048 RB bytes a stage.  The RB row blocks are independent
+// chains of matrix-core work, which lets one wave overlap the softmax of one
+// block with the products of another.
+template <int D, int RB, int NS>
 __global__ __launch_bounds__(kKvWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const BwdArgs A) {
     const FwdArgs &a = A.f;
-    using C = Cfg<D, 32, kKvWaves, 1>;  // 32-row tiles: TILE bytes each for Q and dO
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE + 1;
-    RA_STAGE_ARRAYS(NS, C::TILE + 1024)
+    constexpr int RT = 32 * RB;              // query rows per tile
+    using C = Cfg<D, RT, kKvWaves, 1>;       // RT-row tiles: TILE bytes each for Q and dO; KB = RB
+    constexpr int LDW = 256 * RB;            // bytes of (lse2, D) pairs per wave
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + RB;
+    RA_STAGE_ARRAYS(NS, C::TILE + 1024 * RB)
     auto qtile = [&](auto u) { return kst(u); };
     auto ldtile = [&](auto u) { return kst(u) + C::TILE; };
     auto gtile = [&](auto u) { return vst(u); };
@@ -265,8 +273,8 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             t_lo = lo > t_lo ? lo : t_lo;
         }
     }
-    t_lo &= ~(int64_t)31;
-    const int nrt = t_hi >= t_lo ? (int)((t_hi - t_lo) / 32 + 1) : 0;
+    t_lo = t_lo / RT * RT;
+    const int nrt = t_hi >= t_lo ? (int)((t_hi - t_lo) / RT + 1) : 0;
     const int ntiles = nrt * a.G;
 
     int kaddr[C::NKA];
@@ -279,7 +287,7 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     auto tile_of = [&](int it, int &h, int64_t &t0) {
         const int gq = it / nrt;
         h = hk * a.G + gq;
-        t0 = t_lo + 32 * (int64_t)(it % nrt);
+        t0 = t_lo + RT * (int64_t)(it % nrt);
     };
     auto issue = [&](auto u, int it) {
         int h;
@@ -289,12 +297,14 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         const uint16_t *gb = (const uint16_t *)A.dout + b * a.o_sb + h * a.o_sh;
         load_tile<C>(qb, a.q_ss, t0, a.Lq, qtile(u), w, lane);
         load_tile<C>(gb, a.o_ss, t0, a.Lq, gtile(u), w, lane);
-        // (lse2, D) of rows t0 .. t0+31: one dword per lane into the wave's own copy
-        const int64_t nrows = a.Lq - t0 < 32 ? a.Lq - t0 : 32;
+        // (lse2, D) of rows t0 .. t0+RT-1: one dword per lane per 32 rows into the wave's own copy
+        const int64_t nrows = a.Lq - t0 < RT ? a.Lq - t0 : RT;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(A.ld + (((int64_t)b * a.Hq + h) * a.Lq + t0) * 2), (short)0, (int)(nrows * 8), kBufferFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(ldtile(u) + 256 * w), 4, (unsigned)lane * 4u, 0, 0,
-                                                 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(ldtile(u) + LDW * w + 256 * rb), 4,
+                                                     (unsigned)(256 * rb + lane * 4), 0, 0, 0);
     };
     auto wait_for = [&](int need, int last) {
         const int after = last - need;
@@ -310,24 +320,28 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         int h;
         int64_t t0;
         tile_of(it, h, t0);
-        const int64_t thi = t0 + 31 < a.Lq - 1 ? t0 + 31 : a.Lq - 1;
+        const int64_t thi = t0 + RT - 1 < a.Lq - 1 ? t0 + RT - 1 : a.Lq - 1;
         const bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
-        const bool full = t0 + 31 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
+        const bool full = t0 + RT - 1 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
         if (!skip) {
-            const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + 256 * w;
-            // S = Q K^T and dP = dO V^T: rows on M, this wave's keys on N
-            f32x16 s, dp;
+            const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + LDW * w;
+            // S = Q K^T and dP = dO V^T per 32-row block: rows on M, this wave's keys on N
+            f32x16 s[RB], dp[RB];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int ds = 0; ds < C::DS; ++ds) {
-                s = mfma(kfrag<C>(qt, kaddr, ds, 0), kf[ds], s);
-                dp = mfma(kfrag<C>(gt, kaddr, ds, 0), vf[ds], dp);
-            }
-            // element i is row t0 + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
+                for (int i = 0; i < 16; ++i) s[rb][i] = dp[rb][i] = 0.f;
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    s[rb] = mfma(kfrag<C>(qt, kaddr, ds, rb), kf[ds], s[rb]);
+                    dp[rb] = mfma(kfrag<C>(gt, kaddr, ds, rb), vf[ds], dp[rb]);
+                }
+            // element i of block rb is row t0 + 32rb + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
             if (!full) {
                 const int64_t big = 1 << 30;
-                const int64_t base = a.q_offset + t0 + 4 * g - kpos;  // qpos - kpos at ro = 0
+                const int64_t base = a.q_offset + t0 + 4 * g - kpos;  // qpos - kpos at rb = 0, ro = 0
                 int64_t lo = -big, hi = a.Lq - t0 - 4 * g;
                 if (a.causal) lo = -base;
                 if (a.window > 0) {
@@ -339,39 +353,45 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                 hi = hi < -big ? -big : (hi > big ? big : hi);
                 const int lo32 = (int)lo, hi32 = (int)hi;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int ro = 8 * (i >> 2) + (i & 3);
-                    if (ro < lo32 || ro >= hi32) s[i] = kNegInf;
-                }
-            }
-            // P and dS of the 16 rows, packed as B operands (k-steps of 16 rows)
-            bf16x8 pp[2], pd[2];
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                u32x4 a4, b4;
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    // rows 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
-                    const f32x4 x = *(const f32x4 *)(lt + 8 * (16 * hh + 8 * jj + 4 * g));
-                    const f32x4 y = *(const f32x4 *)(lt + 8 * (16 * hh + 8 * jj + 4 * g) + 16);
-                    const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
-#pragma unroll
-                    for (int r2 = 0; r2 < 2; ++r2) {
-                        const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
-                        const float p0 = exp2_fast(__builtin_fmaf(s[i0], c2, -l4[2 * r2]));
-                        const float p1 = exp2_fast(__builtin_fmaf(s[i1], c2, -l4[2 * r2 + 1]));
-                        a4[2 * jj + r2] = pack_bf16(p0, p1);
-                        b4[2 * jj + r2] = pack_bf16(p0 * (dp[i0] - d4[2 * r2]), p1 * (dp[i1] - d4[2 * r2 + 1]));
+                    for (int i = 0; i < 16; ++i) {
+                        const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+                        if (ro < lo32 || ro >= hi32) s[rb][i] = kNegInf;
                     }
-                }
-                pp[hh] = to_bf16x8(a4);
-                pd[hh] = to_bf16x8(b4);
             }
+            // P and dS, packed as B operands: k-step ks covers rows 16ks .. 16ks+15
+            bf16x8 pp[2 * RB], pd[2 * RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    u32x4 a4, b4;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        // rows 32rb + 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
+                        const char *lp = lt + 8 * (32 * rb + 16 * hh + 8 * jj + 4 * g);
+                        const f32x4 x = *(const f32x4 *)lp;
+                        const f32x4 y = *(const f32x4 *)(lp + 16);
+                        const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
+#pragma unroll
+                        for (int r2 = 0; r2 < 2; ++r2) {
+                            const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
+                            const float p0 = exp2_fast(__builtin_fmaf(s[rb][i0], c2, -l4[2 * r2]));
+                            const float p1 = exp2_fast(__builtin_fmaf(s[rb][i1], c2, -l4[2 * r2 + 1]));
+                            a4[2 * jj + r2] = pack_bf16(p0, p1);
+                            b4[2 * jj + r2] =
+                                pack_bf16(p0 * (dp[rb][i0] - d4[2 * r2]), p1 * (dp[rb][i1] - d4[2 * r2 + 1]));
+                        }
+                    }
+                    pp[2 * rb + hh] = to_bf16x8(a4);
+                    pd[2 * rb + hh] = to_bf16x8(b4);
+                }
             // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+            for (int ks = 0; ks < 2 * RB; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
+                for (int db = 0; db < C::DB; ++db) {
                     dv[db] = mfma(vfrag<C>(gt, vaddr, ks, db), pp[ks], dv[db]);
                     dk[db] = mfma(vfrag<C>(qt, vaddr, ks, db), pd[ks], dk[db]);
                 }
@@ -438,9 +458,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s) {
     const unsigned grid = (unsigned)(nkt * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;
     if (d == 128)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -612,9 +612,9 @@ static int check_bwd(const ra_desc *d, int64_t Lq, Strides *st) {
     if (d->dtype != RA_BF16 || (d->d_qk != 64 && d->d_qk != 128))
         return fail(RA_ERR_UNSUPPORTED, "the backward is built for bf16 with d_qk = d_v in {64, 128}");
     if (kv_fp8(d)) return fail(RA_ERR_UNSUPPORTED, "the backward takes bf16 keys and values");
-    for (int i = 0; i < 3; ++i)
-        if (st->q[i] >= ((int64_t)1 << 24) || st->o[i] >= ((int64_t)1 << 24))
-            return fail(RA_ERR_UNSUPPORTED, "q/out strides must be below 2^24 elements");
+    // 32-row tiles of q and dout are addressed with 32-bit offsets from a 64-bit base
+    if (st->q[1] >= ((int64_t)1 << 24) || st->o[1] >= ((int64_t)1 << 24))
+        return fail(RA_ERR_UNSUPPORTED, "q/out token strides must be below 2^24 elements");
     return RA_OK;
 }
 

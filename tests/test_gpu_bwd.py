@@ -166,3 +166,25 @@ def test_bwd_empty_and_skipped_chunks():
     _, g0 = ra.ring_attn_bwd(q0, chunks, q0, q0, (m0, m0), True, 100)
     torch.cuda.synchronize()
     assert all(float(t.abs().max()) == 0.0 for pair in g0 for t in pair)
+
+
+def test_bwd_full_size_head_slice():
+    """The bench's backward at full size (32 heads, d = 128, 4 x 8192 chunks,
+    query chunk 3, causal, chunks in ring order): every dQ, dK, dV element of
+    one head against the oracle run on that head alone."""
+    wl = inputs.WORKLOADS["prefill_bf16_h32_d128"]
+    x = inputs.make(wl, DEV)
+    order = ra.ring_attn_ring_order(wl.q_offset // wl.chunk_len, wl.P)
+    chunks = x.chunks(order)
+    out, st = ra.ring_attn_fwd(x.q, chunks, True, wl.q_offset, flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True)
+    dout = inputs.output_grad(wl, DEV)
+    dq, grads = ra.ring_attn_bwd(x.q, chunks, out, dout, st, True, wl.q_offset)
+    torch.cuda.synchronize()
+    h = 13
+    qh = x.q[:, :, h:h + 1].cpu().contiguous()
+    ch = [(k[:, :, h:h + 1].cpu().contiguous(), v[:, :, h:h + 1].cpu().contiguous(), s) for (k, v, s) in chunks]
+    dq_ref, dks, dvs = oracle.attention_bwd(qh, ch, dout[:, :, h:h + 1].cpu().contiguous(), wl.q_offset, True)
+    check_grad(dq[:, :, h:h + 1], dq_ref, f"full-size dQ head {h}")
+    for c in range(len(chunks)):
+        check_grad(grads[c][0][:, :, h:h + 1], dks[c], f"full-size dK[{c}] head {h}")
+        check_grad(grads[c][1][:, :, h:h + 1], dvs[c], f"full-size dV[{c}] head {h}")
