@@ -69,10 +69,10 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_threads.restype = i32
     lib.oracle_attention.restype = i32
     lib.oracle_attention.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64,
-                                     i32, vp, vp, vp, vp, i32, i64, dbl, i64, vp, vp, vp]
+                                     i32, vp, vp, vp, vp, vp, dbl, i64, vp, vp, vp]
     lib.oracle_ring_step.restype = i32
     lib.oracle_ring_step.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64,
-                                     vp, vp, i64, i64, i32, i64, dbl, i64, vp, vp, vp, vp]
+                                     vp, vp, i64, i64, vp, dbl, i64, vp, vp, vp, vp]
     lib.oracle_state_init.restype = None
     lib.oracle_state_init.argtypes = [i64, i32, vp, vp, vp]
     lib.oracle_merge.restype = None
@@ -83,7 +83,7 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_dequant_fp8.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp]
     lib.oracle_attention_bwd.restype = i32
     lib.oracle_attention_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp, vp,
-                                         vp, vp, i32, i64, dbl, vp, vp, vp, vp]
+                                         vp, vp, vp, dbl, vp, vp, vp, vp]
     return lib
 
 
@@ -209,6 +209,32 @@ class _Problem:
         self.nr = int(self.rows.shape[0])
 
 
+class _Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int), ("window", ctypes.c_int64), ("anchor", ctypes.c_int64),
+                ("q_seg", ctypes.c_void_p), ("k_seg", ctypes.c_void_p)]
+
+
+def _mask(p, causal, window, anchor, q_seg, k_segs):
+    """The C mask of a call, plus the arrays it points into (kept alive by the caller)."""
+    m = _Mask(int(bool(causal)), int(window), int(anchor), None, None)
+    keep = []
+    if (q_seg is None) != (k_segs is None):
+        raise ValueError("q_seg and k_segs go together")
+    if q_seg is not None:
+        qs = np.ascontiguousarray(np.asarray(q_seg.cpu() if hasattr(q_seg, "cpu") else q_seg, dtype=np.int32))
+        if qs.shape != (p.B, p.Lq) or len(k_segs) != len(p.ks):
+            raise ValueError("q_seg must be [B, Lq] and k_segs one [B, len] array per chunk")
+        ks = [np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int32))
+              for x in k_segs]
+        for a, n in zip(ks, p.lens):
+            if a.shape != (p.B, n):
+                raise ValueError("each k_segs entry must be [B, len]")
+        arr = (ctypes.c_void_p * max(len(ks), 1))(*[_ptr(a) for a in ks])
+        m.q_seg, m.k_seg = _ptr(qs), ctypes.cast(arr, ctypes.c_void_p).value
+        keep = [qs, ks, arr]
+    return m, keep
+
+
 def _scale(scale, dqk):
     return 1.0 / math.sqrt(dqk) if scale is None else float(scale)
 
@@ -217,14 +243,17 @@ def _scale(scale, dqk):
 # entry points
 # --------------------------------------------------------------------------- #
 def attention(q, chunks, q_offset=0, causal=False, scale=None, rows=None,
-              dtype=None, Hkv=None, dv=None, window=0):
+              dtype=None, Hkv=None, dv=None, window=0, anchor=0, q_seg=None, k_segs=None):
     """Plain attention of the query rows ``rows`` against all keys of ``chunks``.
 
     ``chunks`` is a list of ``(k, v, start)``: k ``[B, len, Hkv, d_qk]``, v
     ``[B, len, Hkv, d_v]`` holding the keys at absolute positions
     ``start .. start+len-1``.  Query row r sits at position ``q_offset + r``.
     ``window > 0`` limits a query at p to keys at distance <= window (keys
-    p - window .. p when causal).  Returns ``(out [B, n_rows, Hq, d_v], lse
+    p - window .. p when causal).  ``anchor = S > 0`` also shows it the keys
+    at a - 1, a and a + S, a = S * (p // S).  ``q_seg [B, Lq]`` with
+    ``k_segs`` (one ``[B, len]`` per chunk) are segment labels: a query sees
+    only keys with its label.  Returns ``(out [B, n_rows, Hq, d_v], lse
     [B, Hq, n_rows])`` in float64; a row that sees no key gets out = 0 and
     lse = -inf.
     """
@@ -241,16 +270,18 @@ def attention(q, chunks, q_offset=0, causal=False, scale=None, rows=None,
     vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(a) for a in p.vs])
     st = np.asarray(p.starts if n else [0], dtype=np.int64)
     ln = np.asarray(p.lens if n else [0], dtype=np.int64)
+    mk, _keep = _mask(p, causal, window, anchor, q_seg, k_segs)
     rc = lib.oracle_attention(p.B, p.Hq, Hkv, p.dqk, dv, p.code, _ptr(p.q), p.Lq,
                               int(q_offset), n, kp, vp, _ptr(st), _ptr(ln),
-                              int(bool(causal)), int(window), _scale(scale, p.dqk), p.nr,
+                              ctypes.byref(mk), _scale(scale, p.dqk), p.nr,
                               _ptr(p.rows), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attention failed ({rc})")
     return out, lse
 
 
-def attention_bwd(q, chunks, dout, q_offset=0, causal=False, scale=None, dtype=None, window=0):
+def attention_bwd(q, chunks, dout, q_offset=0, causal=False, scale=None, dtype=None, window=0, anchor=0,
+                  q_seg=None, k_segs=None):
     """Gradients of ``sum(dout * attention(q, chunks, ...))``: returns
     ``(dq [B, Lq, Hq, d_qk], [dk_c [B, len_c, Hkv, d_qk]], [dv_c [B, len_c, Hkv, d_v]])``
     in float64.  ``dout [B, Lq, Hq, d_v]`` has q's element type; masking
@@ -272,9 +303,10 @@ def attention_bwd(q, chunks, dout, q_offset=0, causal=False, scale=None, dtype=N
     dvp = (ctypes.c_void_p * n)(*[_ptr(a) for a in dvs])
     st = np.asarray(p.starts, dtype=np.int64)
     ln = np.asarray(p.lens, dtype=np.int64)
+    mk, _keep = _mask(p, causal, window, anchor, q_seg, k_segs)
     rc = lib.oracle_attention_bwd(p.B, p.Hq, p.Hkv, p.dqk, p.dv, p.code, _ptr(p.q), p.Lq,
-                                  int(q_offset), n, kp, vp, _ptr(st), _ptr(ln), int(bool(causal)),
-                                  int(window), _scale(scale, p.dqk), _ptr(do), _ptr(dq), dkp, dvp)
+                                  int(q_offset), n, kp, vp, _ptr(st), _ptr(ln), ctypes.byref(mk),
+                                  _scale(scale, p.dqk), _ptr(do), _ptr(dq), dkp, dvp)
     if rc != 0:
         raise ValueError(f"oracle_attention_bwd failed ({rc})")
     return dq, dks, dvs
@@ -298,15 +330,16 @@ class State:
 
 
 def ring_step(state: State, q, chunk, q_offset=0, causal=False, scale=None,
-              rows=None, dtype=None, window=0) -> State:
+              rows=None, dtype=None, window=0, anchor=0, q_seg=None, k_seg=None) -> State:
     """Fold one KV chunk ``(k, v, start)`` into ``state`` in place."""
     lib = _get_lib()
     p = _Problem(q, [chunk], dtype, rows)
     if state.O.shape != (p.B, p.Hq, p.nr, p.dv):
         raise ValueError("state shape does not match the problem")
+    mk, _keep = _mask(p, causal, window, anchor, q_seg, None if k_seg is None else [k_seg])
     rc = lib.oracle_ring_step(p.B, p.Hq, p.Hkv, p.dqk, p.dv, p.code, _ptr(p.q),
                               p.Lq, int(q_offset), _ptr(p.ks[0]), _ptr(p.vs[0]),
-                              p.starts[0], p.lens[0], int(bool(causal)), int(window),
+                              p.starts[0], p.lens[0], ctypes.byref(mk),
                               _scale(scale, p.dqk), p.nr, _ptr(p.rows),
                               _ptr(state.m), _ptr(state.l), _ptr(state.O))
     if rc != 0:
@@ -315,7 +348,7 @@ def ring_step(state: State, q, chunk, q_offset=0, causal=False, scale=None,
 
 
 def ring(q, chunks, order=None, q_offset=0, causal=False, scale=None, rows=None,
-         dtype=None, window=0) -> State:
+         dtype=None, window=0, anchor=0, q_seg=None, k_segs=None) -> State:
     """One device's share of the ring: fold the chunks in ``order`` (default:
     list order) into a fresh state and return it."""
     qa, _ = _to_numpy(q, dtype)
@@ -324,7 +357,8 @@ def ring(q, chunks, order=None, q_offset=0, causal=False, scale=None, rows=None,
     dv = int(chunks[0][1].shape[3])
     st = State(B, Hq, nr, dv)
     for c in (range(len(chunks)) if order is None else order):
-        ring_step(st, q, chunks[c], q_offset, causal, scale, rows, dtype, window)
+        ring_step(st, q, chunks[c], q_offset, causal, scale, rows, dtype, window, anchor, q_seg,
+                  None if k_segs is None else k_segs[c])
     return st
 
 

@@ -43,7 +43,17 @@
  * 百万 Token 上下文的秘密", §4.3 稀疏注意力掩码 (query i sees keys
  * i - w .. i); page "billion-token context window engineering" describes
  * the sliding window as keys within a range before and after the query,
- * the reading taken without causal masking.  The query row r
+ * the reading taken without causal masking.
+ *
+ * Anchor tokens (stride S > 0): the same section's sparse mask also lets a
+ * query at p see the keys at a - 1, a and a + S, a = S * floor(p / S), when
+ * they exist, whatever the window and the causal rule say (its mask adds
+ * them to the local window, the later one included).  Segments: with
+ * per-token segment labels (the segment_ids that page "RingAttention推理
+ * 优化：cache_idx参数使用..." passes for packed sequences), a query sees only
+ * keys of its own label; the label test applies on top of everything else.
+ *
+ * The query row r
  * sits at absolute position q_offset + r (q_offset = chunk index * chunk
  * length in a prefill ring, or cache_idx in incremental decoding:
  *   page "RingAttention推理优化：cache_idx参数使用与千万级上下文高效推理实践",
@@ -157,8 +167,31 @@ static double score(const void *q, const void *kc, int dtype, int64_t Lq,
     return dot * scale;
 }
 
-static int visible(int causal, int64_t window, int64_t qpos, int64_t kpos)
+/* The masks of one call.  q_seg [B][Lq] and k_seg[c] [B][len[c]] are
+ * segment labels, or NULL for none. */
+typedef struct oracle_mask {
+    int causal;
+    int64_t window;
+    int64_t anchor;
+    const int32_t *q_seg;
+    const int32_t *const *k_seg;
+} oracle_mask;
+
+/* May query row r (batch b, position qpos) see key j of chunk c (position
+ * kpos, chunk length lenc)? */
+static int visible(const oracle_mask *mk, int64_t Lq, int64_t lenc, int b,
+                   int64_t r, int c, int64_t j, int64_t qpos, int64_t kpos)
 {
+    int causal = mk->causal;
+    int64_t window = mk->window;
+    if (mk->q_seg &&
+        mk->q_seg[(int64_t)b * Lq + r] != mk->k_seg[c][(int64_t)b * lenc + j])
+        return 0;
+    if (mk->anchor > 0) {
+        int64_t a = qpos / mk->anchor * mk->anchor;
+        if (kpos == a - 1 || kpos == a || kpos == a + mk->anchor)
+            return 1;
+    }
     if (causal && kpos > qpos)
         return 0;
     if (window > 0 && (kpos < qpos - window || kpos > qpos + window))
@@ -169,8 +202,8 @@ static int visible(int causal, int64_t window, int64_t qpos, int64_t kpos)
 int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
                      const void *q, int64_t Lq, int64_t q_offset, int n_chunks,
                      const void *const *k, const void *const *v,
-                     const int64_t *start, const int64_t *len, int causal,
-                     int64_t window, double scale, int64_t n_rows,
+                     const int64_t *start, const int64_t *len,
+                     const oracle_mask *mk, double scale, int64_t n_rows,
                      const int64_t *rows, double *out, double *lse)
 {
     if (check_shapes(B, Hq, Hkv, dqk, dv, dtype, Lq, n_chunks, len, n_rows,
@@ -206,7 +239,7 @@ int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             int64_t t = 0;
             for (int c = 0; c < n_chunks; ++c)
                 for (int64_t j = 0; j < len[c]; ++j, ++t) {
-                    if (!visible(causal, window, qpos, start[c] + j)) {
+                    if (!visible(mk, Lq, len[c], b, r, c, j, qpos, start[c] + j)) {
                         s[t] = -INFINITY;
                         continue;
                     }
@@ -252,7 +285,7 @@ int oracle_attention(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
 int oracle_ring_step(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
                      const void *q, int64_t Lq, int64_t q_offset,
                      const void *kc, const void *vc, int64_t start,
-                     int64_t len, int causal, int64_t window, double scale,
+                     int64_t len, const oracle_mask *mk, double scale,
                      int64_t n_rows, const int64_t *rows, double *m,
                      double *l, double *O)
 {
@@ -283,7 +316,7 @@ int oracle_ring_step(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             /* largest score of this chunk's visible keys */
             double cmax = -INFINITY;
             for (int64_t j = 0; j < len; ++j) {
-                if (!visible(causal, window, qpos, start + j)) {
+                if (!visible(mk, Lq, len, b, r, 0, j, qpos, start + j)) {
                     s[j] = -INFINITY;
                     continue;
                 }
@@ -409,7 +442,7 @@ int oracle_attention_bwd(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
                          const void *q, int64_t Lq, int64_t q_offset,
                          int n_chunks, const void *const *k,
                          const void *const *v, const int64_t *start,
-                         const int64_t *len, int causal, int64_t window,
+                         const int64_t *len, const oracle_mask *mk,
                          double scale, const void *dout, double *dq,
                          double *const *dk, double *const *dvv)
 {
@@ -458,7 +491,7 @@ int oracle_attention_bwd(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             int64_t t = 0;
             for (int c = 0; c < n_chunks; ++c)
                 for (int64_t j = 0; j < len[c]; ++j, ++t) {
-                    if (!visible(causal, window, qpos, start[c] + j)) {
+                    if (!visible(mk, Lq, len[c], b, r, c, j, qpos, start[c] + j)) {
                         s[t] = -INFINITY;
                         continue;
                     }
@@ -538,7 +571,7 @@ int oracle_attention_bwd(int B, int Hq, int Hkv, int dqk, int dv, int dtype,
             gv[e] = 0.0;
         for (int h = hk * G; h < (hk + 1) * G; ++h)
             for (int64_t r = 0; r < Lq; ++r) {
-                if (!visible(causal, window, q_offset + r, start[c] + j))
+                if (!visible(mk, Lq, len[c], b, r, c, j, q_offset + r, start[c] + j))
                     continue;
                 int64_t row = ((int64_t)b * Hq + h) * Lq + r;
                 if (lse[row] == -INFINITY)

@@ -663,6 +663,138 @@ def pin_bwd_chunking_invariance():
     _close(np.concatenate([dv1[1], dv1[2], dv1[0]], 1), dv0[0], 1e-13, "chunked dV")
 
 
+# --------------------------------------------------------------------------- #
+# anchor tokens and segments
+# --------------------------------------------------------------------------- #
+def _page_sparse_mask(n, w, S):
+    """The sparse mask of page "Ring Attention：百万 Token 上下文的秘密", §4.3,
+    over a whole sequence of n positions: query i sees the keys
+    max(0, i - w) .. i, and the anchors A, A - 1 (if A > 0) and A + S (if it
+    is a position), A being the start of i's stride-S block."""
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        m[i, max(0, i - w):i + 1] = True
+        A = (i // S) * S
+        m[i, A] = True
+        if A > 0:
+            m[i, A - 1] = True
+        if A + S < n:
+            m[i, A + S] = True
+    return m
+
+
+def _sdpa_masked(q, chunks, mask, d):
+    K = torch.from_numpy(np.concatenate([c[0] for c in chunks], axis=1)).permute(0, 2, 1, 3)
+    V = torch.from_numpy(np.concatenate([c[1] for c in chunks], axis=1)).permute(0, 2, 1, 3)
+    Q = torch.from_numpy(q).permute(0, 2, 1, 3)
+    return torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, attn_mask=torch.from_numpy(mask), scale=1.0 / math.sqrt(d), enable_gqa=True).permute(0, 2, 1, 3).numpy()
+
+
+def pin_anchor_library_sdpa():
+    """Causal window plus anchor tokens against library SDPA under the
+    page's sparse mask built over the whole sequence (the query chunk is a
+    slice of it; ragged chunks, GQA, strides 3, 4, 8)."""
+    rng = np.random.default_rng(808)
+    for (B, Hq, Hkv, d, lens, q_off, Lq, w, S) in ((1, 2, 1, 6, [9, 7, 8], 10, 14, 2, 4),
+                                                  (2, 4, 2, 5, [16, 16], 16, 16, 5, 8),
+                                                  (1, 3, 3, 4, [5, 11, 4], 0, 20, 1, 3),
+                                                  (1, 2, 2, 8, [24], 3, 17, 0, 8)):
+        q, chunks = _rand(rng, B, Lq, Hq, Hkv, d, d, lens)
+        n = sum(lens)
+        page = _page_sparse_mask(n, w if w > 0 else n, S)
+        rows = page[q_off:q_off + Lq]
+        out, _ = oracle.attention(q, chunks, q_off, True, window=w, anchor=S)
+        _close(out, _sdpa_masked(q, chunks, rows, d), 1e-12, f"anchors S={S} w={w} lens={lens}")
+
+
+def pin_anchor_ring_and_two_sided():
+    """With anchors the ring recurrence in any order still equals full
+    attention; without causal masking anchors join a two-sided window (SDPA
+    with the explicit mask); a window covering everything leaves anchors
+    nothing to add."""
+    rng = np.random.default_rng(909)
+    q, chunks = _rand(rng, 1, 12, 2, 1, 6, 6, [10, 9, 13])
+    full, _ = oracle.attention(q, chunks, 8, True, window=3, anchor=5)
+    for order in ([2, 0, 1], [1, 2, 0]):
+        st = oracle.ring(q, chunks, order=order, q_offset=8, causal=True, window=3, anchor=5)
+        o, _ = oracle.finalize(st)
+        _close(o, full, 1e-12, f"anchor ring order={order}")
+    qpos, kpos = 8 + np.arange(12), _positions(chunks)
+    m = np.abs(kpos[None, :] - qpos[:, None]) <= 2
+    A = (qpos // 5) * 5
+    for extra in (A - 1, A, A + 5):
+        m |= kpos[None, :] == extra[:, None]
+    out, _ = oracle.attention(q, chunks, 8, False, window=2, anchor=5)
+    _close(out, _sdpa_masked(q, chunks, m, 6), 1e-12, "anchors with a two-sided window")
+    a, _ = oracle.attention(q, chunks, 8, False, window=100, anchor=5)
+    b, _ = oracle.attention(q, chunks, 8, False)
+    _close(a, b, 0.0, "window over everything")
+
+
+def pin_segments_packing():
+    """Packed documents: attention over a sequence whose segment labels mark
+    three documents equals each document's own attention computed alone
+    (causal, and with a window); labels against library SDPA with the
+    equality mask, including rows whose label no key carries."""
+    rng = np.random.default_rng(1010)
+    docs = [5, 7, 4]
+    n = sum(docs)
+    q, chunks = _rand(rng, 2, n, 4, 2, 6, 6, [6, 10])  # the chunks cut across documents
+    lab = np.repeat(np.arange(len(docs)), docs).astype(np.int32)
+    q_seg = np.tile(lab, (2, 1))
+    k_segs = [q_seg[:, :6], q_seg[:, 6:]]
+    K = np.concatenate([c[0] for c in chunks], axis=1)
+    V = np.concatenate([c[1] for c in chunks], axis=1)
+    for w in (0, 2):
+        out, _ = oracle.attention(q, chunks, 0, True, window=w, q_seg=q_seg, k_segs=k_segs)
+        s0 = 0
+        for L in docs:
+            alone, _ = oracle.attention(q[:, s0:s0 + L], [(K[:, s0:s0 + L], V[:, s0:s0 + L], 0)], 0, True, window=w)
+            _close(out[:, s0:s0 + L], alone, 1e-13, f"packed document at {s0} w={w}")
+            s0 += L
+    # arbitrary labels, non-causal, one label carried by no key
+    q2, ch2 = _rand(rng, 1, 9, 2, 2, 5, 5, [7, 8])
+    qs = rng.integers(0, 3, size=(1, 9)).astype(np.int32)
+    qs[0, 4] = 7
+    ks = [rng.integers(0, 3, size=(1, 7)).astype(np.int32), rng.integers(0, 3, size=(1, 8)).astype(np.int32)]
+    out, _ = oracle.attention(q2, ch2, 0, False, q_seg=qs, k_segs=ks)
+    m = qs[0][:, None] == np.concatenate(ks, axis=1)[0][None, :]
+    seen = m.any(1)
+    _close(out[:, seen], _sdpa_masked(q2[:, seen], ch2, m[seen], 5), 1e-12, "segment labels")
+    assert np.all(out[:, ~seen] == 0.0)
+
+
+def pin_bwd_with_anchors_and_segments():
+    """Gradients under anchors and segment labels against float64 autograd
+    through library SDPA with the same explicit mask."""
+    rng = np.random.default_rng(1111)
+    q, chunks = _rand(rng, 1, 10, 2, 1, 5, 5, [8, 9])
+    do = rng.standard_normal((1, 10, 2, 5))
+    qs = np.array([[0] * 4 + [1] * 6], dtype=np.int32)
+    ks = [np.array([[0] * 8], dtype=np.int32), np.array([[0] * 3 + [1] * 6], dtype=np.int32)]
+    for kw, m in ((dict(window=2, anchor=4), None), (dict(q_seg=qs, k_segs=ks), None)):
+        qpos, kpos = 7 + np.arange(10), _positions(chunks)
+        if "anchor" in kw:
+            m = (kpos[None, :] <= qpos[:, None]) & (kpos[None, :] >= qpos[:, None] - 2)
+            A = (qpos // 4) * 4
+            for extra in (A - 1, A, A + 4):
+                m |= kpos[None, :] == extra[:, None]
+        else:
+            m = (kpos[None, :] <= qpos[:, None]) & (qs[0][:, None] == np.concatenate(ks, 1)[0][None, :])
+        dq, dks, dvs = oracle.attention_bwd(q, chunks, do, 7, True, **kw)
+        Q = torch.from_numpy(q).requires_grad_()
+        K = torch.from_numpy(np.concatenate([c[0] for c in chunks], axis=1)).requires_grad_()
+        V = torch.from_numpy(np.concatenate([c[1] for c in chunks], axis=1)).requires_grad_()
+        out = torch.nn.functional.scaled_dot_product_attention(
+            Q.permute(0, 2, 1, 3), K.permute(0, 2, 1, 3), V.permute(0, 2, 1, 3), attn_mask=torch.from_numpy(m),
+            scale=1.0 / math.sqrt(5), enable_gqa=True)
+        (out.permute(0, 2, 1, 3) * torch.from_numpy(do)).sum().backward()
+        _close(dq, Q.grad.numpy(), 1e-11, f"bwd {list(kw)} dQ")
+        _close(np.concatenate(dks, 1), K.grad.numpy(), 1e-11, f"bwd {list(kw)} dK")
+        _close(np.concatenate(dvs, 1), V.grad.numpy(), 1e-11, f"bwd {list(kw)} dV")
+
+
 ALL_PINS = [
     pin_library_sdpa,
     pin_zero_query_mean,
@@ -686,4 +818,8 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_invariants_and_closed_forms,
     pin_bwd_chunking_invariance,
+    pin_anchor_library_sdpa,
+    pin_anchor_ring_and_two_sided,
+    pin_segments_packing,
+    pin_bwd_with_anchors_and_segments,
 ]

@@ -57,6 +57,18 @@ MUTANTS = [
     ("fp8_scale_bias", "double scale = ldexp(1.0, e - 127);", "double scale = ldexp(1.0, e - 128);", 1),
     ("fp8_scale_block_of_next_token", "exps[((int64_t)b * H + h) * nblk + t / block]",
      "exps[((int64_t)b * H + h) * nblk + (t + 1) / block]", 1),
+    ("anchor_without_previous_key", "if (kpos == a - 1 || kpos == a || kpos == a + mk->anchor)",
+     "if (kpos == a || kpos == a + mk->anchor)", 1),
+    ("anchor_future_key_off_by_one", "if (kpos == a - 1 || kpos == a || kpos == a + mk->anchor)",
+     "if (kpos == a - 1 || kpos == a || kpos == a + mk->anchor - 1)", 1),
+    ("anchor_block_of_next_token", "int64_t a = qpos / mk->anchor * mk->anchor;",
+     "int64_t a = (qpos + 1) / mk->anchor * mk->anchor;", 1),
+    ("anchors_obey_causal", "if (kpos == a - 1 || kpos == a || kpos == a + mk->anchor)",
+     "if ((kpos == a - 1 || kpos == a || kpos == a + mk->anchor) && kpos <= qpos)", 1),
+    ("anchors_ignored", "if (mk->anchor > 0) {", "if (0) {", 1),
+    ("segments_ignored", "if (mk->q_seg &&\n", "if (0 && mk->q_seg &&\n", 1),
+    ("segment_label_of_next_key", "mk->k_seg[c][(int64_t)b * lenc + j])",
+     "mk->k_seg[c][(int64_t)b * lenc + (j + 1) % lenc])", 1),
     ("bwd_D_unweighted", "D += exp(s[t] - ls) * acc;", "D += acc;", 1),
     ("bwd_dq_without_D", "double ds = exp(s[t] - ls) * (dp[t] - D);", "double ds = exp(s[t] - ls) * dp[t];", 1),
     ("bwd_dk_without_D", "double ds = p * (dpv - Dsum[row]);", "double ds = p * dpv;", 1),
@@ -64,7 +76,7 @@ MUTANTS = [
     ("bwd_dk_unscaled", "gk[e] += scale * ds * elem(q, dtype, qb + e);", "gk[e] += ds * elem(q, dtype, qb + e);", 1),
     ("bwd_dq_sign", "g[e] += scale * ds * elem(k[c], dtype, kb + e);", "g[e] -= scale * ds * elem(k[c], dtype, kb + e);", 1),
     ("bwd_first_head_of_group_only", "for (int h = hk * G; h < (hk + 1) * G; ++h)", "for (int h = hk * G; h < hk * G + 1; ++h)", 1),
-    ("bwd_dkdv_ignore_mask", "if (!visible(causal, window, q_offset + r, start[c] + j))\n                    continue;",
+    ("bwd_dkdv_ignore_mask", "if (!visible(mk, Lq, len[c], b, r, c, j, q_offset + r, start[c] + j))\n                    continue;",
      "if (0)\n                    continue;", 1),
     ("bwd_unnormalised_weights", "double p = exp(score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale) - lse[row]);",
      "double p = exp(score(q, k[c], dtype, Lq, len[c], Hq, Hkv, dqk, b, r, h, j, scale) - lse[row] + 0.01);", 1),
