@@ -123,6 +123,18 @@ typedef struct ra_desc {
      * window <= 0: no window.  Tiles and chunks outside every window of a
      * workgroup are not read. */
     int64_t window;
+    /* Anchor tokens: with anchor = S > 0 a query at position p also sees
+     * the keys at A - 1, A and A + S, A = S * floor(p / S), when they
+     * exist, whatever the window and the causal rule say (the same
+     * section's sparse mask, whose anchor stride is 4096).  0: none. */
+    int64_t anchor;
+    /* Segment labels of the query rows, [B, Lq] int32 dense (device), or
+     * NULL.  With labels (given for the queries and every chunk) a query
+     * sees only keys with its own label: packed sequences, the
+     * segment_ids of page "RingAttention推理优化：cache_idx参数使用...".
+     * Anchors and labels are built for d = 64 and 128 (bf16 and fp32);
+     * RA_ERR_UNSUPPORTED with d = 512 or an 8-bit KV cache. */
+    const int32_t *q_seg;
 } ra_desc;
 
 typedef struct ra_kv_chunk {
@@ -134,6 +146,9 @@ typedef struct ra_kv_chunk {
      * exponents, dense [B, Hkv, ceil(len / RA_KV_SCALE_BLOCK)] uint8 */
     const uint8_t *k_exp;
     const uint8_t *v_exp;
+    /* segment labels of the keys, [B, len] int32 dense (device), or NULL;
+     * required exactly when ra_desc.q_seg is given */
+    const int32_t *k_seg;
 } ra_kv_chunk;
 
 typedef struct ra_ctx ra_ctx;
@@ -159,12 +174,17 @@ int ring_attn_ring_order(int device_index, int P, int32_t *order);
 
 /* Chunk classes for a query chunk of Lq rows at absolute positions
  * q_offset .. q_offset+Lq-1 (host only): cls[c] = RA_CHUNK_SKIP (no key
- * visible to any query) / FULL (every key visible to every query) / DIAG
- * for the chunk at starts[c] with lens[c] keys, under causal masking and
- * the local window (as ra_desc.window; <= 0: none).  Non-causal without a
- * window: all FULL (empty chunks: SKIP). */
-int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window, int P,
-                   const int64_t *starts, const int64_t *lens, int32_t *cls);
+ * visible to any query) / FULL (every key visible to every query by the
+ * causal and window rules alone: no mask is applied) / DIAG (masked per
+ * element) for the chunk at starts[c] with lens[c] keys, under causal masking, the
+ * local window and anchor tokens (as ra_desc.window and ra_desc.anchor;
+ * <= 0 / 0: none).  A chunk holding an anchor of some query is never
+ * skipped.  Segment labels are device data and not considered here: they
+ * can only hide more keys.  Non-causal without a window: all FULL (empty
+ * chunks: SKIP). */
+int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window,
+                   int64_t anchor, int P, const int64_t *starts,
+                   const int64_t *lens, int32_t *cls);
 
 /* Bytes of device workspace ring_attn_fwd needs for these arguments
  * (host only; k/v pointers are not read).  0 is a valid answer. */

@@ -75,13 +75,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A) {
 // ---------------------------------------------------------------------------
 // dQ: query rows resident, key tiles streamed (the forward's structure)
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(const BwdArgs A) {
+template <int D, int BN, int NW, int NS, bool EXT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(EXT ? 1 : 2, EXT ? 1 : 2)))
+void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the registers of the label masks)
     const FwdArgs &a = A.f;
     using C = Cfg<D, BN, NW, 1>;
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
-    RA_STAGE_ARRAYS(NS, C::TILE)
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (EXT ? 1 : 0);
+    constexpr int LABB = EXT ? NW * 256 : 0;  // bytes of key labels per stage (after the K tile)
+    RA_STAGE_ARRAYS(NS, C::TILE + LABB)
+    static_assert(!EXT || C::KW <= 64, "a wave's labels are 64 dwords");
 
     const int lane = threadIdx.x & 63, w = wave_index();
     const int l32 = lane & 31, g = lane >> 5;
@@ -118,19 +120,34 @@ void bwd_dq_kernel(const BwdArgs A) {
     k_addrs<C>(0, l32, g, kaddr);
     int vaddr[2][C::NVD];
     v_addrs<C>(0, lane, vaddr);
+    int ql = 0, lab_L = 0;  // the row's segment label; the wave's common one
+    bool lab_uniform = true;
+    if constexpr (EXT) {
+        if (a.q_seg && row.ok) ql = a.q_seg[wt.b * a.Lq + row.t];
+        wave_label(ql, row.ok, lab_L, lab_uniform);
+    }
 
     for (int c = 0; c < a.n_chunks; ++c) {
-        int64_t kbeg, kend;
-        int ntiles;
-        if (!chunk_range(a, wt, c, 0, kbeg, kend, ntiles, BN)) continue;  // uniform
+        TileRange tr;
+        if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr)) continue;  // uniform
+        const int64_t kbeg = tr.kbeg, kend = tr.kend;
+        const int ntiles = tr.ntot;
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        Anchors an{kNoKey, kNoKey, kNoKey};
+        if constexpr (EXT) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
+        const int32_t *kseg = EXT && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto tile_start = [&](int t) -> int64_t {
+            if constexpr (EXT) return tr.start(t, BN);
+            else return kbeg + (int64_t)t * BN;
+        };
         auto issue = [&](auto u, int t) {
-            const int64_t k0 = kbeg + (int64_t)t * BN;
+            const int64_t k0 = tile_start(t);
             load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
             load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+            if constexpr (EXT) load_labels(kseg, k0, kend, kst(u) + C::TILE + 256 * w, lane);
         };
         auto wait_for = [&](int need, int last) {
             const int after = last - need;
@@ -144,14 +161,25 @@ void bwd_dq_kernel(const BwdArgs A) {
         for_tiles<NS>(ntiles, [&](auto u, int it) {
             constexpr int U = decltype(u)::value;
             if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
-            const int64_t k0 = kbeg + (int64_t)it * BN;
-            const bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
-            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
+            const int64_t k0 = tile_start(it);
+            bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
+            bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
+            const char *lab = kst(u) + C::TILE + 256 * w;
+            if constexpr (EXT) {
+                if (skip && tile_has_anchor(a, ch.start, k0, BN, wv_tlo, wv_thi)) skip = false;
+                bool lall, lnone;
+                label_tile(lab, BN, kend - k0, lane, lab_L, lab_uniform, lall, lnone);
+                skip = skip || lnone;
+                full = full && lall;
+            }
             if (!skip) {
                 f32x16 s[C::KB], dp[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);   // S^T = K Q^T
                 scores<C>(vst(u), kaddr, gf, dp);  // dP^T = V dO^T
-                if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                if (!full) {
+                    if constexpr (EXT) mask_scores_ext<C>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
+                    else mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                }
                 // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
                 bf16x8 pf[2 * C::KB];
 #pragma unroll
@@ -210,14 +238,16 @@ constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
 // gives 2 TILE + 2048 RB bytes a stage.  The RB row blocks are independent
 // chains of matrix-core work, which lets one wave overlap the softmax of one
 // block with the products of another.
-template <int D, int RB, int NS>
+template <int D, int RB, int NS, bool EXT>
 __global__ __launch_bounds__(kKvWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const BwdArgs A) {
     const FwdArgs &a = A.f;
     constexpr int RT = 32 * RB;              // query rows per tile
     using C = Cfg<D, RT, kKvWaves, 1>;       // RT-row tiles: TILE bytes each for Q and dO; KB = RB
-    constexpr int LDW = 256 * RB;            // bytes of (lse2, D) pairs per wave
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE + RB;
+    constexpr int LDW = 256 * RB;            // bytes of (lse2, D) pairs per wave (row labels: half that)
+    // EXT: each wave's copy of the rows' segment labels follows the dO tile
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + RB + (EXT ? 1 : 0);
+    static_assert(!EXT || RT <= 64, "a wave's row labels are 64 dwords");
     RA_STAGE_ARRAYS(NS, C::TILE + 1024 * RB)
     auto qtile = [&](auto u) { return kst(u); };
     auto ldtile = [&](auto u) { return kst(u) + C::TILE; };
@@ -237,6 +267,7 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     const int64_t wk0 = kt0 + 32 * w;       // this wave's first key
     const int64_t key = wk0 + l32;          // this lane's key
     const bool key_ok = key < len;
+    auto kpos_of = [&](int64_t k) { return ch.start + k; };
 
     // resident B operands: K^T and V^T fragments of the lane's key
     bf16x8 kf[C::DS], vf[C::DS];
@@ -273,9 +304,57 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             t_lo = lo > t_lo ? lo : t_lo;
         }
     }
+    // anchors: a key at a block start m anchors rows [m - S, m + S) (as A and
+    // as A + S), the key before it rows [m, m + S) (as A - 1)
+    int64_t ar_lo = 1, ar_hi = 0;  // the lane's anchored rows [lo, hi) (positions)
+    int64_t u_lo = 0, u_hi = -1;   // rows anchored by any key of the workgroup (tokens)
+    if constexpr (EXT) {
+        if (a.anchor > 0) {
+            const int64_t S = a.anchor;
+            if (key_ok && kpos_of(key) % S == 0) ar_lo = kpos_of(key) - S, ar_hi = kpos_of(key) + S;
+            if (key_ok && (kpos_of(key) + 1) % S == 0) {
+                const int64_t lo = kpos_of(key) + 1, hi = lo + S;
+                ar_lo = ar_lo < ar_hi && ar_lo < lo ? ar_lo : lo;
+                ar_hi = ar_hi > hi ? ar_hi : hi;
+            }
+            const int64_t m0 = (kp_lo + S - 1) / S * S, y0 = (kp_lo + 1 + S - 1) / S * S;
+            int64_t blo = INT64_MAX, bhi = INT64_MIN;
+            if (m0 <= kp_hi) blo = m0 - S, bhi = kp_hi / S * S + S;
+            if (y0 <= kp_hi + 1) {
+                blo = y0 < blo ? y0 : blo;
+                const int64_t yl = (kp_hi + 1) / S * S + S;
+                bhi = yl > bhi ? yl : bhi;
+            }
+            if (blo < bhi) {
+                u_lo = blo - a.q_offset > 0 ? blo - a.q_offset : 0;
+                u_hi = bhi - 1 - a.q_offset < a.Lq - 1 ? bhi - 1 - a.q_offset : a.Lq - 1;
+            }
+        }
+    }
+    // row segments: the window's rows, then the anchored rows not next to them
     t_lo = t_lo / RT * RT;
-    const int nrt = t_hi >= t_lo ? (int)((t_hi - t_lo) / RT + 1) : 0;
-    const int ntiles = nrt * a.G;
+    int n1 = t_hi >= t_lo ? (int)((t_hi - t_lo) / RT + 1) : 0;
+    int64_t s2 = 0;
+    int n2 = 0;
+    if (EXT && u_lo <= u_hi) {
+        const int64_t ulo = u_lo / RT * RT;
+        if (n1 == 0) {
+            t_lo = ulo, n1 = (int)((u_hi - ulo) / RT + 1);
+        } else if (ulo <= t_hi + 1 && u_hi + 1 >= t_lo) {  // overlapping or adjacent: one segment
+            const int64_t lo = ulo < t_lo ? ulo : t_lo, hi = u_hi > t_hi ? u_hi : t_hi;
+            t_lo = lo, n1 = (int)((hi - lo) / RT + 1);
+        } else {
+            s2 = ulo, n2 = (int)((u_hi - ulo) / RT + 1);
+        }
+    }
+    const int nseg = n1 + n2;
+    const int ntiles = nseg * a.G;
+    int kl = 0, lab_L = 0;  // the key's segment label; the wave's common one
+    bool lab_uniform = true;
+    if constexpr (EXT) {
+        if (ch.kseg && key_ok) kl = ch.kseg[b * len + key];
+        wave_label(kl, key_ok, lab_L, lab_uniform);
+    }
 
     int kaddr[C::NKA];
     k_addrs<C>(0, l32, g, kaddr);
@@ -285,9 +364,9 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     const int64_t kpos = ch.start + key;
 
     auto tile_of = [&](int it, int &h, int64_t &t0) {
-        const int gq = it / nrt;
+        const int gq = it / nseg, j = it % nseg;
         h = hk * a.G + gq;
-        t0 = t_lo + RT * (int64_t)(it % nrt);
+        t0 = j < n1 ? t_lo + RT * (int64_t)j : s2 + RT * (int64_t)(j - n1);
     };
     auto issue = [&](auto u, int it) {
         int h;
@@ -305,6 +384,8 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         for (int rb = 0; rb < RB; ++rb)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(ldtile(u) + LDW * w + 256 * rb), 4,
                                                      (unsigned)(256 * rb + lane * 4), 0, 0, 0);
+        if constexpr (EXT)  // the rows' segment labels (RT <= 64: one dword per lane)
+            load_labels(a.q_seg ? a.q_seg + b * a.Lq : nullptr, t0, a.Lq, gtile(u) + C::TILE + 256 * w, lane);
     };
     auto wait_for = [&](int need, int last) {
         const int after = last - need;
@@ -321,8 +402,18 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         int64_t t0;
         tile_of(it, h, t0);
         const int64_t thi = t0 + RT - 1 < a.Lq - 1 ? t0 + RT - 1 : a.Lq - 1;
-        const bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
-        const bool full = t0 + RT - 1 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
+        bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
+        bool full = t0 + RT - 1 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
+        const char *rlab = gtile(u) + C::TILE + 256 * w;  // EXT: labels of the tile's rows
+        if constexpr (EXT) {
+            // anchored rows of a lane's key inside the tile
+            const bool anch = ar_lo < ar_hi && ar_lo <= a.q_offset + thi && ar_hi > a.q_offset + t0;
+            if (skip && wk0 < len && __builtin_amdgcn_ballot_w64(anch) != 0) skip = false;
+            bool lall, lnone;
+            label_tile(rlab, RT, a.Lq - t0, lane, lab_L, lab_uniform, lall, lnone);
+            skip = skip || lnone;
+            full = full && lall;
+        }
         if (!skip) {
             const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + LDW * w;
             // S = Q K^T and dP = dO V^T per 32-row block: rows on M, this wave's keys on N
@@ -352,13 +443,39 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                 lo = lo < -big ? -big : (lo > big ? big : lo);
                 hi = hi < -big ? -big : (hi > big ? big : hi);
                 const int lo32 = (int)lo, hi32 = (int)hi;
+                if constexpr (EXT) {
+                    // anchored rows and labels
+                    const int64_t p0 = a.q_offset + t0 + 4 * g;  // position at ro = 0
+                    int64_t alo = ar_lo - p0, ahi = ar_hi - p0;
+                    if (!key_ok || ar_lo >= ar_hi) alo = big, ahi = big;
+                    alo = alo < -big ? -big : (alo > big ? big : alo);
+                    ahi = ahi < -big ? -big : (ahi > big ? big : ahi);
+                    const int alo32 = (int)alo, ahi32 = (int)ahi;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                    for (int rb = 0; rb < RB; ++rb) {
+                        int rl[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
-                        if (ro < lo32 || ro >= hi32) s[rb][i] = kNegInf;
+                        for (int j = 0; j < 4; ++j) {
+                            const i32x4 x = *(const i32x4 *)(rlab + 4 * (32 * rb + 8 * j + 4 * g));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) rl[4 * j + e] = x[e];
+                        }
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+                            const bool in = (ro >= lo32 && ro < hi32) || (ro >= alo32 && ro < ahi32);
+                            if (!in || rl[i] != kl) s[rb][i] = kNegInf;
+                        }
                     }
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+                            if (ro < lo32 || ro >= hi32) s[rb][i] = kNegInf;
+                        }
+                }
             }
             // P and dS, packed as B operands: k-step ks covers rows 16ks .. 16ks+15
             bf16x8 pp[2 * RB], pd[2 * RB];
@@ -445,10 +562,15 @@ hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.f.n_rowtiles * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;
-    if (d == 128)
-        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+    const bool ext = a.f.anchor > 0 || a.f.q_seg != nullptr;
+    if (d == 128 && ext)
+        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2, true>), dim3(grid), dim3(256), 0, s, a);
+    else if (d == 128)
+        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2, false>), dim3(grid), dim3(256), 0, s, a);
+    else if (ext)
+        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2, true>), dim3(grid), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2, false>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -457,10 +579,16 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s) {
     const int64_t nkt = (len + kKvKeys - 1) / kKvKeys;
     const unsigned grid = (unsigned)(nkt * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;
-    if (d == 128)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+    const bool ext = a.f.anchor > 0 || a.f.q_seg != nullptr;
+    const dim3 blk(kKvWaves * 64);
+    if (d == 128 && ext)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2, true>), dim3(grid), blk, 0, s, a);
+    else if (d == 128)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2, false>), dim3(grid), blk, 0, s, a);
+    else if (ext)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2, true>), dim3(grid), blk, 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2>), dim3(grid), dim3(kKvWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2, false>), dim3(grid), blk, 0, s, a);
     return hipGetLastError();
 }
 

@@ -184,12 +184,17 @@ __device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const
 // ---------------------------------------------------------------------------
 // The attention kernel: one tile at a time (query-chunk prefill and split-KV decoding)
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int KSPLIT, int NS>
+// EXT instantiations add anchor tokens and segment labels: each stage then
+// also holds 64 key labels per wave (after the K tile), and up to five extra
+// tiles hold anchors outside the window's range.
+template <int D, int BN, int NW, int KSPLIT, int NS, bool EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
-    RA_STAGE_ARRAYS(NS, C::TILE)
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (EXT ? 1 : 0);
+    constexpr int LABB = EXT ? NW * 256 : 0;  // bytes of key labels per stage
+    RA_STAGE_ARRAYS(NS, C::TILE + LABB)
+    static_assert(!EXT || C::KW <= 64, "a wave's labels are 64 dwords");
     // merge scratch of the key-split waves: slot s spans tile buffers 2s, 2s+1
     static_assert(KSPLIT == 1 || (C::ROWW * (KSPLIT - 1) <= 2 && (16 * C::DB + 2) * 64 * 4 <= 2 * C::TILE),
                   "merge scratch must fit in the tile buffers");
@@ -212,6 +217,12 @@ void fwd_bf16_kernel(const FwdArgs a) {
     k_addrs<C>(wk * C::KW, l32, g, kaddr);
     int vaddr[2][C::NVD];
     v_addrs<C>(wk * C::KW, lane, vaddr);
+    int ql = 0, lab_L = 0;  // the row's segment label; the wave's common one
+    bool lab_uniform = true;
+    if constexpr (EXT) {
+        if (a.q_seg && row.ok) ql = a.q_seg[wt.b * a.Lq + row.t];
+        wave_label(ql, row.ok, lab_L, lab_uniform);
+    }
 
     int c_begin = 0, c_end = a.n_chunks, sub = 0;
     if (a.split_mode) {
@@ -220,17 +231,26 @@ void fwd_bf16_kernel(const FwdArgs a) {
         c_end = c_begin + 1;
     }
     for (int c = c_begin; c < c_end; ++c) {
-        int64_t kbeg, kend;
-        int ntiles;
-        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        TileRange tr;
+        if (!chunk_tiles<EXT>(a, wt, c, sub, BN, tr)) continue;  // uniform
+        const int64_t kbeg = tr.kbeg, kend = tr.kend;
+        const int ntiles = tr.ntot;
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        Anchors an{kNoKey, kNoKey, kNoKey};
+        if constexpr (EXT) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
+        const int32_t *kseg = EXT && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto tile_start = [&](int t) -> int64_t {
+            if constexpr (EXT) return tr.start(t, BN);
+            else return kbeg + (int64_t)t * BN;
+        };
         auto issue = [&](auto u, int t) {
-            const int64_t k0 = kbeg + (int64_t)t * BN;
+            const int64_t k0 = tile_start(t);
             load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
             load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+            if constexpr (EXT) load_labels(kseg, k0 + wk * C::KW, kend, kst(u) + C::TILE + 256 * w, lane);
         };
         auto wait_for = [&](int need, int last) {
             const int after = last - need;
@@ -245,16 +265,27 @@ void fwd_bf16_kernel(const FwdArgs a) {
             constexpr int U = decltype(u)::value;
             if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
             // this wave's keys k0 + wk*KW .. + KW-1
-            const int64_t k0 = kbeg + (int64_t)it * BN;
+            const int64_t k0 = tile_start(it);
             const int64_t wk0 = k0 + wk * C::KW;
-            const bool skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
-            const bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
+            bool skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
+            bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
+            const char *lab = kst(u) + C::TILE + 256 * w;
+            if constexpr (EXT) {
+                if (skip && tile_has_anchor(a, ch.start, wk0, C::KW, wv_tlo, wv_thi)) skip = false;
+                bool lall, lnone;
+                label_tile(lab, C::KW, kend - wk0, lane, lab_L, lab_uniform, lall, lnone);
+                skip = skip || lnone;
+                full = full && lall;
+            }
             if (!skip) {
                 if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
                 f32x16 s[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);
                 if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-                if (!full) mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
+                if (!full) {
+                    if constexpr (EXT) mask_scores_ext<C>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
+                    else mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
+                }
                 update_max<C>(s, c2, m_run, m_true, lsum, oacc);
                 bf16x8 pf[2 * C::KB];
                 probabilities<C>(s, c2, m_run, lsum, pf);
@@ -690,11 +721,21 @@ hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s) {
+    const bool ext = a.anchor > 0 || a.q_seg != nullptr;  // anchors / labels: d = 64, 128 only
     switch (d) {
-    case 64: return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2>, a, s);
+    case 64:
+        if (ext) return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2, true>, a, s);
+        return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2, false>, a, s);
     case 128:
-        if (split_mode) return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2>, a, s);
-        return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>, a, s);
+        if (split_mode) {
+            if (ext) return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2, true>, a, s);
+            return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2, false>, a, s);
+        }
+        if (ext)
+            return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(
+                fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, true>, a, s);
+        return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(
+            fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, false>, a, s);
     case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2, 2>, a, s);
     default: return hipErrorInvalidValue;
     }

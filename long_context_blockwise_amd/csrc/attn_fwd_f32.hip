@@ -29,6 +29,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
     constexpr int RB = kThreads / TPR;        // rows per workgroup
     __shared__ __attribute__((aligned(16))) float Ks[kKeys][D];
     __shared__ __attribute__((aligned(16))) float Vs[kKeys][D];
+    __shared__ int Ls[kKeys];  // segment labels of the tile's keys (0 without labels)
 
     const int tid = threadIdx.x;
     const int part = tid % TPR;               // which 64-wide slice of d
@@ -80,6 +81,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
         for (int e = 0; e < 64; ++e) o[e] = op[e];
     }
     const float c2 = a.scale_log2;
+    const int ql = a.q_seg && row_ok ? a.q_seg[(int64_t)b * Lq + t] : 0;
+    const int64_t anc = a.anchor > 0 ? qpos / a.anchor * a.anchor : 0;  // the row's anchor block
 
     int c_begin = 0, c_end = a.n_chunks, sub = 0;
     if (a.split_mode) {
@@ -99,10 +102,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
             const int64_t vis = pos_hi - ch.start + 1 + (a.causal ? 0 : a.window);
             kstop = vis < kstop ? vis : kstop;
         }
-        if (a.window > 0) {  // start at the tile of the first key the first row may see
+        if (a.window > 0 && a.anchor <= 0) {  // start at the tile of the first key the first row may see
             const int64_t lo = pos_lo - a.window - ch.start;
             if (lo > kbeg) kbeg += (lo - kbeg) / kKeys * kKeys;
         }
+        if (a.anchor > 0) kstop = kend;  // anchors may lie anywhere: walk every key
         const float *kbase = (const float *)ch.k + b * a.k_sb + hk * a.k_sh;
         const float *vbase = (const float *)ch.v + b * a.v_sb + hk * a.v_sh;
         for (int64_t k0 = kbeg; k0 < kstop; k0 += kKeys) {
@@ -117,6 +121,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
                 *(f32x4 *)&Ks[row][col] = kv;
                 *(f32x4 *)&Vs[row][col] = vv;
             }
+            if (tid < kKeys)
+                Ls[tid] = ch.kseg && k0 + tid < kend ? ch.kseg[(int64_t)b * ch.len + k0 + tid] : 0;
             __syncthreads();
             for (int j0 = 0; j0 < kKeys; j0 += kSub) {
                 float s[kSub];
@@ -132,9 +138,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
                     }
                     const int64_t key = k0 + j0 + j;
                     const int64_t kpos = ch.start + key;
-                    const bool vis = key < kend && (!a.causal || kpos <= qpos) &&
-                                     (a.window <= 0 ||
-                                      (kpos >= qpos - a.window && (a.causal || kpos <= qpos + a.window)));
+                    const bool anchor = a.anchor > 0 && (kpos == anc - 1 || kpos == anc || kpos == anc + a.anchor);
+                    const bool vis = key < kend && Ls[j0 + j] == ql &&
+                                     (anchor || ((!a.causal || kpos <= qpos) &&
+                                                 (a.window <= 0 || (kpos >= qpos - a.window &&
+                                                                    (a.causal || kpos <= qpos + a.window)))));
                     s[j] = vis ? acc * c2 : kNegInf;
                     smax = fmaxf(smax, s[j]);
                 }

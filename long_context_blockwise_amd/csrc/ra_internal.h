@@ -16,6 +16,7 @@ struct ChunkArg {
     int64_t start;  // absolute position of key 0
     int64_t len;    // keys in the chunk
     const uint8_t *kexp, *vexp;  // 8-bit KV: biased scale exponents [B, Hkv, ceil(len/64)]
+    const int32_t *kseg;         // segment labels of the keys [B, len], or null
 };
 
 // Arguments of the forward kernels (bf16 MFMA and fp32 paths).
@@ -36,6 +37,8 @@ struct FwdArgs {
     int64_t Lq, Lq_pad, q_offset;
     int64_t sub_len;           // split mode: keys per sub-range of a chunk
     int64_t window;            // local window (> 0), or 0: none
+    int64_t anchor;            // anchor-token stride (> 0), or 0: none
+    const int32_t *q_seg;      // segment labels of the query rows [B, Lq], or null
     int B, Hq, Hkv, G;
     int causal;
     int load_state;            // start from (m, l, O) instead of empty

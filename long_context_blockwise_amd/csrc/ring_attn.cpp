@@ -98,6 +98,10 @@ int check_desc(const ra_desc *d, int64_t Lq, Strides *st) {
         return fail(RA_ERR_INVALID_ARG, "kv_dtype %d unknown", d->kv_dtype);
     if (kv_fp8(d) && (d->dtype != RA_BF16 || d->d_qk != 128))
         return fail(RA_ERR_UNSUPPORTED, "an 8-bit KV cache is built for bf16 queries with d = 128");
+    if (d->anchor < 0) return fail(RA_ERR_INVALID_ARG, "anchor must be >= 0");
+    if ((d->anchor > 0 || d->q_seg) && (kv_fp8(d) || (d->dtype == RA_BF16 && d->d_qk == 512)))
+        return fail(RA_ERR_UNSUPPORTED, "anchor tokens and segment labels are built for d = 64, 128 (bf16, fp32)");
+    if (d->q_seg && ((uintptr_t)d->q_seg & 3)) return fail(RA_ERR_INVALID_ARG, "q_seg must be 4-byte aligned");
     const int qalign = d->dtype == RA_BF16 ? 8 : 4;  // elements of 16-byte units
     const int kvalign = kv_fp8(d) ? 16 : qalign;
     auto fill = [&](const int64_t *in, int64_t *out, int64_t S, int64_t H, int64_t D, const char *name) -> int {
@@ -137,6 +141,18 @@ int check_desc(const ra_desc *d, int64_t Lq, Strides *st) {
 
 bool dense_kv(const int64_t *s) { return s[0] == 0 && s[1] == 0 && s[2] == 0; }
 
+// Segment labels come for the queries and every non-empty chunk, or not at all.
+int check_labels(const ra_desc *d, const ra_kv_chunk *chunks, int P) {
+    for (int c = 0; c < P && chunks; ++c) {
+        if (chunks[c].len <= 0) continue;
+        const bool has = chunks[c].k_seg != nullptr;
+        if (has != (d->q_seg != nullptr))
+            return fail(RA_ERR_INVALID_ARG, "chunk %d: segment labels must be given for the queries and every chunk", c);
+        if (has && ((uintptr_t)chunks[c].k_seg & 3)) return fail(RA_ERR_INVALID_ARG, "chunk %d: k_seg misaligned", c);
+    }
+    return RA_OK;
+}
+
 // k/v strides of one chunk (dense BSHD when the descriptor gives none)
 void chunk_strides(const int64_t *given, int64_t len, int Hkv, int dd, int64_t *out) {
     if (dense_kv(given)) {
@@ -148,9 +164,25 @@ void chunk_strides(const int64_t *given, int64_t len, int Hkv, int dd, int64_t *
     }
 }
 
+// Do the keys start .. start+len-1 hold an anchor (stride S) of a query at
+// q_offset .. q_offset+Lq-1?  Block m's anchors are mS - 1, mS and (m+1)S.
+bool holds_anchor(int64_t Lq, int64_t q_offset, int64_t S, int64_t start, int64_t len) {
+    if (S <= 0 || len <= 0 || Lq <= 0) return false;
+    const int64_t m_lo = q_offset / S, m_hi = (q_offset + Lq - 1) / S, end = start + len - 1;
+    // some m in [lo, hi] with start <= mS + off <= end (start - off and end - off are >= 0)
+    auto any = [&](int64_t lo, int64_t hi, int64_t off) {
+        return std::max(lo, (start - off + S - 1) / S) <= std::min(hi, (end - off) / S);
+    };
+    return any(m_lo, m_hi, -1) || any(m_lo, m_hi + 1, 0);
+}
+
 // Chunk class of keys start .. start+len-1 for queries q_offset .. q_offset+Lq-1.
-int classify(int64_t Lq, int64_t q_offset, int causal, int64_t window, int64_t start, int64_t len) {
+int classify(int64_t Lq, int64_t q_offset, int causal, int64_t window, int64_t anchor, int64_t start, int64_t len) {
     if (len <= 0 || Lq <= 0) return RA_CHUNK_SKIP;
+    if (holds_anchor(Lq, q_offset, anchor, start, len)) {
+        const int c = classify(Lq, q_offset, causal, window, 0, start, len);
+        return c == RA_CHUNK_SKIP ? RA_CHUNK_DIAG : c;
+    }
     const int64_t first_q = q_offset, last_q = q_offset + Lq - 1, last_k = start + len - 1;
     const bool win = window > 0;
     // keys any query may see: [first_q - window, last_q (+ window)]
@@ -237,7 +269,7 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
                 return fail(RA_ERR_INVALID_ARG, "chunk %d: an 8-bit KV chunk needs k_exp and v_exp", c);
     }
     for (int c = 0; c < P; ++c)
-        if (classify(Lq, q_offset, causal, d->window, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
+        if (classify(Lq, q_offset, causal, d->window, d->anchor, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
             pl->steps.push_back(c);
 
     const int es = elem_size(d->dtype);
@@ -297,6 +329,8 @@ FwdArgs base_args(const ra_desc *d, const Strides &st, const void *q, int64_t Lq
     a.B = d->B, a.Hq = d->Hq, a.Hkv = d->Hkv, a.G = d->Hq / d->Hkv;
     a.causal = causal ? 1 : 0;
     a.window = d->window > 0 ? d->window : 0;
+    a.anchor = d->anchor;
+    a.q_seg = d->q_seg;
     const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->d_qk);
     a.scale_log2 = scale * 1.4426950408889634f;
     return a;
@@ -343,7 +377,7 @@ struct DeviceGuard {
 
 extern "C" {
 
-const char *ring_attn_version(void) { return "ringattn 0.3 (gfx950)"; }
+const char *ring_attn_version(void) { return "ringattn 0.4 (gfx950)"; }
 
 const char *ring_attn_last_error(void) { return g_err.c_str(); }
 
@@ -392,13 +426,13 @@ int ring_attn_ring_order(int device_index, int P, int32_t *order) {
     return RA_OK;
 }
 
-int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window, int P, const int64_t *starts,
-                   const int64_t *lens, int32_t *cls) {
-    if (P < 0 || Lq < 0 || q_offset < 0) return fail(RA_ERR_INVALID_ARG, "negative argument");
+int ring_attn_plan(int64_t Lq, int64_t q_offset, int causal, int64_t window, int64_t anchor, int P,
+                   const int64_t *starts, const int64_t *lens, int32_t *cls) {
+    if (P < 0 || Lq < 0 || q_offset < 0 || anchor < 0) return fail(RA_ERR_INVALID_ARG, "negative argument");
     if (P > 0 && (!starts || !lens || !cls)) return fail(RA_ERR_INVALID_ARG, "NULL array");
     for (int c = 0; c < P; ++c) {
         if (starts[c] < 0 || lens[c] < 0) return fail(RA_ERR_INVALID_ARG, "chunk %d: negative start/len", c);
-        cls[c] = classify(Lq, q_offset, causal, window, starts[c], lens[c]);
+        cls[c] = classify(Lq, q_offset, causal, window, anchor, starts[c], lens[c]);
     }
     return RA_OK;
 }
@@ -441,6 +475,7 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     for (int c = 0; c < P && chunks; ++c)
         if (chunks[c].len > 0 && (misaligned(chunks[c].k) || misaligned(chunks[c].v)))
             return fail(RA_ERR_INVALID_ARG, "chunk %d: k/v must be 16-byte aligned", c);
+    if ((rc = check_labels(d, chunks, P))) return rc;
     Plan pl;
     if ((rc = make_plan(d, Lq, chunks, P, causal, q_offset, flags, have_state, &pl))) return rc;
     if (pl.total > 0 && (!workspace || ws_bytes < pl.total))
@@ -486,7 +521,7 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
                 if (nsub != nsub0) break;
                 if (dense_kv(d->k_strides) || dense_kv(d->v_strides))
                     if (ch.len != len0) break;  // dense strides depend on the length
-                a.chunks[a.n_chunks++] = ChunkArg{ch.k, ch.v, ch.start, ch.len, ch.k_exp, ch.v_exp};
+                a.chunks[a.n_chunks++] = ChunkArg{ch.k, ch.v, ch.start, ch.len, ch.k_exp, ch.v_exp, ch.k_seg};
                 ++j;
             }
             set_chunk_strides(a, d, len0);
@@ -573,9 +608,9 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
             if (staged) {
                 const char *base = ws + pl.off_stage[li & 1];
                 const size_t kbytes = (size_t)d->B * ch.len * d->Hkv * d->d_qk * es;
-                a.chunks[i] = ChunkArg{base, base + kbytes, ch.start, ch.len};
+                a.chunks[i] = ChunkArg{base, base + kbytes, ch.start, ch.len, nullptr, nullptr, ch.k_seg};
             } else {
-                a.chunks[i] = ChunkArg{ch.k, ch.v, ch.start, ch.len};
+                a.chunks[i] = ChunkArg{ch.k, ch.v, ch.start, ch.len, nullptr, nullptr, ch.k_seg};
             }
         }
         if (staged) {
@@ -638,6 +673,7 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     if (P < 0 || P > ra::kMaxChunks) return fail(RA_ERR_INVALID_ARG, "P must be in 0..%d", ra::kMaxChunks);
     if (P > 0 && (!chunks || !grads)) return fail(RA_ERR_INVALID_ARG, "chunks and grads must be given");
     if ((flags & ~RA_FLAG_ACCUMULATE) != 0) return fail(RA_ERR_INVALID_ARG, "the backward takes only ACCUMULATE");
+    if (P > 0 && (rc = check_labels(d, chunks, P))) return rc;
     const bool accumulate = (flags & RA_FLAG_ACCUMULATE) != 0;
     auto misaligned = [](const void *p) { return ((uintptr_t)p & 15) != 0; };
     for (int c = 0; c < P; ++c) {
@@ -681,7 +717,7 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         // dQ: chunks that share k/v strides go in one launch; later launches add
         std::vector<int> steps;
         for (int c = 0; c < P; ++c)
-            if (classify(Lq, q_offset, causal, d->window, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
+            if (classify(Lq, q_offset, causal, d->window, d->anchor, chunks[c].start, chunks[c].len) != RA_CHUNK_SKIP)
                 steps.push_back(c);
         std::vector<std::vector<int>> launches = group_ring_launches(d, chunks, steps, false);
         bool first = true;
@@ -690,7 +726,7 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
             A.f.n_chunks = (int)grp.size();
             for (size_t i = 0; i < grp.size(); ++i) {
                 const ra_kv_chunk &c = chunks[grp[i]];
-                A.f.chunks[i] = ChunkArg{c.k, c.v, c.start, c.len, nullptr, nullptr};
+                A.f.chunks[i] = ChunkArg{c.k, c.v, c.start, c.len, nullptr, nullptr, c.k_seg};
             }
             if (!grp.empty()) set_chunk_strides(A.f, d, chunks[grp[0]].len);
             // with no chunk to walk, the launch writes dQ = 0 (or leaves the sum)
@@ -704,7 +740,8 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     A.chunk = 0;
     for (int c = 0; c < P; ++c) {
         if (chunks[c].len == 0) continue;
-        A.f.chunks[0] = ChunkArg{chunks[c].k, chunks[c].v, chunks[c].start, chunks[c].len, nullptr, nullptr};
+        A.f.chunks[0] =
+            ChunkArg{chunks[c].k, chunks[c].v, chunks[c].start, chunks[c].len, nullptr, nullptr, chunks[c].k_seg};
         set_chunk_strides(A.f, d, chunks[c].len);
         A.dk = grads[c].dk, A.dv = grads[c].dv;
         if ((e = ra::launch_bwd_dkdv(A, d->d_qk, s)) != hipSuccess) return hip_fail(e, "backward dK/dV launch");

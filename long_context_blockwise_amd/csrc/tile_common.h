@@ -33,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -346,6 +347,105 @@ __device__ inline bool keys_all_seen(const FwdArgs &a, int64_t cstart, int64_t k
     return true;
 }
 
+// ---------------------------------------------------------------------------
+// Anchor tokens and segment labels (kernels instantiated with EXT)
+// ---------------------------------------------------------------------------
+// A query at p also sees the keys at A - 1, A and A + S, A = S floor(p / S),
+// whatever the window and causal rules say; with segment labels it sees only
+// keys of its own label.  Labels travel with the K tiles (one 4-byte label
+// per key, each wave its own keys) and are zero when the call has none.
+constexpr int kNoKey = -2147483647 - 1;  // matches no key index
+
+struct Anchors {
+    int a0, a1, a2;  // key indices relative to kbeg, or kNoKey
+};
+
+// The anchors of a row at position qpos among the keys [kbase, kend) of a
+// chunk starting at cstart, relative to kbeg.
+__device__ inline Anchors row_anchors(const FwdArgs &a, int64_t qpos, int64_t cstart, int64_t kbase, int64_t kbeg,
+                                      int64_t kend) {
+    Anchors r{kNoKey, kNoKey, kNoKey};
+    if (a.anchor <= 0) return r;
+    const int64_t A = qpos / a.anchor * a.anchor - cstart;
+    auto pick = [&](int64_t x) { return x >= kbase && x < kend ? (int)(x - kbeg) : kNoKey; };
+    r.a0 = pick(A - 1);
+    r.a1 = pick(A);
+    r.a2 = pick(A + a.anchor);
+    return r;
+}
+
+// Does the tile of keys k0 .. k0+n-1 (absolute k0 + cstart) hold an anchor of
+// a row at positions q_offset + tlo .. q_offset + thi?  Rows spanning more
+// than two anchor blocks are answered yes.
+__device__ inline bool tile_has_anchor(const FwdArgs &a, int64_t cstart, int64_t k0, int64_t n, int64_t tlo,
+                                       int64_t thi) {
+    if (a.anchor <= 0) return false;
+    const int64_t S = a.anchor;
+    const int64_t A0 = (a.q_offset + tlo) / S * S, A1 = (a.q_offset + thi) / S * S;
+    if (A1 - A0 > S) return true;
+    const int64_t first = cstart + k0, last = first + n - 1;
+    auto in = [&](int64_t x) { return x >= first && x <= last; };
+    return in(A0 - 1) || in(A0) || in(A0 + S) || in(A1 - 1) || in(A1) || in(A1 + S);
+}
+
+// mask_scores with anchors and labels: a key is visible iff (it lies in
+// [lo, hi) or is one of the row's anchors) and its label (the wave's labels
+// of the tile, at lab) equals the row's label ql.
+template <class C>
+__device__ inline void mask_scores_ext(f32x16 (&s)[C::KB], VisRange v, Anchors an, int rel, int g, const char *lab,
+                                       int ql) {
+    const int off = rel + 4 * g;  // key index of element (0, 0) minus the lane-independent part
+    const int hi = v.hi - off, lo = v.lo - off;
+    auto shift = [&](int x) { return x == kNoKey ? kNoKey : x - off; };
+    const int a0 = shift(an.a0), a1 = shift(an.a1), a2 = shift(an.a2);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+        int lk[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const i32x4 x = *(const i32x4 *)(lab + 4 * (32 * kb + 8 * j + 4 * g));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lk[4 * j + e] = x[e];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
+            const bool in = (key >= lo && key < hi) || key == a0 || key == a1 || key == a2;
+            if (!in || lk[i] != ql) s[kb][i] = kNegInf;
+        }
+    }
+}
+
+// The rows' common label L of a wave (uniform = every valid row has it).
+__device__ inline void wave_label(int ql, bool ok, int &L, bool &uniform) {
+    const uint64_t okm = __builtin_amdgcn_ballot_w64(ok);
+    const int first = okm ? __builtin_ctzll(okm) : 0;
+    L = __builtin_amdgcn_readlane(ql, first);
+    uniform = __builtin_amdgcn_ballot_w64(ok && ql != L) == 0;
+}
+
+// Label test of a wave's n (<= 64) keys of a tile (label of key `lane` at
+// lab; keys at or past nvalid do not exist): with uniform row label L, every
+// key carries it (all) / none does (none).
+__device__ inline void label_tile(const char *lab, int n, int64_t nvalid, int lane, int L, bool uniform, bool &all,
+                                  bool &none) {
+    const bool mine = lane < n;
+    const bool valid = mine && lane < nvalid;
+    const int lk = reinterpret_cast<const int *>(lab)[lane];
+    const bool eq = valid && lk == L;
+    all = uniform && __builtin_amdgcn_ballot_w64(mine && !eq) == 0;
+    none = uniform && __builtin_amdgcn_ballot_w64(eq) == 0;
+}
+
+// Key labels of one wave's 64 keys k0 .. k0+63 of a chunk, HBM -> LDS (one
+// dword per lane); zero past kend or when the chunk has none.
+__device__ inline void load_labels(const int32_t *kseg, int64_t k0, int64_t kend, char *dst, int lane) {
+    const unsigned nvalid = kseg ? (unsigned)(kend - k0 < 64 ? (kend - k0 > 0 ? kend - k0 : 0) : 64) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kseg ? kseg + k0 : nullptr), (short)0, (int)(nvalid * 4), kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, (unsigned)lane * 4u, 0, 0, 0);
+}
+
 // S^T (KB 32-key blocks) = K Q^T from an LDS tile over the NDS reduction
 // steps whose K units start at kt, PF fragments in flight.
 template <class C, int NDS>
@@ -413,6 +513,66 @@ __device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, 
     if (kstop <= kbeg) return false;
     ntiles = (int)((kstop - kbeg + bn - 1) / bn);
     return true;
+}
+
+// Tiles of chunk c a workgroup walks: the main range of chunk_range, plus
+// (kernels with anchors) up to five tiles holding anchors of its rows that
+// lie outside it.  Rows spanning more than two anchor blocks take every
+// tile of the chunk.  All fields are uniform across the workgroup.
+struct TileRange {
+    int64_t kbase, kbeg, kend;  // first key of the chunk or sub-range, first main tile, end of keys
+    int nmain, ntot;
+    int64_t e0, e1, e2, e3, e4;  // first keys of the extra tiles
+    __device__ int64_t start(int it, int bn) const {
+        if (it < nmain) return kbeg + (int64_t)it * bn;
+        const int j = it - nmain;
+        return j == 0 ? e0 : j == 1 ? e1 : j == 2 ? e2 : j == 3 ? e3 : e4;
+    }
+};
+
+template <bool EXT>
+__device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, int sub, int bn, TileRange &tr) {
+    const ChunkArg &ch = a.chunks[c];
+    tr.kbase = a.split_mode ? sub * a.sub_len : 0;
+    int64_t kbeg, kend;
+    int nmain = 0;
+    if (!chunk_range(a, wt, c, sub, kbeg, kend, nmain, bn)) {
+        nmain = 0;
+        kbeg = tr.kbase;
+        kend = a.split_mode ? (tr.kbase + a.sub_len < ch.len ? tr.kbase + a.sub_len : ch.len) : ch.len;
+    }
+    tr.kbeg = kbeg, tr.kend = kend, tr.nmain = nmain, tr.ntot = nmain;
+    tr.e0 = tr.e1 = tr.e2 = tr.e3 = tr.e4 = 0;
+    if constexpr (EXT) {
+        if (a.anchor > 0 && kend > tr.kbase) {
+            const int64_t S = a.anchor;
+            const int64_t A0 = (a.q_offset + wt.wg_tlo) / S * S, A1 = (a.q_offset + wt.wg_thi) / S * S;
+            if (A1 - A0 > S) {  // every tile of the chunk
+                tr.kbeg = tr.kbase;
+                tr.nmain = tr.ntot = (int)((kend - tr.kbase + bn - 1) / bn);
+            } else {
+                const int64_t cand[6] = {A0 - 1, A0, A0 + S, A1 - 1, A1, A1 + S};
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const int64_t x = cand[i] - ch.start;
+                    if (x < tr.kbase || x >= kend) continue;
+                    const int64_t ts = tr.kbase + (x - tr.kbase) / bn * bn;
+                    if (ts >= tr.kbeg && ts < tr.kbeg + (int64_t)tr.nmain * bn) continue;
+                    const int ne = tr.ntot - tr.nmain;
+                    if ((ne > 0 && tr.e0 == ts) || (ne > 1 && tr.e1 == ts) || (ne > 2 && tr.e2 == ts) ||
+                        (ne > 3 && tr.e3 == ts))
+                        continue;
+                    if (ne == 0) tr.e0 = ts;
+                    else if (ne == 1) tr.e1 = ts;
+                    else if (ne == 2) tr.e2 = ts;
+                    else if (ne == 3) tr.e3 = ts;
+                    else tr.e4 = ts;
+                    ++tr.ntot;
+                }
+            }
+        }
+    }
+    return tr.ntot > 0;
 }
 
 // ---------------------------------------------------------------------------

@@ -172,6 +172,22 @@ def output_grad(wl: Workload, device="cpu", std: float = 1.0) -> torch.Tensor:
     return draw((wl.B, wl.Lq, wl.Hq, wl.d_v), std, wl.torch_dtype, device, wl.seed, _TENSOR_DO)
 
 
+def packed_labels(B: int, n: int, mean_doc: int, seed: int, device="cpu") -> torch.Tensor:
+    """Segment labels ``[B, n]`` (int32) of sequences packed from documents
+    of seeded random lengths (uniform in 1 .. 2 * mean_doc): position t of
+    batch b carries the index of its document."""
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty((B, n), dtype=torch.int32)
+    for b in range(B):
+        pos, doc = 0, 0
+        while pos < n:
+            L = int(torch.randint(1, 2 * mean_doc + 1, (1,), generator=g))
+            out[b, pos:pos + L] = doc
+            pos += L
+            doc += 1
+    return out.to(device)
+
+
 def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:
     """Draw the query chunk and all KV chunks of a workload on ``device``."""
     dt = wl.torch_dtype

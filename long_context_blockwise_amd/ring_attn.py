@@ -50,12 +50,13 @@ class ra_desc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
                 ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
-                ("window", ctypes.c_int64)]
+                ("window", ctypes.c_int64), ("anchor", ctypes.c_int64), ("q_seg", ctypes.c_void_p)]
 
 
 class ra_kv_chunk(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("start", ctypes.c_int64),
-                ("len", ctypes.c_int64), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
+                ("len", ctypes.c_int64), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p),
+                ("k_seg", ctypes.c_void_p)]
 
 
 class ra_kv_grad(ctypes.Structure):
@@ -89,7 +90,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ring_attn_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
         lib.ring_attn_ctx_destroy.argtypes = [vp]
         lib.ring_attn_ring_order.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i32)]
-        lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, i64, ctypes.c_int, ctypes.POINTER(i64),
+        lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, i64, i64, ctypes.c_int, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i32)]
         lib.ring_attn_workspace_size.argtypes = [ctypes.POINTER(ra_desc), i64, ctypes.POINTER(ra_kv_chunk),
                                                  ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32,
@@ -131,12 +132,12 @@ def ring_attn_ring_order(device_index: int, P: int) -> List[int]:
 
 
 def ring_attn_plan(Lq: int, q_offset: int, causal: bool, starts: Sequence[int],
-                   lens: Sequence[int], window: int = 0) -> List[int]:
+                   lens: Sequence[int], window: int = 0, anchor: int = 0) -> List[int]:
     P = len(starts)
     st = (ctypes.c_int64 * max(P, 1))(*starts)
     ln = (ctypes.c_int64 * max(P, 1))(*lens)
     cls = (ctypes.c_int32 * max(P, 1))()
-    _check(load().ring_attn_plan(Lq, q_offset, int(bool(causal)), int(window), P, st, ln, cls))
+    _check(load().ring_attn_plan(Lq, q_offset, int(bool(causal)), int(window), int(anchor), P, st, ln, cls))
     return list(cls)[:P]
 
 
@@ -189,10 +190,13 @@ def _strides(t) -> Tuple[int, int, int]:
     return t.stride(0), t.stride(1), t.stride(2)
 
 
-def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0) -> Tuple[ra_desc, object]:
+def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0, anchor: int = 0, q_seg=None,
+              k_segs=None) -> Tuple[ra_desc, object]:
     """ra_desc and the ra_kv_chunk array for a query tensor and chunks
     ``(k, v, start)``, or ``(k, v, start, k_exp, v_exp)`` for an 8-bit KV cache
-    (k, v ``torch.float8_e4m3fn``; exponents ``uint8 [B, Hkv, ceil(len/64)]``)."""
+    (k, v ``torch.float8_e4m3fn``; exponents ``uint8 [B, Hkv, ceil(len/64)]``).
+    ``q_seg [B, Lq]`` and ``k_segs`` (one ``[B, len]`` per chunk) are int32
+    segment labels, given together or not at all."""
     import torch
 
     B, Lq, Hq, dqk = q.shape
@@ -204,6 +208,15 @@ def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0) -> Tuple
     d.dtype = _dtype_code(q)
     d.scale = float(scale)
     d.window = int(window)
+    d.anchor = int(anchor)
+    if (q_seg is None) != (k_segs is None):
+        raise RingAttnError(RA_ERR_INVALID_ARG, "q_seg and k_segs go together")
+    if q_seg is not None:
+        if q_seg.dtype != torch.int32 or not q_seg.is_contiguous() or tuple(q_seg.shape) != (B, Lq):
+            raise RingAttnError(RA_ERR_INVALID_ARG, f"q_seg must be contiguous int32 [{B}, {Lq}]")
+        if len(k_segs) != len(chunks):
+            raise RingAttnError(RA_ERR_INVALID_ARG, "one k_segs entry per chunk")
+        d.q_seg = q_seg.data_ptr()
     d.q_strides[:] = _strides(q)
     if out is not None:
         d.o_strides[:] = _strides(out)
@@ -227,6 +240,11 @@ def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0) -> Tuple
         arr[i].v = v.data_ptr()
         arr[i].start = int(start)
         arr[i].len = int(k.shape[1])
+        if k_segs is not None:
+            ks = k_segs[i]
+            if ks.dtype != torch.int32 or not ks.is_contiguous() or tuple(ks.shape) != (B, int(k.shape[1])):
+                raise RingAttnError(RA_ERR_INVALID_ARG, f"k_segs[{i}] must be contiguous int32 [B, len]")
+            arr[i].k_seg = ks.data_ptr()
         if fp8:
             if len(c) != 5:
                 raise RingAttnError(RA_ERR_INVALID_ARG, "8-bit chunks are (k, v, start, k_exp, v_exp)")
@@ -241,8 +259,9 @@ def make_desc(q, chunks, scale: float = 0.0, out=None, window: int = 0) -> Tuple
 
 
 def ring_attn_workspace_size(q, chunks, causal: bool = False, q_offset: int = 0, flags: int = 0,
-                             want_state: bool = False, scale: float = 0.0, window: int = 0) -> int:
-    d, arr = make_desc(q, chunks, scale, window=window)
+                             want_state: bool = False, scale: float = 0.0, window: int = 0, anchor: int = 0,
+                             q_seg=None, k_segs=None) -> int:
+    d, arr = make_desc(q, chunks, scale, window=window, anchor=anchor, q_seg=q_seg, k_segs=k_segs)
     n = ctypes.c_size_t()
     _check(load().ring_attn_workspace_size(ctypes.byref(d), q.shape[1], arr, len(chunks),
                                            int(bool(causal)), int(q_offset), int(flags),
@@ -253,11 +272,14 @@ def ring_attn_workspace_size(q, chunks, causal: bool = False, q_offset: int = 0,
 def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: int = 0,
                   out=None, state=None, want_out: bool = True, want_state: bool = False,
                   scale: float = 0.0, ctx: Optional[RingAttnContext] = None, workspace=None,
-                  stream=None, window: int = 0):
+                  stream=None, window: int = 0, anchor: int = 0, q_seg=None, k_segs=None):
     """One device's share of ring attention; returns ``(out, state)``.
 
     ``window > 0`` limits each query to keys at distance <= window (a local
     window; under causal masking keys p - window .. p of a query at p).
+    ``anchor = S > 0`` adds the anchor keys A - 1, A, A + S (A = S * (p // S));
+    ``q_seg``/``k_segs`` are int32 segment labels (a query sees only keys
+    with its label).
 
     ``state`` (if given) is a tuple ``(m, l, O)`` of fp32 tensors ``[B, Lq, Hq]``,
     ``[B, Lq, Hq]``, ``[B, Lq, Hq, d_v]`` that receives the softmax state (and
@@ -275,7 +297,7 @@ def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: 
         state = (torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
                  torch.empty((B, Lq, Hq), device=q.device, dtype=torch.float32),
                  torch.empty((B, Lq, Hq, dv), device=q.device, dtype=torch.float32))
-    d, arr = make_desc(q, chunks, scale, out, window)
+    d, arr = make_desc(q, chunks, scale, out, window, anchor, q_seg, k_segs)
     lib = load()
     n = ctypes.c_size_t()
     _check(lib.ring_attn_workspace_size(ctypes.byref(d), Lq, arr, len(chunks), int(bool(causal)),
@@ -325,16 +347,16 @@ def ring_attn_merge(m_parts, l_parts, O_parts, out_dtype=None, *, out=None, stat
     return out, state
 
 
-def ring_attn_bwd_workspace_size(q, chunks, scale: float = 0.0, window: int = 0) -> int:
-    d, _ = make_desc(q, chunks, scale, window=window)
+def ring_attn_bwd_workspace_size(q, chunks, scale: float = 0.0, window: int = 0, anchor: int = 0) -> int:
+    d, _ = make_desc(q, chunks, scale, window=window, anchor=anchor)
     n = ctypes.c_size_t()
     _check(load().ring_attn_bwd_workspace_size(ctypes.byref(d), q.shape[1], ctypes.byref(n)))
     return int(n.value)
 
 
 def ring_attn_bwd(q, chunks, out, dout, state, causal: bool = False, q_offset: int = 0, *, flags: int = 0,
-                  dq=None, grads=None, scale: float = 0.0, window: int = 0,
-                  ctx: Optional[RingAttnContext] = None, workspace=None, stream=None):
+                  dq=None, grads=None, scale: float = 0.0, window: int = 0, anchor: int = 0, q_seg=None,
+                  k_segs=None, ctx: Optional[RingAttnContext] = None, workspace=None, stream=None):
     """Gradients of one device's share of ring attention; returns ``(dq, [(dk, dv), ...])``.
 
     ``out``/``dout`` ``[B, Lq, Hq, d_v]`` are the forward output and its
@@ -353,7 +375,7 @@ def ring_attn_bwd(q, chunks, out, dout, state, causal: bool = False, q_offset: i
     for t in (m, l):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, Lq, Hq):
             raise RingAttnError(RA_ERR_INVALID_ARG, "m and l must be contiguous fp32 [B, Lq, Hq]")
-    d, arr = make_desc(q, chunks, scale, out, window)
+    d, arr = make_desc(q, chunks, scale, out, window, anchor, q_seg, k_segs)
     if dq is None:
         dq = torch.empty((B, Lq, Hq, dqk), device=q.device, dtype=torch.float32)
     if grads is None:

@@ -62,11 +62,15 @@ def test_ring_order_rejects_bad_args(lib):
         ra.ring_attn_ring_order(0, 0)
 
 
-def _brute_class(Lq, q_off, causal, start, n, window=0):
+def _brute_class(Lq, q_off, causal, start, n, window=0, anchor=0):
     if n == 0 or Lq == 0:
         return ra.RA_CHUNK_SKIP
 
     def seen(qp, kp):
+        if anchor > 0:
+            A = qp // anchor * anchor
+            if kp in (A - 1, A, A + anchor):
+                return True
         if causal and kp > qp:
             return False
         return window <= 0 or abs(kp - qp) <= window
@@ -74,21 +78,25 @@ def _brute_class(Lq, q_off, causal, start, n, window=0):
     vis = [[seen(q_off + r, start + j) for j in range(n)] for r in range(Lq)]
     if not any(any(row) for row in vis):
         return ra.RA_CHUNK_SKIP
-    if all(all(row) for row in vis):
+    # FULL: no mask needed, i.e. every pair visible by the causal and window rules alone
+    base = [[(not causal or start + j <= q_off + r) and (window <= 0 or abs(start + j - q_off - r) <= window)
+             for j in range(n)] for r in range(Lq)]
+    if all(all(row) for row in base):
         return ra.RA_CHUNK_FULL
     return ra.RA_CHUNK_DIAG
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window", [0, 1, 3, 7, 40])
-def test_plan_matches_brute_force(lib, causal, window):
+@pytest.mark.parametrize("anchor", [0, 1, 4, 7])
+def test_plan_matches_brute_force(lib, causal, window, anchor):
     starts = [0, 5, 9, 20, 21, 30]
     lens = [5, 4, 11, 1, 9, 0]
     for Lq in (1, 3, 8):
         for q_off in (0, 4, 5, 8, 9, 19, 20, 29, 35):
-            got = ra.ring_attn_plan(Lq, q_off, causal, starts, lens, window=window)
-            want = [_brute_class(Lq, q_off, causal, s, n, window) for s, n in zip(starts, lens)]
-            assert got == want, (Lq, q_off, window)
+            got = ra.ring_attn_plan(Lq, q_off, causal, starts, lens, window=window, anchor=anchor)
+            want = [_brute_class(Lq, q_off, causal, s, n, window, anchor) for s, n in zip(starts, lens)]
+            assert got == want, (Lq, q_off, window, anchor)
 
 
 def test_plan_of_the_prefill_share():
@@ -203,9 +211,10 @@ def test_context_needs_a_device(lib):
 
 
 def test_struct_layouts_match_the_header():
-    assert ctypes.sizeof(rb.ra_desc) == 8 * 4 + 13 * 8
+    assert ctypes.sizeof(rb.ra_desc) == 8 * 4 + 15 * 8
     assert rb.ra_desc.window.offset == 8 * 4 + 12 * 8
-    assert ctypes.sizeof(rb.ra_kv_chunk) == 6 * 8
+    assert rb.ra_desc.anchor.offset == 8 * 4 + 13 * 8 and rb.ra_desc.q_seg.offset == 8 * 4 + 14 * 8
+    assert ctypes.sizeof(rb.ra_kv_chunk) == 7 * 8 and rb.ra_kv_chunk.k_seg.offset == 48
     assert rb.ra_desc.kv_dtype.offset == 7 * 4
     assert rb.ra_kv_chunk.k_exp.offset == 32 and rb.ra_kv_chunk.v_exp.offset == 40
 
@@ -289,3 +298,39 @@ def test_bwd_workspace_and_validation(lib):
     grads[1].dv = None
     assert bwd() == rb.RA_ERR_INVALID_ARG
     assert ctypes.sizeof(rb.ra_kv_grad) == 16
+
+
+
+def test_anchor_and_label_validation(lib):
+    """Anchors and labels: negative strides are rejected; d = 512 and the
+    8-bit cache are not built for them; labels come for the queries and
+    every non-empty chunk or not at all."""
+    arr = _chunks([64, 64])
+    d = _desc()
+    d.anchor = -1
+    assert _ws(lib, d, 8, arr, 2, 1, 64, 0, 0)[0] == rb.RA_ERR_INVALID_ARG
+    for bad in (_desc(d=512, Hkv=1),):
+        bad.anchor = 16
+        assert _ws(lib, bad, 8, _chunks([64]), 1, 1, 64, 0, 0)[0] == rb.RA_ERR_UNSUPPORTED
+    f8 = _desc()
+    f8.kv_dtype = rb.RA_FP8_E4M3
+    f8.q_seg = 1 << 12
+    assert _ws(lib, f8, 8, _chunks([64]), 1, 1, 64, 0, 0)[0] == rb.RA_ERR_UNSUPPORTED
+    ok = _desc()
+    ok.anchor = 4096
+    assert _ws(lib, ok, 8, arr, 2, 1, 64, 0, 0)[0] == 0
+    # labels on the queries only, or on a chunk only: rejected before any device work
+    ctx = ctypes.create_string_buffer(256)
+    lab = _desc()
+    lab.q_seg = 1 << 12
+
+    def fwd(desc, chunks):
+        return lib.ring_attn_fwd(ctx, ctypes.byref(desc), 1 << 20, 8, chunks, 2, 1, 64, 0, 1 << 20, None, None,
+                                 None, None, 0, None)
+    assert fwd(lab, _chunks([64, 64])) == rb.RA_ERR_INVALID_ARG
+    one = _chunks([64, 64])
+    one[0].k_seg = 1 << 12
+    assert fwd(_desc(), one) == rb.RA_ERR_INVALID_ARG
+    mis = _chunks([64, 64])
+    mis[0].k_seg, mis[1].k_seg = 1 << 12, (1 << 12) + 2
+    assert fwd(lab, mis) == rb.RA_ERR_INVALID_ARG
