@@ -128,10 +128,15 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
     }
 
     for (int c = 0; c < a.n_chunks; ++c) {
-        TileRange tr;
-        if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr)) continue;  // uniform
-        const int64_t kbeg = tr.kbeg, kend = tr.kend;
-        const int ntiles = tr.ntot;
+        TileRange tr;  // (without EXT the plain range, as in the forward kernel)
+        int64_t kbeg, kend;
+        int ntiles;
+        if constexpr (EXT) {
+            if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr)) continue;  // uniform
+            kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
+        } else {
+            if (!chunk_range(a, wt, c, 0, kbeg, kend, ntiles, BN)) continue;  // uniform
+        }
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         Anchors an{kNoKey, kNoKey, kNoKey};
@@ -332,6 +337,7 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         }
     }
     // row segments: the window's rows, then the anchored rows not next to them
+    // (without EXT the single range, in the code of a kernel without anchors)
     t_lo = t_lo / RT * RT;
     int n1 = t_hi >= t_lo ? (int)((t_hi - t_lo) / RT + 1) : 0;
     int64_t s2 = 0;
@@ -364,9 +370,15 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     const int64_t kpos = ch.start + key;
 
     auto tile_of = [&](int it, int &h, int64_t &t0) {
-        const int gq = it / nseg, j = it % nseg;
-        h = hk * a.G + gq;
-        t0 = j < n1 ? t_lo + RT * (int64_t)j : s2 + RT * (int64_t)(j - n1);
+        if constexpr (EXT) {
+            const int gq = it / nseg, j = it % nseg;
+            h = hk * a.G + gq;
+            t0 = j < n1 ? t_lo + RT * (int64_t)j : s2 + RT * (int64_t)(j - n1);
+        } else {
+            const int gq = it / n1;
+            h = hk * a.G + gq;
+            t0 = t_lo + RT * (int64_t)(it % n1);
+        }
     };
     auto issue = [&](auto u, int it) {
         int h;

@@ -231,10 +231,17 @@ void fwd_bf16_kernel(const FwdArgs a) {
         c_end = c_begin + 1;
     }
     for (int c = c_begin; c < c_end; ++c) {
+        // (without EXT the plain range: the same code as a kernel without
+        // anchors, which the compiler schedules with fewer waits)
         TileRange tr;
-        if (!chunk_tiles<EXT>(a, wt, c, sub, BN, tr)) continue;  // uniform
-        const int64_t kbeg = tr.kbeg, kend = tr.kend;
-        const int ntiles = tr.ntot;
+        int64_t kbeg, kend;
+        int ntiles;
+        if constexpr (EXT) {
+            if (!chunk_tiles<EXT>(a, wt, c, sub, BN, tr)) continue;  // uniform
+            kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
+        } else {
+            if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        }
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         Anchors an{kNoKey, kNoKey, kNoKey};
