@@ -211,19 +211,24 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
     }
 
     if (!row.ok) return;
-    // dQ element i of block db in lane l is d = 32db + 8(i/4) + 4g + i%4
+    // dQ element i of block db in lane l is d = 32db + 8(i/4) + 4g + i%4; with
+    // ACCUMULATE every old value is loaded before any store
     float *dq = A.dq + row.srow * D + 4 * g;
+    f32x4 old[C::DB][4];
+    if (A.accumulate) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) old[db][i4] = *(const f32x4 *)(dq + 32 * db + 8 * i4);
+    }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             f32x4 v;
-            if (A.accumulate) v = *(const f32x4 *)(dq + 32 * db + 8 * i4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x = A.scale * acc[db][4 * i4 + j];
-                v[j] = A.accumulate ? v[j] + x : x;
-            }
+            for (int j = 0; j < 4; ++j) v[j] = A.scale * acc[db][4 * i4 + j];
+            if (A.accumulate) v += old[db][i4];
             *(f32x4 *)(dq + 32 * db + 8 * i4) = v;
         }
 }
@@ -535,21 +540,31 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     // element i of block db in lane l is d = 32db + 8(i/4) + 4g + i%4 of the lane's key
     const int64_t off = ((b * len + key) * a.Hkv + hk) * D + 4 * g;
     float *pk = A.dk + off, *pv = A.dv + off;
+    // with ACCUMULATE every old value is loaded before any store
+    f32x4 ok[C::DB][4], ov[C::DB][4];
+    if (A.accumulate) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                ok[db][i4] = *(const f32x4 *)(pk + 32 * db + 8 * i4);
+                ov[db][i4] = *(const f32x4 *)(pv + 32 * db + 8 * i4);
+            }
+    }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int e = 32 * db + 8 * i4;
             f32x4 x, y;
-            if (A.accumulate) {
-                x = *(const f32x4 *)(pk + e);
-                y = *(const f32x4 *)(pv + e);
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float gk = A.scale * dk[db][4 * i4 + j], gv = dv[db][4 * i4 + j];
-                x[j] = A.accumulate ? x[j] + gk : gk;
-                y[j] = A.accumulate ? y[j] + gv : gv;
+                x[j] = A.scale * dk[db][4 * i4 + j];
+                y[j] = dv[db][4 * i4 + j];
+            }
+            if (A.accumulate) {
+                x += ok[db][i4];
+                y += ov[db][i4];
             }
             *(f32x4 *)(pk + e) = x;
             *(f32x4 *)(pv + e) = y;
