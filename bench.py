@@ -35,18 +35,21 @@ PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of each workload's dominant kernel, from rocprofv3
+# HBM bytes per launch of each workload's dominant kernel (for the backward:
+# per step, summed over its bwd_pre, bwd_dq and bwd_dkdv launches), from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this script, scaled by what the same
 # counters read for a plain 1 GiB elementwise copy (--copy-calibration):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  Valid only for the kernel sources
 # they were taken on; any change to them voids the figures (traffic -> null).
-KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_context_blockwise_amd/csrc/ra_internal.h",
+KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_context_blockwise_amd/csrc/attn_bwd_bf16.hip",
+                  "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "ad45dbde0a622d7d",
-    "prefill_bf16_h32_d128": 6.5269e8,
+    "digest": "af931f5f25d19283",
+    "prefill_bf16_h32_d128": 6.5422e8,
     "decode_b4_gqa32x8_cache1m": 1.7250e10,
-    "decode_b4_gqa32x8_cache1m_fp8": 8.6619e9,
+    "decode_b4_gqa32x8_cache1m_fp8": 8.6620e9,
+    "bwd:prefill_bf16_h32_d128": 8.1304e9,
 }
 
 HEADLINE = "prefill_bf16_h32_d128"
@@ -231,8 +234,8 @@ class BackwardRun(WorkloadRun):
         tflops = self.flops / sec_per_step / 1e12
         achieved = self.flops / (ev_ms / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
-                    kernels="bwd_pre + bwd_dq + bwd_dkdv per step")
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("bwd:" + wl.name),
+                    kernels="bwd_pre + bwd_dq + bwd_dkdv per step (traffic: per step)")
         return dict(workload="bwd:" + wl.name, metric="causal attn bwd TFLOP/s (dQ, dK, dV) per GPU",
                     value=round(tflops, 2), unit="TFLOP/s", ms_per_step=round(sec_per_step * 1e3, 4),
                     tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1), tflops=round(tflops, 2),
