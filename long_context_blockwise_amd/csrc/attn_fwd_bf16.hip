@@ -504,10 +504,16 @@ constexpr int TILE = BN * ROWB;  // bytes of one K (or V) tile
 constexpr int NW = 4;            // waves: 2 row blocks x 2 key halves
 constexpr int LOADS_PER_WAVE = TILE / 1024 / NW;
 constexpr int BLOCK = 64;        // tokens per scale exponent (= keys per wave per tile)
+constexpr int kMaxRangeBlocks = kFp8MaxRangeBlocks;  // scale blocks of one workgroup's key range
 using C = Cfg<D, BN, NW, 2>;     // row/key geometry: 64 rows, 64 keys per wave, KB = 2
 static_assert(C::KW == BLOCK, "each wave's keys of a tile share one scale block");
 
-__device__ inline int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+// Swizzle of the 16-byte units of 128-byte row r: a bijection on the eight
+// rows of one parity within 16 (the K reads: 16 rows at one unit), and rows
+// {0,2,8,10} (+1, +4) land in distinct unit pairs (the V^T reads: two 16-lane
+// groups on units u and u^1 of the same rows), so both read patterns are free
+// of bank conflicts.
+__device__ inline int swz8(int r) { return (((r >> 3) & 1) << 2) | (((r >> 1) & 1) << 1) | ((r >> 2) & 1); }
 
 // Scale 2^(e-127) of a biased exponent e in 1..254, as a float.
 __device__ inline float exp_scale(unsigned e) { return __builtin_bit_cast(float, e << 23); }
@@ -546,6 +552,10 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
     using namespace fp8kv;
     constexpr int LPT = 2 * LOADS_PER_WAVE;
     RA_STAGE_ARRAYS(NS, TILE)
+    // the scale exponents of the workgroup's key range, copied once per chunk
+    // (per-tile loads into registers would be waited for behind the next
+    // tile's prefetch)
+    __shared__ unsigned char exk[kMaxRangeBlocks], exv[kMaxRangeBlocks];
 
     const int lane = threadIdx.x & 63, w = wave_index();
     const int wr = w % C::ROWW, wk = w / C::ROWW;
@@ -616,7 +626,17 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
             wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
         };
 
-        tile_barrier();  // the previous chunk's tiles are no longer read
+        tile_barrier();  // the previous chunk's tiles and exponents are no longer read
+        const int64_t b0 = kbeg / BLOCK;  // exponents of blocks b0 .. b0 + nb - 1
+        {
+            const int64_t b1 = (kbeg + (int64_t)ntiles * BN + BLOCK - 1) / BLOCK;
+            int nb = (int)((b1 < nblk ? b1 : nblk) - b0);  // <= kMaxRangeBlocks (host caps the range)
+            nb = nb < kMaxRangeBlocks ? nb : kMaxRangeBlocks;
+            for (int i = (int)threadIdx.x; i < nb; i += NW * 64) {
+                exk[i] = kexp[b0 + i];
+                exv[i] = vexp[b0 + i];
+            }
+        }
         const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
         for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
         wait_for(0, pre - 1);
@@ -628,8 +648,8 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
             const bool skip = wk0 >= kend || keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
             const bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
             if (!skip) {
-                const int64_t blk = wk0 / BLOCK;
-                const float ks = exp_scale(kexp[blk]), vs = exp_scale(vexp[blk]);
+                const int bi = (int)(wk0 / BLOCK - b0);
+                const float ks = exp_scale(exk[bi]), vs = exp_scale(exv[bi]);
                 const char *kt = kst(u);
                 const char *vt = vst(u);
                 f32x16 s[C::KB];

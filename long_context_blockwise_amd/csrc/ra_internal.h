@@ -9,6 +9,8 @@ namespace ra {
 
 // KV chunks one kernel launch can walk (kernel arguments are at most 4 KiB).
 constexpr int kMaxChunks = 64;
+// Scale blocks of one 8-bit workgroup's key range (its exponents sit in LDS).
+constexpr int kFp8MaxRangeBlocks = 4096;
 
 struct ChunkArg {
     const void *k;

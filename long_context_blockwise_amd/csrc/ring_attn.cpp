@@ -299,6 +299,8 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
         int64_t n_sub = std::max<int64_t>(1, (kSplitTargetWorkgroups + base_wg - 1) / base_wg);
         int64_t sub_len = (maxlen + n_sub - 1) / n_sub;
         sub_len = std::max<int64_t>(256, (sub_len + 63) / 64 * 64);
+        // the 8-bit kernel copies the scale exponents of its key range to LDS
+        if (kv_fp8(d)) sub_len = std::min<int64_t>(sub_len, (int64_t)ra::kFp8MaxRangeBlocks * 64 - 256);
         pl->sub_len = sub_len;
         int total = 0;
         for (int c : pl->steps) total += (int)((chunks[c].len + sub_len - 1) / sub_len);
