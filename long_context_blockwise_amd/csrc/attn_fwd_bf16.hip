@@ -37,7 +37,9 @@
 //
 // Scheduling.  Tile t+1 is requested (HBM -> LDS) before tile t is computed;
 // two workgroups share a CU, so while one wave of a SIMD turns scores into
-// probabilities the other can feed the matrix cores.  For split-KV decoding
+// probabilities the other can feed the matrix cores.  Within a wave the
+// probabilities of keys 16(k+1) .. 16(k+1)+15 are computed between the O^T
+// MFMAs of keys 16k .. 16k+15, so the wave's own VALU work overlaps them.  For split-KV decoding
 // KSPLIT waves share each row block, each over its part of every key tile,
 // and merge their states through LDS at the end.
 #include "tile_common.h"
@@ -49,6 +51,15 @@
 #endif
 #ifndef RA_TUNE_NS
 #define RA_TUNE_NS 2
+#endif
+// Interleave the probabilities of the next 16 keys with the O^T MFMAs of the
+// current 16 (1), or compute all probabilities before the MFMAs (0); and the
+// VALU instructions placed after each MFMA when interleaving.
+#ifndef RA_TUNE_FUSE
+#define RA_TUNE_FUSE 1
+#endif
+#ifndef RA_TUNE_FUSE_VALU
+#define RA_TUNE_FUSE_VALU 7
 #endif
 
 namespace ra {
@@ -124,6 +135,67 @@ __device__ inline void probabilities(const f32x16 (&s)[C::KB], float c2, float m
             }
             pf[2 * kb + hh] = to_bf16x8(pk);
         }
+}
+
+// Waves raise their issue priority while they feed the matrix cores.
+__device__ inline void prio_mfma() {
+    if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ inline void prio_valu() {
+    if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
+// Probabilities of reduction step ks (16 keys) as one bf16 B operand of
+// O^T += V^T P^T; adds the fp32 p to lsum.
+template <class C>
+__device__ inline bf16x8 prob_step(const f32x16 (&s)[C::KB], int ks, float c2, float mref, float &lsum) {
+    const int kb = ks / 2, hh = ks % 2;
+    u32x4 pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float e0 = exp2_fast(__builtin_fmaf(s[kb][8 * hh + 2 * j], c2, -mref));
+        const float e1 = exp2_fast(__builtin_fmaf(s[kb][8 * hh + 2 * j + 1], c2, -mref));
+        lsum += e0 + e1;
+        pk[j] = pack_bf16(e0, e1);
+    }
+    return to_bf16x8(pk);
+}
+
+// probabilities + accumulate_pv with the VALU work of step ks+1 placed
+// between the MFMAs of step ks: the matrix cores run an MFMA while the same
+// wave issues the exponentials of the next step, so one wave keeps both
+// pipes busy instead of alternating between them.
+template <class C, int NDB>
+__device__ inline void softmax_pv(const f32x16 (&s)[C::KB], float c2, float m_run, float &lsum, const char *vt,
+                                  const int (&vaddr)[2][C::NVD], f32x16 (&o)[NDB]) {
+    const float mref = m_run == kNegInf ? 0.f : m_run;
+    constexpr int NK = 2 * C::KB;
+    bf16x8 fr[2][NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) fr[0][db] = vfrag<C>(vt, vaddr, 0, db);
+    bf16x8 p = prob_step<C>(s, 0, c2, mref, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    prio_mfma();
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 1 < NK) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) fr[(ks + 1) & 1][db] = vfrag<C>(vt, vaddr, ks + 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma(fr[ks & 1][db], p, o[db]);
+        if (ks + 1 < NK) {
+            p = prob_step<C>(s, ks + 1, c2, mref, lsum);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, RA_TUNE_FUSE_VALU, 0);  // VALU
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    prio_valu();
 }
 
 // Final state of a lane's row: renormalise to the true max, then write the
@@ -285,20 +357,24 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 full = full && lall;
             }
             if (!skip) {
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+                prio_mfma();
                 f32x16 s[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+                prio_valu();
                 if (!full) {
                     if constexpr (EXT) mask_scores_ext<C>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
                     else mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
                 }
                 update_max<C>(s, c2, m_run, m_true, lsum, oacc);
-                bf16x8 pf[2 * C::KB];
-                probabilities<C>(s, c2, m_run, lsum, pf);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-                accumulate_pv<C>(vst(u), vaddr, pf, oacc);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+                if constexpr (RA_TUNE_FUSE) {
+                    softmax_pv<C>(s, c2, m_run, lsum, vst(u), vaddr, oacc);
+                } else {
+                    bf16x8 pf[2 * C::KB];
+                    probabilities<C>(s, c2, m_run, lsum, pf);
+                    prio_mfma();
+                    accumulate_pv<C>(vst(u), vaddr, pf, oacc);
+                    prio_valu();
+                }
             }
             if (it + 1 < ntiles) {
                 const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
