@@ -238,6 +238,9 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
 constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
+#ifndef RA_TUNE_KV_VALU
+#define RA_TUNE_KV_VALU 3  // VALU instructions placed after each dV/dK MFMA
+#endif
 #ifndef RA_TUNE_KV_RB
 #define RA_TUNE_KV_RB 2
 #endif
@@ -494,41 +497,68 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                         }
                 }
             }
-            // P and dS, packed as B operands: k-step ks covers rows 16ks .. 16ks+15
-            bf16x8 pp[2 * RB], pd[2 * RB];
+            // P and dS of k-step ks (rows 16ks .. 16ks+15), packed as B operands
+            auto p_ds = [&](int ks, bf16x8 &ppk, bf16x8 &pdk) {
+                const int rb = ks / 2, hh = ks % 2;
+                u32x4 a4, b4;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+                for (int jj = 0; jj < 2; ++jj) {
+                    // rows 32rb + 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
+                    const char *lp = lt + 8 * (32 * rb + 16 * hh + 8 * jj + 4 * g);
+                    const f32x4 x = *(const f32x4 *)lp;
+                    const f32x4 y = *(const f32x4 *)(lp + 16);
+                    const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    u32x4 a4, b4;
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        // rows 32rb + 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
-                        const char *lp = lt + 8 * (32 * rb + 16 * hh + 8 * jj + 4 * g);
-                        const f32x4 x = *(const f32x4 *)lp;
-                        const f32x4 y = *(const f32x4 *)(lp + 16);
-                        const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
-#pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2) {
-                            const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
-                            const float p0 = exp2_fast(__builtin_fmaf(s[rb][i0], c2, -l4[2 * r2]));
-                            const float p1 = exp2_fast(__builtin_fmaf(s[rb][i1], c2, -l4[2 * r2 + 1]));
-                            a4[2 * jj + r2] = pack_bf16(p0, p1);
-                            b4[2 * jj + r2] =
-                                pack_bf16(p0 * (dp[rb][i0] - d4[2 * r2]), p1 * (dp[rb][i1] - d4[2 * r2 + 1]));
-                        }
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
+                        const float p0 = exp2_fast(__builtin_fmaf(s[rb][i0], c2, -l4[2 * r2]));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[rb][i1], c2, -l4[2 * r2 + 1]));
+                        a4[2 * jj + r2] = pack_bf16(p0, p1);
+                        b4[2 * jj + r2] =
+                            pack_bf16(p0 * (dp[rb][i0] - d4[2 * r2]), p1 * (dp[rb][i1] - d4[2 * r2 + 1]));
                     }
-                    pp[2 * rb + hh] = to_bf16x8(a4);
-                    pd[2 * rb + hh] = to_bf16x8(b4);
                 }
-            // dV^T += dO^T P and dK^T += Q^T dS
+                ppk = to_bf16x8(a4);
+                pdk = to_bf16x8(b4);
+            };
+            // dV^T += dO^T P and dK^T += Q^T dS, k-step by k-step; P and dS of
+            // step ks+1 are computed between the MFMAs of step ks, whose A
+            // operands were read from LDS during step ks-1
+            constexpr int NK = 2 * RB;
+            bf16x8 fg[2][C::DB], fq[2][C::DB];
 #pragma unroll
-            for (int ks = 0; ks < 2 * RB; ++ks)
+            for (int db = 0; db < C::DB; ++db) {
+                fg[0][db] = vfrag<C>(gt, vaddr, 0, db);
+                fq[0][db] = vfrag<C>(qt, vaddr, 0, db);
+            }
+            bf16x8 pp, pd;
+            p_ds(0, pp, pd);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+                if (ks + 1 < NK) {
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        fg[(ks + 1) & 1][db] = vfrag<C>(gt, vaddr, ks + 1, db);
+                        fq[(ks + 1) & 1][db] = vfrag<C>(qt, vaddr, ks + 1, db);
+                    }
+                }
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    dv[db] = mfma(vfrag<C>(gt, vaddr, ks, db), pp[ks], dv[db]);
-                    dk[db] = mfma(vfrag<C>(qt, vaddr, ks, db), pd[ks], dk[db]);
+                    dv[db] = mfma(fg[ks & 1][db], pp, dv[db]);
+                    dk[db] = mfma(fq[ks & 1][db], pd, dk[db]);
                 }
+                if (ks + 1 < NK) {
+                    p_ds(ks + 1, pp, pd);
+#pragma unroll
+                    for (int n = 0; n < 2 * C::DB; ++n) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+                        __builtin_amdgcn_sched_group_barrier(0x002, RA_TUNE_KV_VALU, 0);  // VALU
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (it + 1 < ntiles) {
             const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
