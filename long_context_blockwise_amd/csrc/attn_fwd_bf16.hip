@@ -116,6 +116,44 @@ __device__ inline void update_max(const f32x16 (&s)[C::KB], float c2, float &m_r
     }
 }
 
+// update_max for an O accumulator the matrix cores keep in AGPRs: the rare
+// rescale multiplies each register where it lives (read, multiply, write
+// back), so the compiler has no reason to keep a VGPR copy of O across the
+// loop.  VALU instructions cannot read AGPRs directly, hence the asm.  The
+// s_nops keep the gfx950 wait states between the last MFMA write of O and the
+// first read here, and between the last write here and the next MFMA that
+// reads O; both are far apart in the kernel already.
+template <class C, int NDB>
+__device__ inline void update_max_agpr(const f32x16 (&s)[C::KB], float c2, float &m_run, float &m_true, float &lsum,
+                                       f32x16 (&o)[NDB]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_pair(mx);
+    const float mt = mx * c2;
+    m_true = fmaxf(m_true, mt);
+    const bool need = mt > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? exp2_fast(m_run - mt) : 1.f;
+        m_run = need ? mt : m_run;
+        lsum *= alpha;
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = o[db][i], t;
+                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                             : "+a"(x), "=&v"(t)
+                             : "v"(alpha));
+                o[db][i] = x;
+            }
+        asm volatile("s_nop 7" ::: "memory");
+    }
+}
+
 // p = exp2(s*c - m_ref) as bf16 B operands of O^T += V^T P^T; adds the fp32 p to lsum.
 template <class C>
 __device__ inline void probabilities(const f32x16 (&s)[C::KB], float c2, float m_run, float &lsum,
@@ -510,34 +548,32 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
             constexpr int U = decltype(u)::value;
             if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
             const int64_t k0 = kbeg + (int64_t)it * BN;
-            // both waves of a row block take the same branch
-            const bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
+            // Tiles no row of the block sees (at most the last of a diagonal
+            // chunk) are computed and masked like the others: a branch around
+            // them would join two copies of O, and the compiler would copy the
+            // 128 O registers out of the AGPRs on every tile.
             const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
             f32x16 s[1];
-            if (!skip) {
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-                scores<C>(kst(u) + half_off, kaddr, qf, s);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+            scores<C>(kst(u) + half_off, kaddr, qf, s);
+            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4)
-                    xs_mine[i4 * 64 + lane] = f32x4{s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]};
-            }
+            for (int i4 = 0; i4 < 4; ++i4)
+                xs_mine[i4 * 64 + lane] = f32x4{s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]};
             tile_barrier();  // partial scores visible to the partner wave
-            if (!skip) {
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 o = xs_other[i4 * 64 + lane];
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 o = xs_other[i4 * 64 + lane];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) s[0][4 * i4 + j] += o[j];
-                }
-                if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
-                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
-                bf16x8 pf[2];
-                probabilities<C>(s, c2, m_run, lsum, pf);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-                accumulate_pv<C>(vst(u) + half_off, vaddr, pf, oacc);
-                if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+                for (int j = 0; j < 4; ++j) s[0][4 * i4 + j] += o[j];
             }
+            if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+            update_max_agpr<C>(s, c2, m_run, m_true, lsum, oacc);
+            bf16x8 pf[2];
+            probabilities<C>(s, c2, m_run, lsum, pf);
+            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+            accumulate_pv<C>(vst(u) + half_off, vaddr, pf, oacc);
+            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
             // the next tile's partial scores overwrite xs only after this barrier
             // (after a chunk's last tile: the barrier at the next chunk's start)
             if (it + 1 < ntiles) {
