@@ -241,6 +241,9 @@ constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
 #ifndef RA_TUNE_KV_VALU
 #define RA_TUNE_KV_VALU 3  // VALU instructions placed after each dV/dK MFMA
 #endif
+#ifndef RA_TUNE_KV_NS
+#define RA_TUNE_KV_NS 2  // LDS stages of the dK/dV kernel
+#endif
 #ifndef RA_TUNE_KV_RB
 #define RA_TUNE_KV_RB 2
 #endif
@@ -639,13 +642,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s) {
     const bool ext = a.f.anchor > 0 || a.f.q_seg != nullptr;
     const dim3 blk(kKvWaves * 64);
     if (d == 128 && ext)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2, true>), dim3(grid), blk, 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, (RA_TUNE_KV_RB < 2 ? RA_TUNE_KV_RB : 2), RA_TUNE_KV_NS, true>), dim3(grid), blk, 0, s, a);
     else if (d == 128)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, 2, false>), dim3(grid), blk, 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, RA_TUNE_KV_RB, RA_TUNE_KV_NS, false>), dim3(grid), blk, 0, s, a);
     else if (ext)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2, true>), dim3(grid), blk, 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, (RA_TUNE_KV_RB < 2 ? RA_TUNE_KV_RB : 2), RA_TUNE_KV_NS, true>), dim3(grid), blk, 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, 2, false>), dim3(grid), blk, 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, RA_TUNE_KV_RB, RA_TUNE_KV_NS, false>), dim3(grid), blk, 0, s, a);
     return hipGetLastError();
 }
 
