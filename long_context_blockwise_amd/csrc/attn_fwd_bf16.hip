@@ -473,6 +473,11 @@ void fwd_bf16_kernel(const FwdArgs a) {
 // these partial scores through LDS and adds them (the sum is commutative, so
 // both waves hold bitwise the same scores and run the same softmax), and each
 // wave multiplies the probabilities into its half of O.
+//
+// The partial scores of tile j+1 are computed and published in the iteration
+// that finishes tile j, so one barrier per tile both publishes them and
+// frees the tile buffers: K runs one tile ahead of V, each with two LDS
+// buffers, and the partial scores have two buffers of their own.
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NRB>
 struct CfgHalf : Cfg<D, BN, 2 * NRB, 1> {
@@ -481,16 +486,36 @@ struct CfgHalf : Cfg<D, BN, 2 * NRB, 1> {
     static constexpr int DBH = D / 64;   // 32-wide O^T blocks of a half of d_v
 };
 
-template <int D, int BN, int NRB, int NS>
+template <int D, int BN, int NRB>
 __global__ __launch_bounds__(NRB * 128) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_half_kernel(const FwdArgs a) {
     using C = CfgHalf<D, BN, NRB>;
     static_assert(C::KB == 1, "one 32-key block per tile");
     static_assert((D / 16) % C::SWB == 0, "each half of a row covers whole swizzle windows");
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
-    RA_STAGE_ARRAYS(NS, C::TILE)
-    // partial scores of each wave: [row block][half][4 x 64 lanes] of f32x4
-    __shared__ __attribute__((aligned(16))) f32x4 xs[NRB][2][4 * 64];
+    constexpr int LPT = C::LOADS_PER_WAVE;  // loads of one K (or V) tile per wave
+    // K and V tiles in arrays of their own, two of each: iteration j reads K
+    // tile j+1 and V tile j and loads K tile j+2 and V tile j+1
+    __shared__ __attribute__((aligned(1024))) char ks0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char ks1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char vs1[C::TILE];
+    // partial scores of each wave for two tiles, [row block][half][4 x 64
+    // lanes] of f32x4 per tile parity: two arrays, so the compiler can tell
+    // their accesses from the loads in flight into the tile buffers
+    __shared__ __attribute__((aligned(16))) f32x4 xs0[NRB][2][4 * 64];
+    __shared__ __attribute__((aligned(16))) f32x4 xs1[NRB][2][4 * 64];
+    auto kbuf = [&](auto u) -> char * {
+        if constexpr (decltype(u)::value % 2 == 0) return ks0;
+        else return ks1;
+    };
+    auto vbuf = [&](auto u) -> char * {
+        if constexpr (decltype(u)::value % 2 == 0) return vs0;
+        else return vs1;
+    };
+    auto xsb = [&](auto u) -> f32x4 (*)[2][4 * 64] {
+        if constexpr (decltype(u)::value % 2 == 0) return xs0;
+        else return xs1;
+    };
 
     const int lane = threadIdx.x & 63, w = wave_index();
     const int rb = w >> 1, hf = w & 1;
@@ -513,8 +538,6 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
     // byte offset of this wave's half of every K and V row: D/2 bf16 values,
     // whole swizzle windows, so the per-lane addresses carry over unchanged
     const int half_off = hf * D;
-    f32x4 *xs_mine = xs[rb][hf];
-    const f32x4 *xs_other = xs[rb][hf ^ 1];
 
     int c_begin = 0, c_end = a.n_chunks, sub = 0;
     if (a.split_mode) {
@@ -530,56 +553,68 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
-        auto issue = [&](auto u, int t) {
+        // Tiles past the end load nothing and zero-fill their buffer, so
+        // every iteration issues the same loads and the compiler's own waits
+        // for the buffers a phase reads stay partial.
+        auto tile_k0 = [&](int t) {
             const int64_t k0 = kbeg + (int64_t)t * BN;
-            load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
-            load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+            return k0 < kend ? k0 : kend;
         };
-        auto wait_for = [&](int need, int last) {
-            const int after = last - need;
-            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
-        };
-
-        tile_barrier();  // the previous chunk's tiles are no longer read
-        const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
-        for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
-        wait_for(0, pre - 1);
-        for_tiles<NS>(ntiles, [&](auto u, int it) {
-            constexpr int U = decltype(u)::value;
-            if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
-            const int64_t k0 = kbeg + (int64_t)it * BN;
-            // Tiles no row of the block sees (at most the last of a diagonal
-            // chunk) are computed and masked like the others: a branch around
-            // them would join two copies of O, and the compiler would copy the
-            // 128 O registers out of the AGPRs on every tile.
-            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
-            f32x16 s[1];
+        auto load_k = [&](auto u, int t) { load_tile<C>(kbase, a.k_ss, tile_k0(t), kend, kbuf(u), w, lane); };
+        auto load_v = [&](auto u, int t) { load_tile<C>(vbase, a.v_ss, tile_k0(t), kend, vbuf(u), w, lane); };
+        // this wave's partial scores (its half of d_qk) of the tile in K
+        // buffer u, kept in sp and published to the partner wave in xsb(u)
+        auto partial = [&](auto u, f32x16 &sp) {
+            f32x16 s1[1];
             if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-            scores<C>(kst(u) + half_off, kaddr, qf, s);
+            scores<C>(kbuf(u) + half_off, kaddr, qf, s1);
             if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4)
-                xs_mine[i4 * 64 + lane] = f32x4{s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]};
-            tile_barrier();  // partial scores visible to the partner wave
+                xsb(u)[rb][hf][i4 * 64 + lane] = f32x4{s1[0][4 * i4], s1[0][4 * i4 + 1], s1[0][4 * i4 + 2], s1[0][4 * i4 + 3]};
+            sp = s1[0];
+        };
+
+        // prologue: K and V of tile 0, K of tile 1; partial scores of tile 0
+        tile_barrier();  // the previous chunk's tiles and partial scores are no longer read
+        load_k(ic<0>{}, 0);
+        load_v(ic<0>{}, 0);
+        load_k(ic<1>{}, 1);
+        wait_tiles_in_flight<LPT>(0);
+        f32x16 sp[2];  // this wave's partial scores by tile parity
+        partial(ic<0>{}, sp[0]);
+        tile_barrier();  // partial scores of tile 0 published; K tile 0 read
+        for_tiles<2>(ntiles, [&](auto u, int j) {
+            constexpr int U = decltype(u)::value;
+            load_k(ic<U>{}, j + 2);
+            load_v(ic<U ^ 1>{}, j + 1);
+            // scores of tile j: this wave's part plus the partner's (addition
+            // commutes, so both waves hold the same scores bitwise)
+            f32x16 s[1];
+            s[0] = sp[U];
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 o = xs_other[i4 * 64 + lane];
+                const f32x4 o = xsb(u)[rb][hf ^ 1][i4 * 64 + lane];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s[0][4 * i4 + j] += o[j];
+                for (int jj = 0; jj < 4; ++jj) s[0][4 * i4 + jj] += o[jj];
             }
+            // every tile of the range is computed: tiles no row of the block
+            // sees (at most the last of a diagonal chunk) are masked to zero
+            // probabilities, since a branch around them would join two copies
+            // of O and the compiler would copy O out of the AGPRs on every tile
+            const int64_t k0 = kbeg + (int64_t)j * BN;
+            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
             if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
             update_max_agpr<C>(s, c2, m_run, m_true, lsum, oacc);
+            // partial scores of tile j+1 (after the last tile: of a zero-filled
+            // buffer, never read) while the probabilities of tile j are formed
+            partial(ic<U ^ 1>{}, sp[U ^ 1]);
             bf16x8 pf[2];
             probabilities<C>(s, c2, m_run, lsum, pf);
             if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-            accumulate_pv<C>(vst(u) + half_off, vaddr, pf, oacc);
+            accumulate_pv<C>(vbuf(u) + half_off, vaddr, pf, oacc);
             if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-            // the next tile's partial scores overwrite xs only after this barrier
-            // (after a chunk's last tile: the barrier at the next chunk's start)
-            if (it + 1 < ntiles) {
-                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-                wait_for(it + 1, last);
-            }
+            wait_tiles_in_flight<LPT>(0);  // K tile j+2, V tile j+1 and the partial scores of j+1
         });
     }
 
@@ -875,7 +910,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t
                 fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, true>, a, s);
         return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(
             fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, false>, a, s);
-    case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2, 2>, a, s);
+    case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2>, a, s);
     default: return hipErrorInvalidValue;
     }
 }
