@@ -599,8 +599,11 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         const std::vector<int> &L = launches[li];
         const bool staged = pl.stage && li > 0;
         if (pl.stage && li + 1 < nl && li >= 1) {
-            // refill the buffer of step li-1 (now li+1) once step li-1 is done
-            if ((e = hipStreamWaitEvent(ctx->side, ctx->freed[(li + 1) & 1], 0)) != hipSuccess)
+            // refill the buffer of step li-1 (now li+1) once step li-1 is done;
+            // step 0 reads its chunk in place, so at li = 1 the buffer is unused
+            // (and its event was not recorded by this call: waiting on it would
+            // tie the side stream to earlier work, which graph capture rejects)
+            if (li >= 2 && (e = hipStreamWaitEvent(ctx->side, ctx->freed[(li + 1) & 1], 0)) != hipSuccess)
                 return hip_fail(e, "side wait");
             if ((e = stage_copy(li + 1)) != hipSuccess) return hip_fail(e, "staging copy");
         }
