@@ -53,7 +53,8 @@ MEASURED_TRAFFIC = {
 }
 
 HEADLINE = "prefill_bf16_h32_d128"
-SECONDARY = "decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,bwd:prefill_bf16_h32_d128"
+SECONDARY = ("decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,bwd:prefill_bf16_h32_d128,"
+             "local_w4096_s4096_h32_d128,docs4096_h32_d128")
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -92,6 +93,50 @@ def visible_pairs_fast(wl):
     return total
 
 
+def masked(wl):
+    return bool(wl.window or wl.anchor or wl.doc_mean)
+
+
+def visible_pairs(wl, rows=None):
+    """Unmasked (query, key) pairs of one query head, summed over batches,
+    for the given rows (default all).  A key at position k is visible to the
+    query at p when it carries p's segment label (packed documents) and
+    either is one of p's anchors (A - 1, A, A + S with A = S floor(p / S))
+    or passes the causal rule (k <= p) and the window (|p - k| <= W)."""
+    if not masked(wl):
+        per = visible_pairs_fast(wl) if rows is None else visible_pairs_per_head(wl, rows)
+        return per * wl.B
+    import numpy as np
+
+    from long_context_blockwise_amd import inputs
+
+    rows = np.arange(wl.Lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    N = sum(wl.lens())  # chunks are contiguous: key position = index over all chunks
+    p = wl.q_offset + rows
+    W, S = wl.window, wl.anchor
+    lo = np.maximum(0, p - W) if W else np.zeros_like(p)
+    if wl.causal:
+        hi = np.minimum(p, N - 1)
+    else:
+        hi = np.minimum(p + W, N - 1) if W else np.full_like(p, N - 1)
+    q_seg, k_segs = inputs.segment_labels(wl)
+    total = 0
+    for b in range(wl.B):
+        if q_seg is not None:  # packed documents: labels never decrease along the sequence
+            lab = np.concatenate([k[b].numpy() for k in k_segs])
+            ql = q_seg[b].numpy()[rows]
+            first, last = np.searchsorted(lab, ql, "left"), np.searchsorted(lab, ql, "right")
+        else:
+            first, last = np.zeros_like(p), np.full_like(p, N)
+        cnt = np.maximum(0, np.minimum(hi, last - 1) - np.maximum(lo, first) + 1)
+        if S:
+            A = p // S * S
+            for k in (A - 1, A, A + S):
+                cnt = cnt + ((k >= 0) & (k < N) & (k >= first) & (k < last) & ~((k >= lo) & (k <= hi)))
+        total += int(cnt.sum())
+    return total
+
+
 def kernel_digest():
     import hashlib
 
@@ -110,7 +155,7 @@ def measured_traffic(name):
 
 
 def algorithmic(wl):
-    pairs = visible_pairs_fast(wl) * wl.B * wl.Hq
+    pairs = visible_pairs(wl) * wl.Hq
     flops = pairs * 2 * (wl.d_qk + wl.d_v)
     es = 2 if wl.dtype == "bf16" else 4
     if wl.kv_dtype == "fp8":  # 1-byte codes plus one exponent byte per 64 tokens for K and for V
@@ -145,12 +190,16 @@ class WorkloadRun:
             self.order = ra.ring_attn_ring_order(dev_index, wl.P)
             self.flags = ra.RA_FLAG_STAGE
         self.chunks = self.x.chunks(self.order)
+        q_seg, k_segs = inputs.segment_labels(wl, device)
+        # local window, anchors and segment labels of the workload (if any)
+        self.masks = dict(window=wl.window, anchor=wl.anchor, q_seg=q_seg,
+                          k_segs=None if k_segs is None else [k_segs[c] for c in self.order])
         self.out = torch.empty((wl.B, wl.Lq, wl.Hq, wl.d_v), device=device, dtype=wl.torch_dtype)
-        ws = ra.ring_attn_workspace_size(self.x.q, self.chunks, wl.causal, wl.q_offset, self.flags)
+        ws = ra.ring_attn_workspace_size(self.x.q, self.chunks, wl.causal, wl.q_offset, self.flags, **self.masks)
         self.ws = torch.empty(max(ws, 1), device=device, dtype=torch.uint8)
         self.ctx = ra.RingAttnContext(torch.device(device).index or 0)
         cls = ra.ring_attn_plan(wl.Lq, wl.q_offset, wl.causal, [c[2] for c in self.chunks],
-                                [c[0].shape[1] for c in self.chunks])
+                                [c[0].shape[1] for c in self.chunks], window=wl.window, anchor=wl.anchor)
         computed = sum(1 for c in cls if c != ra.RA_CHUNK_SKIP)
         # kernel launches of the dominant kernel per step
         self.launches = 1 if self.decode else computed
@@ -158,7 +207,7 @@ class WorkloadRun:
 
     def step(self):
         self.ra.ring_attn_fwd(self.x.q, self.chunks, self.wl.causal, self.wl.q_offset,
-                              flags=self.flags, out=self.out, ctx=self.ctx, workspace=self.ws)
+                              flags=self.flags, out=self.out, ctx=self.ctx, workspace=self.ws, **self.masks)
 
     def time(self, steps, warmup):
         torch = self.torch
@@ -195,6 +244,10 @@ class WorkloadRun:
             roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
                         frac=round(achieved / peak, 4), traffic=measured_traffic(wl.name))
             metric, value, unit = "causal attn fwd TFLOP/s (% MFMA peak) per GPU", tflops, "TFLOP/s"
+            if wl.window or wl.anchor:
+                metric = "local-window + anchor attn fwd TFLOP/s over visible pairs per GPU"
+            elif wl.doc_mean:
+                metric = "packed-document attn fwd TFLOP/s over visible pairs per GPU"
         return dict(workload=wl.name, metric=metric, value=round(value, 2), unit=unit,
                     ms_per_step=round(sec_per_step * 1e3, 4),
                     tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1),
@@ -220,7 +273,7 @@ class BackwardRun(WorkloadRun):
                        torch.empty(c[1].shape, device=device, dtype=torch.float32)) for c in self.chunks]
         self.bws = torch.empty(max(ra.ring_attn_bwd_workspace_size(self.x.q, self.chunks), 1), device=device,
                                dtype=torch.uint8)
-        pairs = visible_pairs_fast(wl) * wl.B * wl.Hq
+        pairs = visible_pairs(wl) * wl.Hq
         # S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q per visible pair
         self.flops = pairs * 2 * (3 * wl.d_qk + 2 * wl.d_v)
         torch.cuda.synchronize()
@@ -266,7 +319,7 @@ def cpu_baseline(name, budget_s=20.0):
         t_total += dt
         spent += dt
         n *= 2
-    pairs = visible_pairs_per_head(wl, done_rows) * wl.B * wl.Hq
+    pairs = visible_pairs(wl, done_rows) * wl.Hq
     flops = pairs * 2 * (wl.d_qk + wl.d_v)
     return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=oracle.threads(),
                 kind="oracle",

@@ -294,17 +294,19 @@ __device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const
 // ---------------------------------------------------------------------------
 // The attention kernel: one tile at a time (query-chunk prefill and split-KV decoding)
 // ---------------------------------------------------------------------------
-// EXT instantiations add anchor tokens and segment labels: each stage then
-// also holds 64 key labels per wave (after the K tile), and up to five extra
-// tiles hold anchors outside the window's range.
-template <int D, int BN, int NW, int KSPLIT, int NS, bool EXT>
+// EXT instantiations add anchor tokens (EXT >= 1) and segment labels
+// (EXT = 2): up to five extra tiles hold anchors outside the window's range,
+// and with labels each stage also holds 64 key labels per wave (after the K
+// tile).
+template <int D, int BN, int NW, int KSPLIT, int NS, int EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (EXT ? 1 : 0);
-    constexpr int LABB = EXT ? NW * 256 : 0;  // bytes of key labels per stage
+    constexpr bool ANC = EXT >= 1, LAB = EXT == 2;
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (LAB ? 1 : 0);
+    constexpr int LABB = LAB ? NW * 256 : 0;  // bytes of key labels per stage
     RA_STAGE_ARRAYS(NS, C::TILE + LABB)
-    static_assert(!EXT || C::KW <= 64, "a wave's labels are 64 dwords");
+    static_assert(!LAB || C::KW <= 64, "a wave's labels are 64 dwords");
     // merge scratch of the key-split waves: slot s spans tile buffers 2s, 2s+1
     static_assert(KSPLIT == 1 || (C::ROWW * (KSPLIT - 1) <= 2 && (16 * C::DB + 2) * 64 * 4 <= 2 * C::TILE),
                   "merge scratch must fit in the tile buffers");
@@ -329,9 +331,13 @@ void fwd_bf16_kernel(const FwdArgs a) {
     v_addrs<C>(wk * C::KW, lane, vaddr);
     int ql = 0, lab_L = 0;  // the row's segment label; the wave's common one
     bool lab_uniform = true;
-    if constexpr (EXT) {
+    int lab_lo = 0, lab_hi = 0;  // the labels of the workgroup's rows lie in [lab_lo, lab_hi]
+    __shared__ int red[LAB ? 2 * NW : 1];
+    if constexpr (LAB) {
         if (a.q_seg && row.ok) ql = a.q_seg[wt.b * a.Lq + row.t];
         wave_label(ql, row.ok, lab_L, lab_uniform);
+        if (a.q_seg)  // uniform
+            wg_min_max<NW>(row.ok ? ql : 2147483647, row.ok ? ql : -2147483647 - 1, red, w, lane, lab_lo, lab_hi);
     }
 
     int c_begin = 0, c_end = a.n_chunks, sub = 0;
@@ -346,28 +352,37 @@ void fwd_bf16_kernel(const FwdArgs a) {
         TileRange tr;
         int64_t kbeg, kend;
         int ntiles;
-        if constexpr (EXT) {
-            if (!chunk_tiles<EXT>(a, wt, c, sub, BN, tr)) continue;  // uniform
+        if constexpr (ANC) {
+            int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
+            if (LAB && a.q_seg && a.chunks[c].kseg) {  // uniform
+                const int64_t k0 = a.split_mode ? sub * a.sub_len : 0;
+                const int64_t len = a.chunks[c].len;
+                const int64_t k1 = a.split_mode && k0 + a.sub_len < len ? k0 + a.sub_len : len;
+                label_key_span<NW>(a.chunks[c].kseg + wt.b * len, k0, k1, lab_lo, lab_hi, red, w, lane, kf, kl);
+                if (kl < kf) continue;  // no key of the chunk carries a label of the rows
+            }
+            if (!chunk_tiles<ANC>(a, wt, c, sub, BN, tr, kf, kl)) continue;  // uniform
             kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
+            if (ntiles == 0) continue;
         } else {
             if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         }
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         Anchors an{kNoKey, kNoKey, kNoKey};
-        if constexpr (EXT) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
-        const int32_t *kseg = EXT && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
+        if constexpr (ANC) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
+        const int32_t *kseg = LAB && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto tile_start = [&](int t) -> int64_t {
-            if constexpr (EXT) return tr.start(t, BN);
+            if constexpr (ANC) return tr.start(t, BN);
             else return kbeg + (int64_t)t * BN;
         };
         auto issue = [&](auto u, int t) {
             const int64_t k0 = tile_start(t);
             load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
             load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
-            if constexpr (EXT) load_labels(kseg, k0 + wk * C::KW, kend, kst(u) + C::TILE + 256 * w, lane);
+            if constexpr (LAB) load_labels(kseg, k0 + wk * C::KW, kend, kst(u) + C::TILE + 256 * w, lane);
         };
         auto wait_for = [&](int need, int last) {
             const int after = last - need;
@@ -387,8 +402,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
             bool skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
             bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
             const char *lab = kst(u) + C::TILE + 256 * w;
-            if constexpr (EXT) {
+            if constexpr (ANC) {
                 if (skip && tile_has_anchor(a, ch.start, wk0, C::KW, wv_tlo, wv_thi)) skip = false;
+            }
+            if constexpr (LAB) {
                 bool lall, lnone;
                 label_tile(lab, C::KW, kend - wk0, lane, lab_L, lab_uniform, lall, lnone);
                 skip = skip || lnone;
@@ -400,7 +417,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 scores<C>(kst(u), kaddr, qf, s);
                 prio_valu();
                 if (!full) {
-                    if constexpr (EXT) mask_scores_ext<C>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
+                    if constexpr (ANC) mask_scores_ext<C, LAB>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
                     else mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
                 }
                 update_max<C>(s, c2, m_run, m_true, lsum, oacc);
@@ -894,22 +911,21 @@ hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s) {
     return launch<fp8kv::C>(fwd_fp8kv_kernel<2>, a, s);
 }
 
+// The kernel for the call's masks: plain, with anchors, with labels (and anchors).
+template <int D, int BN, int NW, int KS, int NS>
+hipError_t launch_masked(const FwdArgs &a, hipStream_t s) {
+    using C = Cfg<D, BN, NW, KS>;
+    if (a.q_seg) return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 2>, a, s);
+    if (a.anchor > 0) return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 1>, a, s);
+    return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 0>, a, s);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t s) {
-    const bool ext = a.anchor > 0 || a.q_seg != nullptr;  // anchors / labels: d = 64, 128 only
-    switch (d) {
-    case 64:
-        if (ext) return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2, true>, a, s);
-        return launch<Cfg<64, 64, 4, 1>>(fwd_bf16_kernel<64, 64, 4, 1, 2, false>, a, s);
+    switch (d) {  // anchors / labels: d = 64, 128 only
+    case 64: return launch_masked<64, 64, 4, 1, 2>(a, s);
     case 128:
-        if (split_mode) {
-            if (ext) return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2, true>, a, s);
-            return launch<Cfg<128, 64, 4, 2>>(fwd_bf16_kernel<128, 64, 4, 2, 2, false>, a, s);
-        }
-        if (ext)
-            return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(
-                fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, true>, a, s);
-        return launch<Cfg<128, RA_TUNE_BN128, 4, 1>>(
-            fwd_bf16_kernel<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS, false>, a, s);
+        if (split_mode) return launch_masked<128, 64, 4, 2, 2>(a, s);
+        return launch_masked<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>(a, s);
     case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2>, a, s);
     default: return hipErrorInvalidValue;
     }

@@ -389,9 +389,9 @@ __device__ inline bool tile_has_anchor(const FwdArgs &a, int64_t cstart, int64_t
 }
 
 // mask_scores with anchors and labels: a key is visible iff (it lies in
-// [lo, hi) or is one of the row's anchors) and its label (the wave's labels
-// of the tile, at lab) equals the row's label ql.
-template <class C>
+// [lo, hi) or is one of the row's anchors) and (LAB) its label (the wave's
+// labels of the tile, at lab) equals the row's label ql.
+template <class C, bool LAB = true>
 __device__ inline void mask_scores_ext(f32x16 (&s)[C::KB], VisRange v, Anchors an, int rel, int g, const char *lab,
                                        int ql) {
     const int off = rel + 4 * g;  // key index of element (0, 0) minus the lane-independent part
@@ -400,18 +400,20 @@ __device__ inline void mask_scores_ext(f32x16 (&s)[C::KB], VisRange v, Anchors a
     const int a0 = shift(an.a0), a1 = shift(an.a1), a2 = shift(an.a2);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-        int lk[16];
+        int lk[16] = {};
+        if constexpr (LAB) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const i32x4 x = *(const i32x4 *)(lab + 4 * (32 * kb + 8 * j + 4 * g));
+            for (int j = 0; j < 4; ++j) {
+                const i32x4 x = *(const i32x4 *)(lab + 4 * (32 * kb + 8 * j + 4 * g));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) lk[4 * j + e] = x[e];
+                for (int e = 0; e < 4; ++e) lk[4 * j + e] = x[e];
+            }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
             const bool in = (key >= lo && key < hi) || key == a0 || key == a1 || key == a2;
-            if (!in || lk[i] != ql) s[kb][i] = kNegInf;
+            if (!in || (LAB && lk[i] != ql)) s[kb][i] = kNegInf;
         }
     }
 }
@@ -422,6 +424,49 @@ __device__ inline void wave_label(int ql, bool ok, int &L, bool &uniform) {
     const int first = okm ? __builtin_ctzll(okm) : 0;
     L = __builtin_amdgcn_readlane(ql, first);
     uniform = __builtin_amdgcn_ballot_w64(ok && ql != L) == 0;
+}
+
+// Minimum and maximum of x over the workgroup's NW waves (red: 2 NW ints of
+// LDS; every wave must call it).
+template <int NW>
+__device__ inline void wg_min_max(int lo, int hi, int *red, int w, int lane, int &gmin, int &gmax) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+    }
+    if (lane == 0) red[w] = lo, red[NW + w] = hi;
+    __syncthreads();
+    gmin = red[0], gmax = red[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        gmin = red[i] < gmin ? red[i] : gmin;
+        gmax = red[NW + i] > gmax ? red[NW + i] : gmax;
+    }
+    __syncthreads();  // red may be written again
+}
+
+// First and last key in [k0, k1) of a chunk (labels kseg) whose label lies
+// in [lo, hi], over the workgroup's NW waves: kl < kf when there is none.
+// With packed documents (labels that never decrease) this is the span of
+// the rows' documents.
+template <int NW>
+__device__ inline void label_key_span(const int32_t *kseg, int64_t k0, int64_t k1, int lo, int hi, int *red, int w,
+                                      int lane, int64_t &kf, int64_t &kl) {
+    int first = 2147483647, last = -1;
+    for (int64_t i = k0 + (int64_t)threadIdx.x; i < k1; i += NW * 64) {
+        const int L = kseg[i];
+        if (L >= lo && L <= hi) {
+            const int r = (int)(i - k0);
+            first = r < first ? r : first;
+            last = r;
+        }
+    }
+    int f, l;
+    wg_min_max<NW>(first, last, red, w, lane, f, l);
+    kf = l < 0 ? 1 : k0 + f;
+    kl = l < 0 ? 0 : k0 + l;
 }
 
 // Label test of a wave's n (<= 64) keys of a tile (label of key `lane` at
@@ -522,16 +567,32 @@ __device__ inline bool chunk_range(const FwdArgs &a, const WorkTile &wt, int c, 
 struct TileRange {
     int64_t kbase, kbeg, kend;  // first key of the chunk or sub-range, first main tile, end of keys
     int nmain, ntot;
-    int64_t e0, e1, e2, e3, e4;  // first keys of the extra tiles
+    // first keys of the anchor tiles outside the main range: six fixed
+    // candidate slots and a mask of the used ones, read with constant
+    // indices only (a compacted list indexed by the tile counter would live
+    // in scratch memory, and every scratch load waits for the tile loads in
+    // flight)
+    int64_t cand[6];
+    unsigned used;
     __device__ int64_t start(int it, int bn) const {
         if (it < nmain) return kbeg + (int64_t)it * bn;
-        const int j = it - nmain;
-        return j == 0 ? e0 : j == 1 ? e1 : j == 2 ? e2 : j == 3 ? e3 : e4;
+        int j = it - nmain;
+        int64_t r = 0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int u = (used >> i) & 1;
+            if (u && j == 0) r = cand[i];
+            j -= u;
+        }
+        return r;
     }
 };
 
+// (EXT) Keys outside [kf, kl] carry no label of the workgroup's rows: the
+// main tiles and the anchor tiles are cut to that range.
 template <bool EXT>
-__device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, int sub, int bn, TileRange &tr) {
+__device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, int sub, int bn, TileRange &tr,
+                                   int64_t kf = 0, int64_t kl = INT64_MAX) {
     const ChunkArg &ch = a.chunks[c];
     tr.kbase = a.split_mode ? sub * a.sub_len : 0;
     int64_t kbeg, kend;
@@ -541,32 +602,40 @@ __device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, 
         kbeg = tr.kbase;
         kend = a.split_mode ? (tr.kbase + a.sub_len < ch.len ? tr.kbase + a.sub_len : ch.len) : ch.len;
     }
+    if (EXT && nmain > 0) {  // main tiles cut to [kf, kl], on the same tile grid
+        const int64_t mend = kbeg + (int64_t)nmain * bn;
+        const int64_t end = kl < mend ? kl + 1 : mend;
+        if (kf > kbeg) kbeg += (kf - kbeg) / bn * bn;
+        nmain = end > kbeg ? (int)((end - kbeg + bn - 1) / bn) : 0;
+    }
     tr.kbeg = kbeg, tr.kend = kend, tr.nmain = nmain, tr.ntot = nmain;
-    tr.e0 = tr.e1 = tr.e2 = tr.e3 = tr.e4 = 0;
+    tr.used = 0;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) tr.cand[i] = 0;
     if constexpr (EXT) {
         if (a.anchor > 0 && kend > tr.kbase) {
             const int64_t S = a.anchor;
             const int64_t A0 = (a.q_offset + wt.wg_tlo) / S * S, A1 = (a.q_offset + wt.wg_thi) / S * S;
-            if (A1 - A0 > S) {  // every tile of the chunk
-                tr.kbeg = tr.kbase;
-                tr.nmain = tr.ntot = (int)((kend - tr.kbase + bn - 1) / bn);
+            if (A1 - A0 > S) {  // every tile of the chunk (within [kf, kl])
+                int64_t b0 = tr.kbase;
+                const int64_t e = kl < kend ? kl + 1 : kend;
+                if (kf > b0) b0 += (kf - b0) / bn * bn;
+                tr.kbeg = b0;
+                tr.nmain = tr.ntot = e > b0 ? (int)((e - b0 + bn - 1) / bn) : 0;
             } else {
-                const int64_t cand[6] = {A0 - 1, A0, A0 + S, A1 - 1, A1, A1 + S};
+                const int64_t pos[6] = {A0 - 1, A0, A0 + S, A1 - 1, A1, A1 + S};
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
-                    const int64_t x = cand[i] - ch.start;
-                    if (x < tr.kbase || x >= kend) continue;
+                    const int64_t x = pos[i] - ch.start;
+                    if (x < tr.kbase || x >= kend || x < kf || x > kl) continue;
                     const int64_t ts = tr.kbase + (x - tr.kbase) / bn * bn;
                     if (ts >= tr.kbeg && ts < tr.kbeg + (int64_t)tr.nmain * bn) continue;
-                    const int ne = tr.ntot - tr.nmain;
-                    if ((ne > 0 && tr.e0 == ts) || (ne > 1 && tr.e1 == ts) || (ne > 2 && tr.e2 == ts) ||
-                        (ne > 3 && tr.e3 == ts))
-                        continue;
-                    if (ne == 0) tr.e0 = ts;
-                    else if (ne == 1) tr.e1 = ts;
-                    else if (ne == 2) tr.e2 = ts;
-                    else if (ne == 3) tr.e3 = ts;
-                    else tr.e4 = ts;
+                    bool dup = false;  // the tile of an earlier candidate
+#pragma unroll
+                    for (int j = 0; j < i; ++j) dup = dup || (((tr.used >> j) & 1) && tr.cand[j] == ts);
+                    if (dup) continue;
+                    tr.cand[i] = ts;
+                    tr.used |= 1u << i;
                     ++tr.ntot;
                 }
             }

@@ -18,6 +18,11 @@ Workloads (one device's share of the ring, shapes from the pages' settings):
   tokens as 32 chunks of 32768; the last query chunk, causal; N(0,1)*0.5.
 * ``mla_h16_d512``: 16 query heads sharing one 512-wide KV head, bf16, 131072
   tokens as 8 chunks of 16384; query chunk 7, causal; N(0,1)*4/sqrt(512).
+* ``local_w4096_s4096_h32_d128``: the prefill share with a local window (a
+  query at p sees keys p - 4096 .. p) and anchor tokens every 4096 positions.
+* ``docs4096_h32_d128``: the prefill share over packed documents of seeded
+  lengths uniform in 1 .. 8192 (mean 4096), with segment labels: a query
+  sees the earlier keys of its own document.
 * ``decode_b4_gqa32x8_cache1m``: 4 sequences, 32 query / 8 KV heads, d=128,
   bf16, a 1,048,576-token KV cache in 64 chunks of 16384; 16 new query tokens
   at cache_idx = 1,048,560 (their K/V are the cache's last 16 slots), causal.
@@ -62,6 +67,9 @@ class Workload:
     # explicit per-chunk lengths (ragged tails); None means all chunk_len
     chunk_lens: Optional[Tuple[int, ...]] = field(default=None)
     kv_dtype: Optional[str] = None  # None: same as dtype; "fp8": 8-bit KV cache
+    window: int = 0     # local window half-width in tokens (0: none)
+    anchor: int = 0     # anchor stride in tokens (0: none)
+    doc_mean: int = 0   # packed documents of this mean length carry segment labels (0: none)
 
     @property
     def torch_dtype(self):
@@ -97,6 +105,13 @@ WORKLOADS = {
                              dtype="bf16", chunk_len=16384, P=8, Lq=16384,
                              q_offset=7 * 16384, causal=True, std=4.0 / 512 ** 0.5,
                              seed=4),
+    "local_w4096_s4096_h32_d128": Workload("local_w4096_s4096_h32_d128", B=1, Hq=32, Hkv=32,
+                                           d_qk=128, d_v=128, dtype="bf16", chunk_len=8192,
+                                           P=4, Lq=8192, q_offset=3 * 8192, causal=True,
+                                           std=0.5, seed=2, window=4096, anchor=4096),
+    "docs4096_h32_d128": Workload("docs4096_h32_d128", B=1, Hq=32, Hkv=32, d_qk=128, d_v=128,
+                                  dtype="bf16", chunk_len=8192, P=4, Lq=8192, q_offset=3 * 8192,
+                                  causal=True, std=0.5, seed=2, doc_mean=4096),
     "decode_b4_gqa32x8_cache1m": Workload("decode_b4_gqa32x8_cache1m", B=4, Hq=32,
                                           Hkv=8, d_qk=128, d_v=128, dtype="bf16",
                                           chunk_len=16384, P=64, Lq=16,
@@ -186,6 +201,19 @@ def packed_labels(B: int, n: int, mean_doc: int, seed: int, device="cpu") -> tor
             pos += L
             doc += 1
     return out.to(device)
+
+
+def segment_labels(wl: Workload, device="cpu"):
+    """``(q_seg [B, Lq], [k_seg_c [B, len_c] for each chunk c])`` of a
+    workload with packed documents (``packed_labels`` over all its tokens),
+    or ``(None, None)``."""
+    if not wl.doc_mean:
+        return None, None
+    total = sum(wl.lens())
+    lab = packed_labels(wl.B, max(total, wl.q_offset + wl.Lq), wl.doc_mean, wl.seed, device)
+    q_seg = lab[:, wl.q_offset:wl.q_offset + wl.Lq].contiguous()
+    k_segs = [lab[:, s:s + n].contiguous() for s, n in zip(wl.starts(), wl.lens())]
+    return q_seg, k_segs
 
 
 def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:

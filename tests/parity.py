@@ -71,10 +71,13 @@ def kv_slice(chunks, hk):
     return [(k[:, :, hk:hk + 1], v[:, :, hk:hk + 1], s) for (k, v, s) in chunks]
 
 
-def sampled_reference(q, chunks, q_offset, causal, rows, kv_heads, batches=None):
+def sampled_reference(q, chunks, q_offset, causal, rows, kv_heads, batches=None, window=0, anchor=0,
+                      q_seg=None, k_segs=None):
     """Oracle values for the given rows, for the query heads of the given KV
     heads (and batches): returns {(b, hk): out [1, n_rows, G, d_v]}.  Slices
-    are cut on the device and only they are copied to the host."""
+    are cut on the device and only they are copied to the host.  Window,
+    anchors and segment labels (``q_seg [B, Lq]``, ``k_segs`` per chunk
+    ``[B, len]``) mask as in the oracle's attention."""
     B, _, Hq, _ = q.shape
     Hkv = chunks[0][0].shape[2]
     G = Hq // Hkv
@@ -89,7 +92,10 @@ def sampled_reference(q, chunks, q_offset, causal, rows, kv_heads, batches=None)
                 if len(c) == 5:  # 8-bit chunk: exponents [B, Hkv, nblk] of the same (batch, head)
                     cut += (c[3][b:b + 1, hk:hk + 1].cpu().contiguous(), c[4][b:b + 1, hk:hk + 1].cpu().contiguous())
                 cs.append(cut)
-            out, _ = oracle.attention(qs, cs, q_offset, causal, rows=rows)
+            qsb = None if q_seg is None else q_seg[b:b + 1].cpu().contiguous()
+            ksb = None if k_segs is None else [t[b:b + 1].cpu().contiguous() for t in k_segs]
+            out, _ = oracle.attention(qs, cs, q_offset, causal, rows=rows, window=window, anchor=anchor,
+                                      q_seg=qsb, k_segs=ksb)
             res[(b, hk)] = out
     return res
 

@@ -3,7 +3,8 @@ times (bench.WorkloadRun: staged ring for prefill shares, split-KV + merge
 for decoding), checked against the oracle on sampled outputs the oracle
 computes row by row: stratified query rows (one per tile plus tile and
 chunk boundaries) for a subset of (batch, KV head) groups, every query head
-of each group."""
+of each group.  The local-window and packed-document workloads carry their
+window, anchors and segment labels to both sides."""
 import os
 import sys
 
@@ -26,6 +27,8 @@ CASES = {
     "prefill_bf16_h32_d128": (512, list(range(0, 32, 3)), None),
     "ring_1m_gqa32x8_d128": (4096, [0, 5], None),
     "mla_h16_d512": (1024, [0], None),
+    "local_w4096_s4096_h32_d128": (512, list(range(1, 32, 5)), None),
+    "docs4096_h32_d128": (512, list(range(2, 32, 5)), None),
     "decode_b4_gqa32x8_cache1m": (1, [0, 7], [0, 3]),
     "decode_b4_gqa32x8_cache1m_fp8": (1, [0, 7], [0, 3]),
 }
@@ -45,7 +48,9 @@ def test_workload_full_size(name):
     else:
         rows = inputs.sample_rows(wl.Lq, tile=tile, seed=3,
                                   extra=(wl.Lq - 64, wl.Lq - 65, 8191, 8192, 16383, 16384))
-    ref = sampled_reference(run.x.q, run.x.chunks(), wl.q_offset, wl.causal, rows, kv_heads, batches)
+    q_seg, k_segs = inputs.segment_labels(wl)  # chunk index order, like run.x.chunks()
+    ref = sampled_reference(run.x.q, run.x.chunks(), wl.q_offset, wl.causal, rows, kv_heads, batches,
+                            window=wl.window, anchor=wl.anchor, q_seg=q_seg, k_segs=k_segs)
     G = wl.Hq // wl.Hkv
     got = np.concatenate([gather_sampled(run.out, rows, b, hk, G) for (b, hk) in ref])
     want = np.concatenate(list(ref.values()))
