@@ -2,9 +2,12 @@
 // computed with true fp32 products and sums on the vector ALUs (no reduced
 // precision anywhere, for callers that need fp32 accuracy).
 //
-// Each query row is owned by TPR = d/64 consecutive threads, each holding 64
-// of the row's query and output elements in registers; K/V tiles of 32 keys
-// are staged in LDS and read by all threads (broadcast reads).  The running
+// Each query row is owned by 16 consecutive threads: TPR = d/64 threads per
+// 64-wide slice of d times KS = 16/TPR key groups.  A thread holds 64 of the
+// row's query and output elements in registers and takes 32/KS of the keys of
+// every tile, with a running softmax state of its own; the key groups of a
+// row (lanes of one wave) merge their states at the end with lane shuffles.
+// K/V tiles of 32 keys are staged in LDS and read by all threads.  The running
 // softmax state follows the same online update as the bf16 path (page "Ring
 // Attention：百万 Token 上下文的秘密", §3.1 Flash Ring Attention: blockwise
 // attention per received KV chunk; §2.3: the state after all chunks equals
@@ -20,19 +23,22 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kThreads = 256;
-constexpr int kKeys = 32;  // keys per LDS tile
-constexpr int kSub = 8;    // keys per online-softmax update
+constexpr int kKeys = 32;     // keys per LDS tile
+constexpr int kRowLanes = 16;  // threads per query row
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
-    constexpr int TPR = D / 64;               // threads per query row
-    constexpr int RB = kThreads / TPR;        // rows per workgroup
+    constexpr int TPR = D / 64;               // threads per 64-wide slice set of a row
+    constexpr int KS = kRowLanes / TPR;       // key groups per row
+    constexpr int kSub = kKeys / KS;          // keys of a tile per thread
+    constexpr int RB = kThreads / kRowLanes;  // rows per workgroup
     __shared__ __attribute__((aligned(16))) float Ks[kKeys][D];
     __shared__ __attribute__((aligned(16))) float Vs[kKeys][D];
     __shared__ int Ls[kKeys];  // segment labels of the tile's keys (0 without labels)
 
     const int tid = threadIdx.x;
     const int part = tid % TPR;               // which 64-wide slice of d
+    const int kg = (tid / TPR) % KS;          // which keys of each tile
     const int nsplit = a.split_mode ? a.n_chunks * a.n_sub : 1;
     int lid = blockIdx.x;
     const int rt = lid % a.n_rowtiles;
@@ -43,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
     const int b = lid / a.Hkv;
 
     const int64_t Lq = a.Lq, Lq_pad = a.Lq_pad;
-    const int64_t prow = (int64_t)rt * RB + tid / TPR;
+    const int64_t prow = (int64_t)rt * RB + tid / kRowLanes;
     const int gq = (int)(prow / Lq_pad);
     const int64_t t = prow % Lq_pad;
     const bool row_ok = gq < a.G && t < Lq;
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
     }
     float m = kNegInf, l = 0.f;
     const int64_t srow = ((int64_t)b * Lq + t) * a.Hq + h;
-    if (a.load_state && row_ok) {
+    if (a.load_state && row_ok && kg == 0) {  // one key group carries the prior state
         m = a.m[srow] * kLog2e;
         l = a.l[srow];
         const float *op = a.O + srow * D + 64 * part;
@@ -124,7 +130,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
             if (tid < kKeys)
                 Ls[tid] = ch.kseg && k0 + tid < kend ? ch.kseg[(int64_t)b * ch.len + k0 + tid] : 0;
             __syncthreads();
-            for (int j0 = 0; j0 < kKeys; j0 += kSub) {
+            {
+                const int j0 = kg * kSub;
                 float s[kSub];
                 float smax = kNegInf;
 #pragma unroll
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
                     s[j] = vis ? acc * c2 : kNegInf;
                     smax = fmaxf(smax, s[j]);
                 }
-                if (smax == kNegInf) continue;  // nothing visible in these keys
+                if (smax == kNegInf) continue;  // nothing visible in these keys (skips to the next tile)
                 const float mn = fmaxf(m, smax);
                 const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mn);
                 l *= alpha;
@@ -164,7 +171,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs a) {
         }
     }
 
-    if (!row_ok) return;
+    // merge the key groups' states: lanes tid ^ (TPR << i) hold the same
+    // row and slice with other keys
+#pragma unroll
+    for (int x = TPR; x < kRowLanes; x <<= 1) {
+        const float m2 = __shfl_xor(m, x), l2 = __shfl_xor(l, x);
+        const float mn = fmaxf(m, m2);
+        const float a1 = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float a2 = m2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+        l = a1 * l + a2 * l2;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) o[e] = a1 * o[e] + a2 * __shfl_xor(o[e], x);
+        m = mn;
+    }
+    if (!row_ok || kg != 0) return;
     if (a.split_mode || a.store_state) {
         const int64_t slot_rows = (int64_t)a.B * Lq * a.Hq;
         float *mp = a.split_mode ? a.pm + (a.part_base + split) * slot_rows : a.m;
@@ -199,7 +219,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int fwd_f32_row_tile(int d) { return d == 64 || d == 128 ? kThreads / (d / 64) : 0; }
+int fwd_f32_row_tile(int d) { return d == 64 || d == 128 ? kThreads / kRowLanes : 0; }
 
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, hipStream_t s) {
     switch (d) {
