@@ -56,7 +56,7 @@ MEASURED_TRAFFIC = {
 
 HEADLINE = "prefill_bf16_h32_d128"
 SECONDARY = ("decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,bwd:prefill_bf16_h32_d128,"
-             "local_w4096_s4096_h32_d128,docs4096_h32_d128")
+             "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128")
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -268,13 +268,14 @@ class BackwardRun(WorkloadRun):
         from long_context_blockwise_amd import inputs
 
         self.out, self.state = ra.ring_attn_fwd(self.x.q, self.chunks, wl.causal, wl.q_offset,
-                                                flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True, ctx=self.ctx)
+                                                flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True, ctx=self.ctx,
+                                                **self.masks)
         self.dout = inputs.output_grad(wl, device)
         self.dq = torch.empty((wl.B, wl.Lq, wl.Hq, wl.d_qk), device=device, dtype=torch.float32)
         self.grads = [(torch.empty(c[0].shape, device=device, dtype=torch.float32),
                        torch.empty(c[1].shape, device=device, dtype=torch.float32)) for c in self.chunks]
-        self.bws = torch.empty(max(ra.ring_attn_bwd_workspace_size(self.x.q, self.chunks), 1), device=device,
-                               dtype=torch.uint8)
+        bws = ra.ring_attn_bwd_workspace_size(self.x.q, self.chunks, window=wl.window, anchor=wl.anchor)
+        self.bws = torch.empty(max(bws, 1), device=device, dtype=torch.uint8)
         pairs = visible_pairs(wl) * wl.Hq
         # S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q per visible pair
         self.flops = pairs * 2 * (3 * wl.d_qk + 2 * wl.d_v)
@@ -282,7 +283,8 @@ class BackwardRun(WorkloadRun):
 
     def step(self):
         self.ra.ring_attn_bwd(self.x.q, self.chunks, self.out, self.dout, self.state, self.wl.causal,
-                              self.wl.q_offset, dq=self.dq, grads=self.grads, ctx=self.ctx, workspace=self.bws)
+                              self.wl.q_offset, dq=self.dq, grads=self.grads, ctx=self.ctx, workspace=self.bws,
+                              **self.masks)
 
     def result(self, sec_per_step, ev_ms):
         wl = self.wl
@@ -291,7 +293,12 @@ class BackwardRun(WorkloadRun):
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("bwd:" + wl.name),
                     kernels="bwd_pre + bwd_dq + bwd_dkdv per step (traffic: per step)")
-        return dict(workload="bwd:" + wl.name, metric="causal attn bwd TFLOP/s (dQ, dK, dV) per GPU",
+        metric = "causal attn bwd TFLOP/s (dQ, dK, dV) per GPU"
+        if wl.doc_mean:
+            metric = "packed-document attn bwd TFLOP/s (dQ, dK, dV) over visible pairs per GPU"
+        elif wl.window or wl.anchor:
+            metric = "local-window + anchor attn bwd TFLOP/s (dQ, dK, dV) over visible pairs per GPU"
+        return dict(workload="bwd:" + wl.name, metric=metric,
                     value=round(tflops, 2), unit="TFLOP/s", ms_per_step=round(sec_per_step * 1e3, 4),
                     tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1), tflops=round(tflops, 2),
                     launches_per_step=2 + len(self.chunks), roofline=roof)

@@ -122,9 +122,13 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
     v_addrs<C>(0, lane, vaddr);
     int ql = 0, lab_L = 0;  // the row's segment label; the wave's common one
     bool lab_uniform = true;
+    int lab_lo = 0, lab_hi = 0;  // the labels of the workgroup's rows lie in [lab_lo, lab_hi]
+    __shared__ int red[EXT ? 2 * NW : 1];
     if constexpr (EXT) {
         if (a.q_seg && row.ok) ql = a.q_seg[wt.b * a.Lq + row.t];
         wave_label(ql, row.ok, lab_L, lab_uniform);
+        if (a.q_seg)  // uniform
+            wg_min_max<NW>(row.ok ? ql : 2147483647, row.ok ? ql : -2147483647 - 1, red, w, lane, lab_lo, lab_hi);
     }
 
     for (int c = 0; c < a.n_chunks; ++c) {
@@ -132,8 +136,15 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
         int64_t kbeg, kend;
         int ntiles;
         if constexpr (EXT) {
-            if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr)) continue;  // uniform
+            int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
+            if (a.q_seg && a.chunks[c].kseg) {  // uniform
+                const int64_t len = a.chunks[c].len;
+                label_key_span<NW>(a.chunks[c].kseg + wt.b * len, 0, len, lab_lo, lab_hi, red, w, lane, kf, kl);
+                if (kl < kf) continue;  // no key of the chunk carries a label of the rows
+            }
+            if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr, kf, kl)) continue;  // uniform
             kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
+            if (ntiles == 0) continue;
         } else {
             if (!chunk_range(a, wt, c, 0, kbeg, kend, ntiles, BN)) continue;  // uniform
         }
@@ -347,6 +358,25 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             }
         }
     }
+    int kl = 0, lab_L = 0;  // the key's segment label; the wave's common one
+    bool lab_uniform = true;
+    __shared__ int red[EXT ? 2 * kKvWaves : 1];
+    if constexpr (EXT) {
+        if (ch.kseg && key_ok) kl = ch.kseg[b * len + key];
+        wave_label(kl, key_ok, lab_L, lab_uniform);
+        if (a.q_seg && ch.kseg) {  // uniform: only rows with a label of the workgroup's keys see them
+            int klo, khi;
+            wg_min_max<kKvWaves>(key_ok ? kl : 2147483647, key_ok ? kl : -2147483647 - 1, red, w, lane, klo, khi);
+            int64_t rf, rl;
+            label_key_span<kKvWaves>(a.q_seg + b * a.Lq, 0, a.Lq, klo, khi, red, w, lane, rf, rl);
+            t_lo = rf > t_lo ? rf : t_lo;
+            t_hi = rl < t_hi ? rl : t_hi;
+            if (u_lo <= u_hi) {
+                u_lo = rf > u_lo ? rf : u_lo;
+                u_hi = rl < u_hi ? rl : u_hi;
+            }
+        }
+    }
     // row segments: the window's rows, then the anchored rows not next to them
     // (without EXT the single range, in the code of a kernel without anchors)
     t_lo = t_lo / RT * RT;
@@ -366,12 +396,6 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     }
     const int nseg = n1 + n2;
     const int ntiles = nseg * a.G;
-    int kl = 0, lab_L = 0;  // the key's segment label; the wave's common one
-    bool lab_uniform = true;
-    if constexpr (EXT) {
-        if (ch.kseg && key_ok) kl = ch.kseg[b * len + key];
-        wave_label(kl, key_ok, lab_L, lab_uniform);
-    }
 
     int kaddr[C::NKA];
     k_addrs<C>(0, l32, g, kaddr);
