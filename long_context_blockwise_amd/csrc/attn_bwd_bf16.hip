@@ -139,7 +139,16 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
             int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
             if (a.q_seg && a.chunks[c].kseg) {  // uniform
                 const int64_t len = a.chunks[c].len;
-                label_key_span<NW>(a.chunks[c].kseg + wt.b * len, 0, len, lab_lo, lab_hi, red, w, lane, kf, kl);
+                int64_t k0 = 0, k1 = len;
+                if (a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
+                    int64_t rb, re;
+                    int rn;
+                    if (!chunk_range(a, wt, c, 0, rb, re, rn, BN)) continue;
+                    const int64_t rend = rb + (int64_t)rn * BN;
+                    k0 = rb;
+                    k1 = rend < len ? rend : len;
+                }
+                label_key_span<NW>(a.chunks[c].kseg + wt.b * len, k0, k1, lab_lo, lab_hi, red, w, lane, kf, kl);
                 if (kl < kf) continue;  // no key of the chunk carries a label of the rows
             }
             if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr, kf, kl)) continue;  // uniform
@@ -181,20 +190,29 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
             bool skip = keys_unseen(a, ch.start, k0, BN, wv_tlo, wv_thi);
             bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
             const char *lab = kst(u) + C::TILE + 256 * w;
+            const bool range_full = full;
+            LabelTest lt{true, false, false, true};
             if constexpr (EXT) {
                 if (skip && tile_has_anchor(a, ch.start, k0, BN, wv_tlo, wv_thi)) skip = false;
-                bool lall, lnone;
-                label_tile(lab, BN, kend - k0, lane, lab_L, lab_uniform, lall, lnone);
-                skip = skip || lnone;
-                full = full && lall;
+                lt = label_tile(lab, BN, kend - k0, lane, ql, row.ok, lab_L, lab_uniform);
+                skip = skip || lt.none;
+                full = full && lt.all;
             }
             if (!skip) {
                 f32x16 s[C::KB], dp[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);   // S^T = K Q^T
                 scores<C>(vst(u), kaddr, gf, dp);  // dP^T = V dO^T
                 if (!full) {
-                    if constexpr (EXT) mask_scores_ext<C>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
-                    else mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                    if constexpr (EXT) {
+                        if (lt.per_lane) {  // uniform
+                            if (!range_full) mask_scores_ext<C, false>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
+                            if (!lt.all) mask_lane(s, lt.hit);
+                        } else {
+                            mask_scores_ext<C>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
+                        }
+                    } else {
+                        mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                    }
                 }
                 // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
                 bf16x8 pf[2 * C::KB];
@@ -367,8 +385,15 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         if (a.q_seg && ch.kseg) {  // uniform: only rows with a label of the workgroup's keys see them
             int klo, khi;
             wg_min_max<kKvWaves>(key_ok ? kl : 2147483647, key_ok ? kl : -2147483647 - 1, red, w, lane, klo, khi);
+            // (only the rows of the window's range and the anchored rows are scanned)
+            int64_t r0 = t_lo, r1 = t_hi + 1;
+            if (u_lo <= u_hi) {
+                r0 = u_lo < r0 ? u_lo : r0;
+                r1 = u_hi + 1 > r1 ? u_hi + 1 : r1;
+            }
+            if (r1 < r0) r1 = r0;
             int64_t rf, rl;
-            label_key_span<kKvWaves>(a.q_seg + b * a.Lq, 0, a.Lq, klo, khi, red, w, lane, rf, rl);
+            label_key_span<kKvWaves>(a.q_seg + b * a.Lq, r0, r1, klo, khi, red, w, lane, rf, rl);
             t_lo = rf > t_lo ? rf : t_lo;
             t_hi = rl < t_hi ? rl : t_hi;
             if (u_lo <= u_hi) {
@@ -451,15 +476,16 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         const int64_t thi = t0 + RT - 1 < a.Lq - 1 ? t0 + RT - 1 : a.Lq - 1;
         bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
         bool full = t0 + RT - 1 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
+        const bool range_full = full;
+        LabelTest lbt{true, false, false, true};
         const char *rlab = gtile(u) + C::TILE + 256 * w;  // EXT: labels of the tile's rows
         if constexpr (EXT) {
             // anchored rows of a lane's key inside the tile
             const bool anch = ar_lo < ar_hi && ar_lo <= a.q_offset + thi && ar_hi > a.q_offset + t0;
             if (skip && wk0 < len && __builtin_amdgcn_ballot_w64(anch) != 0) skip = false;
-            bool lall, lnone;
-            label_tile(rlab, RT, a.Lq - t0, lane, lab_L, lab_uniform, lall, lnone);
-            skip = skip || lnone;
-            full = full && lall;
+            lbt = label_tile(rlab, RT, a.Lq - t0, lane, kl, key_ok, lab_L, lab_uniform);
+            skip = skip || lbt.none;
+            full = full && lbt.all;
         }
         if (!skip) {
             const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + LDW * w;
@@ -498,20 +524,34 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                     alo = alo < -big ? -big : (alo > big ? big : alo);
                     ahi = ahi < -big ? -big : (ahi > big ? big : ahi);
                     const int alo32 = (int)alo, ahi32 = (int)ahi;
+                    if (lbt.per_lane) {  // uniform: the tile's rows carry one label
+                        if (!range_full) {
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        int rl[16];
+                            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const i32x4 x = *(const i32x4 *)(rlab + 4 * (32 * rb + 8 * j + 4 * g));
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) rl[4 * j + e] = x[e];
+                                for (int i = 0; i < 16; ++i) {
+                                    const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+                                    const bool in = (ro >= lo32 && ro < hi32) || (ro >= alo32 && ro < ahi32);
+                                    if (!in) s[rb][i] = kNegInf;
+                                }
                         }
+                        if (!lbt.all) mask_lane(s, lbt.hit);
+                    } else {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
-                            const bool in = (ro >= lo32 && ro < hi32) || (ro >= alo32 && ro < ahi32);
-                            if (!in || rl[i] != kl) s[rb][i] = kNegInf;
+                        for (int rb = 0; rb < RB; ++rb) {
+                            int rl[16];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const i32x4 x = *(const i32x4 *)(rlab + 4 * (32 * rb + 8 * j + 4 * g));
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) rl[4 * j + e] = x[e];
+                            }
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+                                const bool in = (ro >= lo32 && ro < hi32) || (ro >= alo32 && ro < ahi32);
+                                if (!in || rl[i] != kl) s[rb][i] = kNegInf;
+                            }
                         }
                     }
                 } else {

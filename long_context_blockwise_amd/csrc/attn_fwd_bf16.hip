@@ -319,11 +319,19 @@ void fwd_bf16_kernel(const FwdArgs a) {
     token_range(a, wt.p0 + 32 * wr, wt.p0 + 32 * wr + 32, wv_tlo, wv_thi);
     const LaneRow row = lane_row(a, wt, wt.p0 + 32 * wr + l32);
 
+    // With labels a workgroup may find no visible key in any chunk of the
+    // launch (packed documents): the queries and the state are then read only
+    // when the first chunk with tiles comes (live), and an untouched state
+    // that stays in place is not written back.  (With anchors alone the early
+    // loads hide latency that the deferred ones would expose.)
     bf16x8 qf[C::DS];
-    load_q(a, wt, row, g, 0, qf);
     f32x16 oacc[C::DB];
     float m_run, m_true, lsum;
-    load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+    bool live = !LAB;
+    if constexpr (!LAB) {
+        load_q(a, wt, row, g, 0, qf);
+        load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+    }
     const float c2 = a.scale_log2;
     int kaddr[C::NKA];
     k_addrs<C>(wk * C::KW, l32, g, kaddr);
@@ -355,15 +363,28 @@ void fwd_bf16_kernel(const FwdArgs a) {
         if constexpr (ANC) {
             int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
             if (LAB && a.q_seg && a.chunks[c].kseg) {  // uniform
-                const int64_t k0 = a.split_mode ? sub * a.sub_len : 0;
+                int64_t k0 = a.split_mode ? sub * a.sub_len : 0;
                 const int64_t len = a.chunks[c].len;
-                const int64_t k1 = a.split_mode && k0 + a.sub_len < len ? k0 + a.sub_len : len;
+                int64_t k1 = a.split_mode && k0 + a.sub_len < len ? k0 + a.sub_len : len;
+                if (a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
+                    int64_t rb, re;
+                    int rn;
+                    if (!chunk_range(a, wt, c, sub, rb, re, rn, BN)) continue;
+                    const int64_t rend = rb + (int64_t)rn * BN;
+                    k0 = rb > k0 ? rb : k0;
+                    k1 = rend < k1 ? rend : k1;
+                }
                 label_key_span<NW>(a.chunks[c].kseg + wt.b * len, k0, k1, lab_lo, lab_hi, red, w, lane, kf, kl);
                 if (kl < kf) continue;  // no key of the chunk carries a label of the rows
             }
             if (!chunk_tiles<ANC>(a, wt, c, sub, BN, tr, kf, kl)) continue;  // uniform
             kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
             if (ntiles == 0) continue;
+            if (LAB && !live) {  // uniform
+                live = true;
+                load_q(a, wt, row, g, 0, qf);
+                load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+            }
         } else {
             if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
         }
@@ -405,30 +426,47 @@ void fwd_bf16_kernel(const FwdArgs a) {
             if constexpr (ANC) {
                 if (skip && tile_has_anchor(a, ch.start, wk0, C::KW, wv_tlo, wv_thi)) skip = false;
             }
-            if constexpr (LAB) {
-                bool lall, lnone;
-                label_tile(lab, C::KW, kend - wk0, lane, lab_L, lab_uniform, lall, lnone);
-                skip = skip || lnone;
-                full = full && lall;
-            }
+            const bool range_full = full;
             if (!skip) {
+                // the key labels are read before the scores, whose MFMAs hide
+                // the read; a tile whose keys carry no label of the wave's
+                // rows is dropped after them
+                int lk = 0;
+                if constexpr (LAB) lk = reinterpret_cast<const int *>(lab)[lane];
                 prio_mfma();
                 f32x16 s[C::KB];
                 scores<C>(kst(u), kaddr, qf, s);
                 prio_valu();
-                if (!full) {
-                    if constexpr (ANC) mask_scores_ext<C, LAB>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
-                    else mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
+                LabelTest lt{true, false, false, true};
+                if constexpr (LAB) {
+                    lt = label_test(lk, C::KW, kend - wk0, lane, ql, row.ok, lab_L, lab_uniform);
+                    full = full && lt.all;
                 }
-                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
-                if constexpr (RA_TUNE_FUSE) {
-                    softmax_pv<C>(s, c2, m_run, lsum, vst(u), vaddr, oacc);
-                } else {
-                    bf16x8 pf[2 * C::KB];
-                    probabilities<C>(s, c2, m_run, lsum, pf);
-                    prio_mfma();
-                    accumulate_pv<C>(vst(u), vaddr, pf, oacc);
-                    prio_valu();
+                if (!lt.none) {  // uniform
+                    if (!full) {
+                        if constexpr (LAB) {
+                            if (lt.per_lane) {  // uniform
+                                if (!range_full) mask_scores_ext<C, false>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
+                                if (!lt.all) mask_lane(s, lt.hit);
+                            } else {
+                                mask_scores_ext<C, true>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
+                            }
+                        } else if constexpr (ANC) {
+                            mask_scores_ext<C, false>(s, vis, an, (int)(wk0 - kbeg), g, lab, ql);
+                        } else {
+                            mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
+                        }
+                    }
+                    update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                    if constexpr (RA_TUNE_FUSE) {
+                        softmax_pv<C>(s, c2, m_run, lsum, vst(u), vaddr, oacc);
+                    } else {
+                        bf16x8 pf[2 * C::KB];
+                        probabilities<C>(s, c2, m_run, lsum, pf);
+                        prio_mfma();
+                        accumulate_pv<C>(vst(u), vaddr, pf, oacc);
+                        prio_valu();
+                    }
                 }
             }
             if (it + 1 < ntiles) {
@@ -438,6 +476,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
         });
     }
 
+    if (!live) {  // uniform
+        if (a.load_state && a.store_state && !a.store_out && !a.split_mode) return;  // the state is the result
+        load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+    }
     renormalise(m_run, m_true, lsum, oacc);
     if constexpr (KSPLIT > 1) {
         // waves wk > 0 hand their (m, l, O) to wave wk == 0 of the same rows.

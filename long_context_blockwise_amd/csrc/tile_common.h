@@ -450,17 +450,31 @@ __device__ inline void wg_min_max(int lo, int hi, int *red, int w, int lane, int
 // First and last key in [k0, k1) of a chunk (labels kseg) whose label lies
 // in [lo, hi], over the workgroup's NW waves: kl < kf when there is none.
 // With packed documents (labels that never decrease) this is the span of
-// the rows' documents.
+// the rows' documents.  Each thread keeps kScanLoads label loads in flight
+// per pass (indexes past the end re-read the last key, which changes
+// neither end), so a pass costs one memory round trip.
+constexpr int kScanLoads = 8;
 template <int NW>
 __device__ inline void label_key_span(const int32_t *kseg, int64_t k0, int64_t k1, int lo, int hi, int *red, int w,
                                       int lane, int64_t &kf, int64_t &kl) {
+    constexpr int T = NW * 64;
+    const int n = k1 > k0 ? (int)(k1 - k0) : 0;  // chunk lengths stay below 2^31
+    const int32_t *p = kseg + k0;
     int first = 2147483647, last = -1;
-    for (int64_t i = k0 + (int64_t)threadIdx.x; i < k1; i += NW * 64) {
-        const int L = kseg[i];
-        if (L >= lo && L <= hi) {
-            const int r = (int)(i - k0);
-            first = r < first ? r : first;
-            last = r;
+    for (int base = 0; base < n; base += T * kScanLoads) {
+        int r[kScanLoads], L[kScanLoads];
+#pragma unroll
+        for (int u = 0; u < kScanLoads; ++u) {
+            const int i = base + u * T + (int)threadIdx.x;
+            r[u] = i < n ? i : n - 1;
+            L[u] = p[r[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < kScanLoads; ++u) {
+            if (L[u] >= lo && L[u] <= hi) {
+                first = r[u] < first ? r[u] : first;
+                last = r[u] > last ? r[u] : last;
+            }
         }
     }
     int f, l;
@@ -469,17 +483,47 @@ __device__ inline void label_key_span(const int32_t *kseg, int64_t k0, int64_t k
     kl = l < 0 ? 0 : k0 + l;
 }
 
-// Label test of a wave's n (<= 64) keys of a tile (label of key `lane` at
-// lab; keys at or past nvalid do not exist): with uniform row label L, every
-// key carries it (all) / none does (none).
-__device__ inline void label_tile(const char *lab, int n, int64_t nvalid, int lane, int L, bool uniform, bool &all,
-                                  bool &none) {
+// Label test of a wave's n (<= 64) tile entries (keys, or rows in the
+// dK/dV kernel; the label of entry `lane` at lab; entries at or past nvalid
+// do not exist) against each lane's own label x (valid where ok; L and
+// uniform as wave_label gives them):
+//   all       every entry is visible to every valid lane: no label mask;
+//   none      no valid lane shares a label with an entry: the tile is skipped;
+//   per_lane  the entries carry one label, so the test reduces to `hit`
+//             (x equals it) per lane: a lane without a hit sees nothing.
+// A wave whose lanes straddle a document boundary thus masks whole lanes on
+// the tiles inside one document instead of testing every element.
+struct LabelTest {
+    bool all, none, per_lane, hit;
+};
+// (label_test takes the entry label lk = lab[lane] already read, so that the
+// read can be issued ahead of other work.)
+__device__ inline LabelTest label_test(int lk, int n, int64_t nvalid, int lane, int x, bool ok, int L, bool uniform) {
+    LabelTest t;
     const bool mine = lane < n;
     const bool valid = mine && lane < nvalid;
-    const int lk = reinterpret_cast<const int *>(lab)[lane];
-    const bool eq = valid && lk == L;
-    all = uniform && __builtin_amdgcn_ballot_w64(mine && !eq) == 0;
-    none = uniform && __builtin_amdgcn_ballot_w64(eq) == 0;
+    const uint64_t vm = __builtin_amdgcn_ballot_w64(valid);
+    const int KL = __builtin_amdgcn_readlane(lk, vm ? __builtin_ctzll(vm) : 0);
+    const bool kuni = __builtin_amdgcn_ballot_w64(valid && lk != KL) == 0;
+    t.hit = ok && x == KL;
+    t.per_lane = kuni;
+    t.all = kuni && __builtin_amdgcn_ballot_w64(mine && !valid) == 0 && __builtin_amdgcn_ballot_w64(ok && !t.hit) == 0;
+    t.none = vm == 0 || (kuni ? __builtin_amdgcn_ballot_w64(t.hit) == 0
+                              : uniform && __builtin_amdgcn_ballot_w64(valid && lk == L) == 0);
+    return t;
+}
+__device__ inline LabelTest label_tile(const char *lab, int n, int64_t nvalid, int lane, int x, bool ok, int L,
+                                       bool uniform) {
+    return label_test(reinterpret_cast<const int *>(lab)[lane], n, nvalid, lane, x, ok, L, uniform);
+}
+
+// Every score of a lane without a label hit masked.
+template <int N>
+__device__ inline void mask_lane(f32x16 (&s)[N], bool hit) {
+#pragma unroll
+    for (int b = 0; b < N; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[b][i] = hit ? s[b][i] : kNegInf;
 }
 
 // Key labels of one wave's 64 keys k0 .. k0+63 of a chunk, HBM -> LDS (one
