@@ -294,15 +294,15 @@ __device__ inline void write_results(const FwdArgs &a, const WorkTile &wt, const
 // ---------------------------------------------------------------------------
 // The attention kernel: one tile at a time (query-chunk prefill and split-KV decoding)
 // ---------------------------------------------------------------------------
-// EXT instantiations add anchor tokens (EXT >= 1) and segment labels
-// (EXT = 2): up to five extra tiles hold anchors outside the window's range,
+// EXT instantiations add anchor tokens (EXT bit 1) and segment labels
+// (EXT bit 2): up to five extra tiles hold anchors outside the window's range,
 // and with labels each stage also holds 64 key labels per wave (after the K
 // tile).
 template <int D, int BN, int NW, int KSPLIT, int NS, int EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D, BN, NW, KSPLIT>;
-    constexpr bool ANC = EXT >= 1, LAB = EXT == 2;
+    constexpr bool ANC = (EXT & 1) != 0, LAB = (EXT & 2) != 0;
     constexpr int LPT = 2 * C::LOADS_PER_WAVE + (LAB ? 1 : 0);
     constexpr int LABB = LAB ? NW * 256 : 0;  // bytes of key labels per stage
     RA_STAGE_ARRAYS(NS, C::TILE + LABB)
@@ -360,13 +360,13 @@ void fwd_bf16_kernel(const FwdArgs a) {
         TileRange tr;
         int64_t kbeg, kend;
         int ntiles;
-        if constexpr (ANC) {
+        if constexpr (ANC || LAB) {
             int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
             if (LAB && a.q_seg && a.chunks[c].kseg) {  // uniform
                 int64_t k0 = a.split_mode ? sub * a.sub_len : 0;
                 const int64_t len = a.chunks[c].len;
                 int64_t k1 = a.split_mode && k0 + a.sub_len < len ? k0 + a.sub_len : len;
-                if (a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
+                if (!ANC || a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
                     int64_t rb, re;
                     int rn;
                     if (!chunk_range(a, wt, c, sub, rb, re, rn, BN)) continue;
@@ -377,7 +377,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 label_key_span<NW>(a.chunks[c].kseg + wt.b * len, k0, k1, lab_lo, lab_hi, red, w, lane, kf, kl);
                 if (kl < kf) continue;  // no key of the chunk carries a label of the rows
             }
-            if (!chunk_tiles<ANC>(a, wt, c, sub, BN, tr, kf, kl)) continue;  // uniform
+            if (!chunk_tiles<ANC, LAB>(a, wt, c, sub, BN, tr, kf, kl)) continue;  // uniform
             kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
             if (ntiles == 0) continue;
             if (LAB && !live) {  // uniform
@@ -397,7 +397,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto tile_start = [&](int t) -> int64_t {
             if constexpr (ANC) return tr.start(t, BN);
-            else return kbeg + (int64_t)t * BN;
+            else return kbeg + (int64_t)t * BN;  // (with labels alone: main tiles only)
         };
         auto issue = [&](auto u, int t) {
             const int64_t k0 = tile_start(t);
@@ -957,6 +957,7 @@ hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s) {
 template <int D, int BN, int NW, int KS, int NS>
 hipError_t launch_masked(const FwdArgs &a, hipStream_t s) {
     using C = Cfg<D, BN, NW, KS>;
+    if (a.q_seg && a.anchor > 0) return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 3>, a, s);
     if (a.q_seg) return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 2>, a, s);
     if (a.anchor > 0) return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 1>, a, s);
     return launch<C>(fwd_bf16_kernel<D, BN, NW, KS, NS, 0>, a, s);

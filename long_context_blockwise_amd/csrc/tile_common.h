@@ -632,9 +632,10 @@ struct TileRange {
     }
 };
 
-// (EXT) Keys outside [kf, kl] carry no label of the workgroup's rows: the
-// main tiles and the anchor tiles are cut to that range.
-template <bool EXT>
+// Keys outside [kf, kl] carry no label of the workgroup's rows: (CLAMP) the
+// main tiles and (EXT) the anchor tiles are cut to that range.  EXT adds the
+// anchor tiles; labels without anchors take CLAMP alone.
+template <bool EXT, bool CLAMP = EXT>
 __device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, int sub, int bn, TileRange &tr,
                                    int64_t kf = 0, int64_t kl = INT64_MAX) {
     const ChunkArg &ch = a.chunks[c];
@@ -646,7 +647,7 @@ __device__ inline bool chunk_tiles(const FwdArgs &a, const WorkTile &wt, int c, 
         kbeg = tr.kbase;
         kend = a.split_mode ? (tr.kbase + a.sub_len < ch.len ? tr.kbase + a.sub_len : ch.len) : ch.len;
     }
-    if (EXT && nmain > 0) {  // main tiles cut to [kf, kl], on the same tile grid
+    if (CLAMP && nmain > 0) {  // main tiles cut to [kf, kl], on the same tile grid
         const int64_t mend = kbeg + (int64_t)nmain * bn;
         const int64_t end = kl < mend ? kl + 1 : mend;
         if (kf > kbeg) kbeg += (kf - kbeg) / bn * bn;
