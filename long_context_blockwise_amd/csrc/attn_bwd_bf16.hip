@@ -75,15 +75,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A) {
 // ---------------------------------------------------------------------------
 // dQ: query rows resident, key tiles streamed (the forward's structure)
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NS, bool EXT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(EXT ? 1 : 2, EXT ? 1 : 2)))
-void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the registers of the label masks)
+// EXT bit 1: anchor tokens (one wave per SIMD, for the registers of the
+// anchor tiles); EXT bit 2: segment labels.
+template <int D, int BN, int NW, int NS, int EXT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((EXT & 1) ? 1 : 2, (EXT & 1) ? 1 : 2)))
+void bwd_dq_kernel(const BwdArgs A) {
+    constexpr bool ANC = (EXT & 1) != 0, LAB = (EXT & 2) != 0;
     const FwdArgs &a = A.f;
     using C = Cfg<D, BN, NW, 1>;
-    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (EXT ? 1 : 0);
-    constexpr int LABB = EXT ? NW * 256 : 0;  // bytes of key labels per stage (after the K tile)
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE + (LAB ? 1 : 0);
+    constexpr int LABB = LAB ? NW * 256 : 0;  // bytes of key labels per stage (after the K tile)
     RA_STAGE_ARRAYS(NS, C::TILE + LABB)
-    static_assert(!EXT || C::KW <= 64, "a wave's labels are 64 dwords");
+    static_assert(!LAB || C::KW <= 64, "a wave's labels are 64 dwords");
 
     const int lane = threadIdx.x & 63, w = wave_index();
     const int l32 = lane & 31, g = lane >> 5;
@@ -123,8 +126,8 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
     int ql = 0, lab_L = 0;  // the row's segment label; the wave's common one
     bool lab_uniform = true;
     int lab_lo = 0, lab_hi = 0;  // the labels of the workgroup's rows lie in [lab_lo, lab_hi]
-    __shared__ int red[EXT ? 2 * NW : 1];
-    if constexpr (EXT) {
+    __shared__ int red[LAB ? 2 * NW : 1];
+    if constexpr (LAB) {
         if (a.q_seg && row.ok) ql = a.q_seg[wt.b * a.Lq + row.t];
         wave_label(ql, row.ok, lab_L, lab_uniform);
         if (a.q_seg)  // uniform
@@ -135,12 +138,12 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
         TileRange tr;  // (without EXT the plain range, as in the forward kernel)
         int64_t kbeg, kend;
         int ntiles;
-        if constexpr (EXT) {
+        if constexpr (ANC || LAB) {
             int64_t kf = 0, kl = INT64_MAX;  // keys that can carry a label of the rows
-            if (a.q_seg && a.chunks[c].kseg) {  // uniform
+            if (LAB && a.q_seg && a.chunks[c].kseg) {  // uniform
                 const int64_t len = a.chunks[c].len;
                 int64_t k0 = 0, k1 = len;
-                if (a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
+                if (!ANC || a.anchor == 0) {  // uniform: then only keys in the rows' causal/window range are seen
                     int64_t rb, re;
                     int rn;
                     if (!chunk_range(a, wt, c, 0, rb, re, rn, BN)) continue;
@@ -151,7 +154,7 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
                 label_key_span<NW>(a.chunks[c].kseg + wt.b * len, k0, k1, lab_lo, lab_hi, red, w, lane, kf, kl);
                 if (kl < kf) continue;  // no key of the chunk carries a label of the rows
             }
-            if (!chunk_tiles<EXT>(a, wt, c, 0, BN, tr, kf, kl)) continue;  // uniform
+            if (!chunk_tiles<ANC, LAB>(a, wt, c, 0, BN, tr, kf, kl)) continue;  // uniform
             kbeg = tr.kbeg, kend = tr.kend, ntiles = tr.ntot;
             if (ntiles == 0) continue;
         } else {
@@ -160,19 +163,19 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
         Anchors an{kNoKey, kNoKey, kNoKey};
-        if constexpr (EXT) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
-        const int32_t *kseg = EXT && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
+        if constexpr (ANC) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
+        const int32_t *kseg = LAB && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
         const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
         const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
         auto tile_start = [&](int t) -> int64_t {
-            if constexpr (EXT) return tr.start(t, BN);
+            if constexpr (ANC) return tr.start(t, BN);
             else return kbeg + (int64_t)t * BN;
         };
         auto issue = [&](auto u, int t) {
             const int64_t k0 = tile_start(t);
             load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
             load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
-            if constexpr (EXT) load_labels(kseg, k0, kend, kst(u) + C::TILE + 256 * w, lane);
+            if constexpr (LAB) load_labels(kseg, k0, kend, kst(u) + C::TILE + 256 * w, lane);
         };
         auto wait_for = [&](int need, int last) {
             const int after = last - need;
@@ -192,8 +195,10 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
             const char *lab = kst(u) + C::TILE + 256 * w;
             const bool range_full = full;
             LabelTest lt{true, false, false, true};
-            if constexpr (EXT) {
+            if constexpr (ANC) {
                 if (skip && tile_has_anchor(a, ch.start, k0, BN, wv_tlo, wv_thi)) skip = false;
+            }
+            if constexpr (LAB) {
                 lt = label_tile(lab, BN, kend - k0, lane, ql, row.ok, lab_L, lab_uniform);
                 skip = skip || lt.none;
                 full = full && lt.all;
@@ -203,13 +208,15 @@ void bwd_dq_kernel(const BwdArgs A) {  // (EXT: one wave per SIMD, for the regis
                 scores<C>(kst(u), kaddr, qf, s);   // S^T = K Q^T
                 scores<C>(vst(u), kaddr, gf, dp);  // dP^T = V dO^T
                 if (!full) {
-                    if constexpr (EXT) {
+                    if constexpr (LAB) {
                         if (lt.per_lane) {  // uniform
                             if (!range_full) mask_scores_ext<C, false>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
                             if (!lt.all) mask_lane(s, lt.hit);
                         } else {
                             mask_scores_ext<C>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
                         }
+                    } else if constexpr (ANC) {
+                        mask_scores_ext<C, false>(s, vis, an, (int)(k0 - kbeg), g, lab, ql);
                     } else {
                         mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
                     }
@@ -683,18 +690,25 @@ hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int EXT>
+static void launch_dq(const BwdArgs &a, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 64, 4, 2, EXT>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int D>
+static void launch_dq_ext(const BwdArgs &a, unsigned grid, hipStream_t s) {
+    const int ext = (a.f.anchor > 0 ? 1 : 0) | (a.f.q_seg != nullptr ? 2 : 0);
+    if (ext == 3) launch_dq<D, 3>(a, grid, s);
+    else if (ext == 2) launch_dq<D, 2>(a, grid, s);
+    else if (ext == 1) launch_dq<D, 1>(a, grid, s);
+    else launch_dq<D, 0>(a, grid, s);
+}
+
 hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.f.n_rowtiles * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;
-    const bool ext = a.f.anchor > 0 || a.f.q_seg != nullptr;
-    if (d == 128 && ext)
-        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2, true>), dim3(grid), dim3(256), 0, s, a);
-    else if (d == 128)
-        hipLaunchKernelGGL((bwd_dq_kernel<128, 64, 4, 2, false>), dim3(grid), dim3(256), 0, s, a);
-    else if (ext)
-        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<64, 64, 4, 2, false>), dim3(grid), dim3(256), 0, s, a);
+    if (d == 128) launch_dq_ext<128>(a, grid, s);
+    else launch_dq_ext<64>(a, grid, s);
     return hipGetLastError();
 }
 

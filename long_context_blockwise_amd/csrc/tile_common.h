@@ -399,23 +399,18 @@ __device__ inline void mask_scores_ext(f32x16 (&s)[C::KB], VisRange v, Anchors a
     auto shift = [&](int x) { return x == kNoKey ? kNoKey : x - off; };
     const int a0 = shift(an.a0), a1 = shift(an.a1), a2 = shift(an.a2);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-        int lk[16] = {};
-        if constexpr (LAB) {
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const i32x4 x = *(const i32x4 *)(lab + 4 * (32 * kb + 8 * j + 4 * g));
+        for (int j = 0; j < 4; ++j) {  // four keys at a time (few registers live)
+            i32x4 lk = {0, 0, 0, 0};
+            if constexpr (LAB) lk = *(const i32x4 *)(lab + 4 * (32 * kb + 8 * j + 4 * g));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lk[4 * j + e] = x[e];
+            for (int e = 0; e < 4; ++e) {
+                const int key = 32 * kb + 8 * j + e;
+                const bool in = (key >= lo && key < hi) || key == a0 || key == a1 || key == a2;
+                if (!in || (LAB && lk[e] != ql)) s[kb][4 * j + e] = kNegInf;
             }
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
-            const bool in = (key >= lo && key < hi) || key == a0 || key == a1 || key == a2;
-            if (!in || (LAB && lk[i] != ql)) s[kb][i] = kNegInf;
-        }
-    }
 }
 
 // The rows' common label L of a wave (uniform = every valid row has it).
