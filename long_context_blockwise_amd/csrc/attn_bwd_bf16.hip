@@ -321,9 +321,10 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     const bool key_ok = key < len;
     auto kpos_of = [&](int64_t k) { return ch.start + k; };
 
-    // resident B operands: K^T and V^T fragments of the lane's key
+    // resident B operands: K^T and V^T fragments of the lane's key (with EXT
+    // read once the workgroup is known to have rows to visit)
     bf16x8 kf[C::DS], vf[C::DS];
-    {
+    auto load_kv = [&]() {
         const uint16_t *kp = (const uint16_t *)ch.k + b * a.k_sb + key * a.k_ss + hk * a.k_sh + 8 * g;
         const uint16_t *vp = (const uint16_t *)ch.v + b * a.v_sb + key * a.v_ss + hk * a.v_sh + 8 * g;
 #pragma unroll
@@ -336,7 +337,8 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             kf[ds] = to_bf16x8(x);
             vf[ds] = to_bf16x8(y);
         }
-    }
+    };
+    if constexpr (!EXT) load_kv();
     f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -428,6 +430,12 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     }
     const int nseg = n1 + n2;
     const int ntiles = nseg * a.G;
+    if constexpr (EXT) {
+        // no row sees the workgroup's keys (packed documents): their gradients
+        // are zero, which ACCUMULATE leaves as they are
+        if (ntiles == 0 && A.accumulate) return;  // uniform
+        if (ntiles > 0) load_kv();
+    }
 
     int kaddr[C::NKA];
     k_addrs<C>(0, l32, g, kaddr);

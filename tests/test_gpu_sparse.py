@@ -136,3 +136,46 @@ def test_sparse_unsupported_shapes():
     with pytest.raises(ra.RingAttnError) as e:
         ra.ring_attn_fwd(x.q, x.chunks(), True, 32, anchor=16)
     assert e.value.code == ra.RA_ERR_UNSUPPORTED
+
+
+def test_sparse_backward_unseen_chunks():
+    """Packed documents whose rows see no key of chunks 0 and 1: those
+    chunks' dK/dV are written as exact zeros (over NaN-filled buffers), and
+    with ACCUMULATE left bitwise as they were; chunk 2 matches the oracle in
+    both modes."""
+    x = inputs.make(_wl(B=1, d=128, lens=(256, 256, 256), Lq=256, q_offset=512), DEV)
+    chunks = x.chunks()
+    pos = torch.arange(768, dtype=torch.int32)
+    lab = ((pos >= 512).int() + (pos >= 640).int()).unsqueeze(0).to(DEV)
+    q_seg = lab[:, 512:].contiguous()
+    k_segs = [lab[:, s:s + 256].contiguous() for s in (0, 256, 512)]
+    out, st = ra.ring_attn_fwd(x.q, chunks, True, 512, flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True, q_seg=q_seg,
+                               k_segs=k_segs)
+    dout = inputs.output_grad(x.wl, DEV)
+    dq_ref, dks, dvs = oracle.attention_bwd(x.q.cpu(), to_host(chunks), dout.cpu(), 512, True, q_seg=q_seg.cpu(),
+                                            k_segs=[k.cpu() for k in k_segs])
+    nan = lambda t: torch.full(t.shape, float("nan"), device=DEV, dtype=torch.float32)
+    dq = nan(x.q)
+    grads = [(nan(c[0]), nan(c[1])) for c in chunks]
+    ra.ring_attn_bwd(x.q, chunks, out, dout, st, True, 512, dq=dq, grads=grads, q_seg=q_seg, k_segs=k_segs)
+    torch.cuda.synchronize()
+    for c in (0, 1):
+        assert torch.count_nonzero(grads[c][0]).item() == 0 and torch.count_nonzero(grads[c][1]).item() == 0, c
+    _check_grad(dq, dq_ref, "unseen chunks dQ")
+    _check_grad(grads[2][0], dks[2], "unseen chunks dK[2]")
+    _check_grad(grads[2][1], dvs[2], "unseen chunks dV[2]")
+
+    g = torch.Generator(device=DEV).manual_seed(9)
+    base = lambda t: torch.randn(t.shape, device=DEV, dtype=torch.float32, generator=g)
+    dq0 = base(x.q)
+    g0 = [(base(c[0]), base(c[1])) for c in chunks]
+    dq1 = dq0.clone()
+    g1 = [(a.clone(), b.clone()) for a, b in g0]
+    ra.ring_attn_bwd(x.q, chunks, out, dout, st, True, 512, flags=ra.RA_FLAG_ACCUMULATE, dq=dq1, grads=g1,
+                     q_seg=q_seg, k_segs=k_segs)
+    torch.cuda.synchronize()
+    for c in (0, 1):
+        assert torch.equal(g1[c][0], g0[c][0]) and torch.equal(g1[c][1], g0[c][1]), c
+    _check_grad(dq1 - dq0, dq_ref, "accumulated dQ")
+    _check_grad(g1[2][0] - g0[2][0], dks[2], "accumulated dK[2]")
+    _check_grad(g1[2][1] - g0[2][1], dvs[2], "accumulated dV[2]")
