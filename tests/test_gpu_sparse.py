@@ -71,6 +71,7 @@ PREFILL = [
     (128, (192, 320), 200, 250, False, 0, 0, "arbitrary"),
     (128, (256, 256, 256), 256, 512, True, 16, 64, "packed"),  # labels and anchors
     (64, (128, 128, 128), 128, 256, True, 8, 32, "arbitrary"),
+    (128, (300, 200), 257, 43, False, 20, 0, "arbitrary"),    # two-sided window, labels alone
 ]
 
 
@@ -108,7 +109,7 @@ def _check_grad(got, ref, what):
 
 @pytest.mark.parametrize("d,window,anchor,labels", [(128, 32, 64, None), (64, 0, 100, None),
                                                     (128, 0, 0, "packed"), (128, 16, 64, "packed"),
-                                                    (64, 8, 32, "arbitrary")])
+                                                    (64, 8, 32, "arbitrary"), (128, 24, 0, "arbitrary")])
 def test_sparse_backward(d, window, anchor, labels):
     x = inputs.make(_wl(B=1, d=d, lens=(256, 256, 256), Lq=256, q_offset=512), DEV)
     chunks = x.chunks()
