@@ -142,8 +142,13 @@ int check_desc(const ra_desc *d, int64_t Lq, Strides *st) {
 bool dense_kv(const int64_t *s) { return s[0] == 0 && s[1] == 0 && s[2] == 0; }
 
 // Segment labels come for the queries and every non-empty chunk, or not at all.
-int check_labels(const ra_desc *d, const ra_kv_chunk *chunks, int P) {
+int check_labels(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P) {
+    // the label scans index keys and query rows with 32-bit integers
+    const int64_t lim = (int64_t)1 << 31;
+    if (d->q_seg && Lq >= lim) return fail(RA_ERR_UNSUPPORTED, "with segment labels Lq must be below 2^31");
     for (int c = 0; c < P && chunks; ++c) {
+        if (chunks[c].k_seg && chunks[c].len >= lim)
+            return fail(RA_ERR_UNSUPPORTED, "chunk %d: with segment labels a chunk must hold fewer than 2^31 keys", c);
         if (chunks[c].len <= 0) continue;
         const bool has = chunks[c].k_seg != nullptr;
         if (has != (d->q_seg != nullptr))
@@ -477,7 +482,7 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     for (int c = 0; c < P && chunks; ++c)
         if (chunks[c].len > 0 && (misaligned(chunks[c].k) || misaligned(chunks[c].v)))
             return fail(RA_ERR_INVALID_ARG, "chunk %d: k/v must be 16-byte aligned", c);
-    if ((rc = check_labels(d, chunks, P))) return rc;
+    if ((rc = check_labels(d, Lq, chunks, P))) return rc;
     Plan pl;
     if ((rc = make_plan(d, Lq, chunks, P, causal, q_offset, flags, have_state, &pl))) return rc;
     if (pl.total > 0 && (!workspace || ws_bytes < pl.total))
@@ -678,7 +683,7 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     if (P < 0 || P > ra::kMaxChunks) return fail(RA_ERR_INVALID_ARG, "P must be in 0..%d", ra::kMaxChunks);
     if (P > 0 && (!chunks || !grads)) return fail(RA_ERR_INVALID_ARG, "chunks and grads must be given");
     if ((flags & ~RA_FLAG_ACCUMULATE) != 0) return fail(RA_ERR_INVALID_ARG, "the backward takes only ACCUMULATE");
-    if (P > 0 && (rc = check_labels(d, chunks, P))) return rc;
+    if (P > 0 && (rc = check_labels(d, Lq, chunks, P))) return rc;
     const bool accumulate = (flags & RA_FLAG_ACCUMULATE) != 0;
     auto misaligned = [](const void *p) { return ((uintptr_t)p & 15) != 0; };
     for (int c = 0; c < P; ++c) {

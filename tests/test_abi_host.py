@@ -334,3 +334,16 @@ def test_anchor_and_label_validation(lib):
     mis = _chunks([64, 64])
     mis[0].k_seg, mis[1].k_seg = 1 << 12, (1 << 12) + 2
     assert fwd(lab, mis) == rb.RA_ERR_INVALID_ARG
+    # label scans index keys and rows with 32-bit integers: longer inputs are refused
+    big = _chunks([64, 1 << 31])
+    big[0].k_seg, big[1].k_seg = 1 << 12, 1 << 13
+    assert fwd(lab, big) == rb.RA_ERR_UNSUPPORTED
+    assert lib.ring_attn_fwd(ctx, ctypes.byref(lab), 1 << 20, 1 << 31, _labelled([64, 64]), 2, 1, 0, 0, 1 << 20,
+                             None, None, None, None, 0, None) == rb.RA_ERR_UNSUPPORTED
+
+
+def _labelled(lens):
+    arr = _chunks(lens)
+    for i in range(len(lens)):
+        arr[i].k_seg = (1 << 12) + 64 * i
+    return arr
