@@ -172,7 +172,12 @@ int ring_attn_ctx_destroy(ra_ctx *ctx);
  * device_index-2, ... modulo P.  Host only; writes P ints to `order`. */
 int ring_attn_ring_order(int device_index, int P, int32_t *order);
 
-/* Chunk classes for a query chunk of Lq rows at absolute positions
+/* Chunk classes of one ring device's schedule (page "RingAttention推理优化：
+ * cache_idx参数使用与千万级上下文高效推理实践", section cache_idx的工作原理 and
+ * its blockwise settings with causal_block_size=1: token-level causality on
+ * absolute positions; page "Ring Attention：百万 Token 上下文的秘密", §4.3
+ * 稀疏注意力掩码: local window plus anchor tokens).
+ * For a query chunk of Lq rows at absolute positions
  * q_offset .. q_offset+Lq-1 (host only): cls[c] = RA_CHUNK_SKIP (no key
  * visible to any query) / FULL (every key visible to every query by the
  * causal and window rules alone: no mask is applied) / DIAG (masked per
@@ -193,7 +198,16 @@ int ring_attn_workspace_size(const ra_desc *d, int64_t Lq,
                              int64_t q_offset, uint32_t flags, int want_state,
                              size_t *bytes);
 
-/* One device's share of ring attention.
+/* One device's share of ring attention (page "Ring Attention：百万 Token
+ * 上下文的秘密": §2.2 环形通信 for the ring of KV chunks, §2.3 数学正确性 for
+ * the exactness of the chunked result, §3.1 Flash Ring Attention for the
+ * blockwise online-softmax computation of each step, §3.2 通信-计算重叠 for
+ * the double-buffered receive that STAGE stands in for; page
+ * "RingAttention推理优化：cache_idx参数使用与千万级上下文高效推理实践",
+ * section cache_idx的工作原理, for q_offset = cache_idx in decoding).  Each
+ * output row is softmax(q k^T * scale) v over the keys of all chunks the
+ * row may see; the fp32 state (m, l, O) after the call is the running max,
+ * denominator and unnormalised output of the online softmax.
  *
  *   q          [B, Lq, Hq, d_qk] query chunk (device)
  *   chunks     P KV chunks (host array of device pointers), processed in

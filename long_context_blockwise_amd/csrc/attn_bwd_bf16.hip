@@ -412,9 +412,12 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         }
     }
     // row segments: the window's rows, then the anchored rows not next to them
-    // (without EXT the single range, in the code of a kernel without anchors)
+    // (without EXT the single range, in the code of a kernel without anchors).
+    // An empty range (no row sees the keys, or no row carries their labels)
+    // stays empty: rounding its start down to the tile grid must not revive it.
+    const bool no_rows = t_hi < t_lo;
     t_lo = t_lo / RT * RT;
-    int n1 = t_hi >= t_lo ? (int)((t_hi - t_lo) / RT + 1) : 0;
+    int n1 = no_rows ? 0 : (int)((t_hi - t_lo) / RT + 1);
     int64_t s2 = 0;
     int n2 = 0;
     if (EXT && u_lo <= u_hi) {

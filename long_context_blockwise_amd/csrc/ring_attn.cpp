@@ -143,12 +143,14 @@ bool dense_kv(const int64_t *s) { return s[0] == 0 && s[1] == 0 && s[2] == 0; }
 
 // Segment labels come for the queries and every non-empty chunk, or not at all.
 int check_labels(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P) {
-    // the label scans index keys and query rows with 32-bit integers
-    const int64_t lim = (int64_t)1 << 31;
-    if (d->q_seg && Lq >= lim) return fail(RA_ERR_UNSUPPORTED, "with segment labels Lq must be below 2^31");
+    // the label scans index keys and query rows with 32-bit integers, and a
+    // pass may step up to 2^16 entries past the end before it stops
+    const int64_t lim = ((int64_t)1 << 31) - ((int64_t)1 << 16);
+    if (d->q_seg && Lq >= lim) return fail(RA_ERR_UNSUPPORTED, "with segment labels Lq must be below 2^31 - 2^16");
     for (int c = 0; c < P && chunks; ++c) {
         if (chunks[c].k_seg && chunks[c].len >= lim)
-            return fail(RA_ERR_UNSUPPORTED, "chunk %d: with segment labels a chunk must hold fewer than 2^31 keys", c);
+            return fail(RA_ERR_UNSUPPORTED,
+                        "chunk %d: with segment labels a chunk must hold fewer than 2^31 - 2^16 keys", c);
         if (chunks[c].len <= 0) continue;
         const bool has = chunks[c].k_seg != nullptr;
         if (has != (d->q_seg != nullptr))
@@ -240,16 +242,13 @@ struct Plan {
     int64_t rows = 0;  // B * Lq * Hq
 };
 
-int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, int causal, int64_t q_offset,
-              uint32_t flags, bool caller_state, Plan *pl) {
+// Positions of a call: q_offset >= 0, chunks with start, len >= 0, their
+// k and v given, and disjoint in position (shared by the forward and the
+// backward).
+int check_positions(const ra_kv_chunk *chunks, int P, int64_t q_offset) {
     if (P < 0) return fail(RA_ERR_INVALID_ARG, "P must be >= 0");
     if (P > 0 && !chunks) return fail(RA_ERR_INVALID_ARG, "chunks is NULL");
     if (q_offset < 0) return fail(RA_ERR_INVALID_ARG, "q_offset must be >= 0");
-    if (flags & ~(RA_FLAG_STAGE | RA_FLAG_SPLIT_KV | RA_FLAG_NO_SPLIT_KV | RA_FLAG_ACCUMULATE))
-        return fail(RA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-    if ((flags & RA_FLAG_SPLIT_KV) && (flags & (RA_FLAG_NO_SPLIT_KV | RA_FLAG_STAGE)))
-        return fail(RA_ERR_INVALID_ARG, "SPLIT_KV cannot be combined with NO_SPLIT_KV or STAGE");
-    // chunks: sane and disjoint in position
     std::vector<std::pair<int64_t, int64_t>> iv;
     for (int c = 0; c < P; ++c) {
         if (chunks[c].len < 0 || chunks[c].start < 0)
@@ -261,6 +260,17 @@ int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, in
     std::sort(iv.begin(), iv.end());
     for (size_t i = 1; i < iv.size(); ++i)
         if (iv[i].first < iv[i - 1].second) return fail(RA_ERR_INVALID_ARG, "KV chunks overlap in position");
+    return RA_OK;
+}
+
+int make_plan(const ra_desc *d, int64_t Lq, const ra_kv_chunk *chunks, int P, int causal, int64_t q_offset,
+              uint32_t flags, bool caller_state, Plan *pl) {
+    if (flags & ~(RA_FLAG_STAGE | RA_FLAG_SPLIT_KV | RA_FLAG_NO_SPLIT_KV | RA_FLAG_ACCUMULATE))
+        return fail(RA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+    if ((flags & RA_FLAG_SPLIT_KV) && (flags & (RA_FLAG_NO_SPLIT_KV | RA_FLAG_STAGE)))
+        return fail(RA_ERR_INVALID_ARG, "SPLIT_KV cannot be combined with NO_SPLIT_KV or STAGE");
+    int rc = check_positions(chunks, P, q_offset);
+    if (rc) return rc;
 
     pl->G = d->Hq / d->Hkv;
     pl->rows = (int64_t)d->B * Lq * d->Hq;
@@ -489,6 +499,9 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total, ws_bytes);
     if (pl.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
         return fail(RA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    // the merge writes the output densely (checked before anything is enqueued)
+    if (pl.split && out && !(st.o[2] == d->d_v && st.o[1] == (int64_t)d->Hq * d->d_v && st.o[0] == Lq * d->Hq * d->d_v))
+        return fail(RA_ERR_UNSUPPORTED, "split-KV needs a dense output");
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return fail(RA_ERR_HIP, "hipSetDevice(%d) failed", ctx->device);
@@ -558,8 +571,6 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         mg.n_parts = slot;
         mg.d_v = d->d_v;
         mg.out_bf16 = d->dtype == RA_BF16;
-        if (out && !(st.o[2] == d->d_v && st.o[1] == (int64_t)d->Hq * d->d_v && st.o[0] == Lq * d->Hq * d->d_v))
-            return fail(RA_ERR_UNSUPPORTED, "split-KV needs a dense output");
         if ((e = ra::launch_merge(mg, s)) != hipSuccess) return hip_fail(e, "merge launch");
         return RA_OK;
     }
@@ -683,11 +694,11 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     if (P < 0 || P > ra::kMaxChunks) return fail(RA_ERR_INVALID_ARG, "P must be in 0..%d", ra::kMaxChunks);
     if (P > 0 && (!chunks || !grads)) return fail(RA_ERR_INVALID_ARG, "chunks and grads must be given");
     if ((flags & ~RA_FLAG_ACCUMULATE) != 0) return fail(RA_ERR_INVALID_ARG, "the backward takes only ACCUMULATE");
+    if ((rc = check_positions(chunks, P, q_offset))) return rc;
     if (P > 0 && (rc = check_labels(d, Lq, chunks, P))) return rc;
     const bool accumulate = (flags & RA_FLAG_ACCUMULATE) != 0;
     auto misaligned = [](const void *p) { return ((uintptr_t)p & 15) != 0; };
     for (int c = 0; c < P; ++c) {
-        if (chunks[c].len < 0) return fail(RA_ERR_INVALID_ARG, "chunk %d: negative length", c);
         if (chunks[c].len == 0) continue;
         if (!chunks[c].k || !chunks[c].v || !grads[c].dk || !grads[c].dv)
             return fail(RA_ERR_INVALID_ARG, "chunk %d: k, v, dk and dv must be given", c);

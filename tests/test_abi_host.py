@@ -281,8 +281,8 @@ def test_bwd_workspace_and_validation(lib):
         grads[i].dk = grads[i].dv = 1 << 16
     buf = 1 << 20  # 16-byte aligned stand-in device addresses
 
-    def bwd(flags=0, P=2, g=grads, dq=buf, ws=buf, ws_bytes=1 << 20, c=ctx):
-        return lib.ring_attn_bwd(c, ctypes.byref(d), buf, 64, arr, P, 1, 64, flags, buf, buf, buf, buf, dq, g,
+    def bwd(flags=0, P=2, g=grads, dq=buf, ws=buf, ws_bytes=1 << 20, c=ctx, q_off=64, chunks=arr):
+        return lib.ring_attn_bwd(c, ctypes.byref(d), buf, 64, chunks, P, 1, q_off, flags, buf, buf, buf, buf, dq, g,
                                  ws, ws_bytes, None)
 
     assert bwd(c=None) == rb.RA_ERR_INVALID_ARG
@@ -295,6 +295,12 @@ def test_bwd_workspace_and_validation(lib):
     assert bwd(ws=None) == rb.RA_ERR_WORKSPACE
     assert bwd(ws_bytes=100) == rb.RA_ERR_WORKSPACE
     assert bwd(ws=buf + 16) == rb.RA_ERR_WORKSPACE
+    # positions are checked as in the forward: q_offset and chunk starts >= 0, chunks disjoint
+    assert bwd(q_off=-1) == rb.RA_ERR_INVALID_ARG
+    assert bwd(chunks=_chunks([64, 64], start=-64)) == rb.RA_ERR_INVALID_ARG
+    overlap = _chunks([64, 64])
+    overlap[1].start = 32
+    assert bwd(chunks=overlap) == rb.RA_ERR_INVALID_ARG
     grads[1].dv = None
     assert bwd() == rb.RA_ERR_INVALID_ARG
     assert ctypes.sizeof(rb.ra_kv_grad) == 16
@@ -334,12 +340,19 @@ def test_anchor_and_label_validation(lib):
     mis = _chunks([64, 64])
     mis[0].k_seg, mis[1].k_seg = 1 << 12, (1 << 12) + 2
     assert fwd(lab, mis) == rb.RA_ERR_INVALID_ARG
-    # label scans index keys and rows with 32-bit integers: longer inputs are refused
-    big = _chunks([64, 1 << 31])
-    big[0].k_seg, big[1].k_seg = 1 << 12, 1 << 13
-    assert fwd(lab, big) == rb.RA_ERR_UNSUPPORTED
-    assert lib.ring_attn_fwd(ctx, ctypes.byref(lab), 1 << 20, 1 << 31, _labelled([64, 64]), 2, 1, 0, 0, 1 << 20,
-                             None, None, None, None, 0, None) == rb.RA_ERR_UNSUPPORTED
+    # label scans index keys and rows with 32-bit integers and may step 2^16
+    # entries past the end: a chunk or query chunk of 2^31 - 2^16 or more is refused
+    lim = (1 << 31) - (1 << 16)
+    for n in (lim, 1 << 31):
+        big = _chunks([64, n])
+        big[0].k_seg, big[1].k_seg = 1 << 12, 1 << 13
+        assert fwd(lab, big) == rb.RA_ERR_UNSUPPORTED
+        assert lib.ring_attn_fwd(ctx, ctypes.byref(lab), 1 << 20, n, _labelled([64, 64]), 2, 1, 0, 0, 1 << 20,
+                                 None, None, None, None, 0, None) == rb.RA_ERR_UNSUPPORTED
+    # one key fewer passes the label checks (and stops at the missing workspace)
+    ok = _chunks([64, lim - 1])
+    ok[0].k_seg, ok[1].k_seg = 1 << 12, 1 << 13
+    assert fwd(lab, ok) == rb.RA_ERR_WORKSPACE
 
 
 def _labelled(lens):

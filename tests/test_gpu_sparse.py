@@ -180,3 +180,15 @@ def test_sparse_backward_unseen_chunks():
     _check_grad(dq1 - dq0, dq_ref, "accumulated dQ")
     _check_grad(g1[2][0] - g0[2][0], dks[2], "accumulated dK[2]")
     _check_grad(g1[2][1] - g0[2][1], dvs[2], "accumulated dV[2]")
+
+    # the unseen chunks' workgroups return before touching their gradients:
+    # -0.0 seeded there stays -0.0 bit for bit (a pass over masked rows would
+    # add +0.0 and turn it into +0.0)
+    negz = lambda t: torch.full(t.shape, -0.0, device=DEV, dtype=torch.float32)
+    gz = [(negz(c[0]), negz(c[1])) for c in chunks]
+    ra.ring_attn_bwd(x.q, chunks, out, dout, st, True, 512, flags=ra.RA_FLAG_ACCUMULATE, dq=dq0.clone(), grads=gz,
+                     q_seg=q_seg, k_segs=k_segs)
+    torch.cuda.synchronize()
+    for c in (0, 1):
+        for t in gz[c]:
+            assert torch.equal(t.view(torch.int32), negz(t).view(torch.int32)), c
