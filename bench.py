@@ -6,24 +6,45 @@ is already resident in HBM:
   * prefill workloads: the device's query chunk against every KV chunk in
     ring order, each received chunk staged through the double buffer on the
     side stream (RA_FLAG_STAGE), causal chunks skipped/masked, output and
-    normalisation fused;
-  * decode workloads: split-KV partials over the cache, then the merge.
+    normalisation fused.  ``inplace:NAME`` runs the same share with every
+    chunk read where it lies (no staging; chunks of one length share a
+    launch), which prices the ring stand-in;
+  * decode workloads: split-KV partials over the cache, then the merge;
+  * ``bwd:NAME``: the gradients (dQ, dK, dV) of a prefill share.
 
-Prints ONE JSON line.  `value` is the headline workload's algorithmic
-TFLOP/s (unmasked query-key pairs x 4 x d per head, no dense-tile flops).
+The headline is the 1M-token ring share (32 query / 8 KV heads, d=128, the
+last of 32 chunks of 32768 tokens, causal): the largest single-GPU prefill
+configuration.  Prints ONE JSON line.  `value` is its algorithmic TFLOP/s
+(unmasked query-key pairs x 2 (d_qk + d_v) per head; no dense-tile flops).
 `roofline` prices the dominant kernel against the bf16 MFMA peak (prefill)
-or HBM bandwidth (decode) with its average launch time from HIP events on the
-launch stream; `cpu_baseline` times the CPU oracle on a bounded row sample of
-the same workload.  `secondary` holds the other workloads timed in the run.
+or HBM bandwidth (decode) with its average launch time from HIP events on
+the launch stream; `cpu_baseline` times the CPU oracle on a bounded,
+stratified row sample of the same workload; `secondary` holds the other
+workloads timed in the run; `run_info` records the board clock sampled
+during the headline's timed steps, the host CPU and the source digest.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--secondary NAMES]
+    python bench.py --profile NAMES [--profile-out DIR]   # rocprofv3 harness
+
+``--profile`` runs this script under rocprofv3 once per pass (kernel trace;
+two counter groups for the matrix and vector pipes; FETCH_SIZE; WRITE_SIZE;
+the same two for a plain copy that calibrates them) and writes one summary
+per workload: MFMA utilisation and VALU activity for prefill, achieved HBM
+bytes and GB/s for decode, each against the chip's published peaks.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import shlex
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -32,31 +53,26 @@ if ROOT not in sys.path:
 
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
-PEAK_FP32_TFLOPS = 157.3
+PEAK_FP32_TFLOPS = 157.3   # fp32 vector
 PEAK_HBM_GBS = 8000.0
+N_CU, N_SIMD, N_XCD = 256, 1024, 8
 
 # HBM bytes per launch of each workload's dominant kernel (for the backward:
 # per step, summed over its bwd_pre, bwd_dq and bwd_dkdv launches), from rocprofv3
-# --pmc FETCH_SIZE and WRITE_SIZE runs of this script, scaled by what the same
-# counters read for a plain 1 GiB elementwise copy (--copy-calibration):
-# FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  Valid only for the kernel sources
-# they were taken on; any change to them voids the figures (traffic -> null).
+# --pmc FETCH_SIZE and WRITE_SIZE runs of this script (--profile), scaled by
+# what the same counters read for a plain 1 GiB elementwise copy.  Valid only
+# for the kernel sources they were taken on; any change to them voids the
+# figures (traffic -> null).
 KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_context_blockwise_amd/csrc/attn_bwd_bf16.hip",
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "2f121dd3a9a8dce6",
-    "prefill_bf16_h32_d128": 5.8531e8,
-    "decode_b4_gqa32x8_cache1m": 1.7250e10,
-    "decode_b4_gqa32x8_cache1m_fp8": 8.6614e9,
-    "bwd:prefill_bf16_h32_d128": 8.2409e9,
-    "local_w4096_s4096_h32_d128": 8.4241e8,
-    "docs4096_h32_d128": 2.0920e8,
-    "bwd:docs4096_h32_d128": 2.9350e9,
+    "digest": "none",
 }
 
-HEADLINE = "prefill_bf16_h32_d128"
-SECONDARY = ("decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,bwd:prefill_bf16_h32_d128,"
+HEADLINE = "ring_1m_gqa32x8_d128"
+SECONDARY = ("prefill_bf16_h32_d128,mla_h16_d512,decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,"
+             "tiny_ring_fp32,bwd:prefill_bf16_h32_d128,inplace:prefill_bf16_h32_d128,inplace:ring_1m_gqa32x8_d128,"
              "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128")
 
 
@@ -140,14 +156,35 @@ def visible_pairs(wl, rows=None):
     return total
 
 
-def kernel_digest():
-    import hashlib
-
+def _digest(files):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_digest():
+    return _digest(KERNEL_SOURCES)
+
+
+def source_digest():
+    """Digest of everything the timed path runs: kernels, host runtime, header,
+    binding and this script (the tree that runs carries no git metadata)."""
+    files = sorted(glob.glob(os.path.join(ROOT, "long_context_blockwise_amd", "csrc", "*")))
+    files = [os.path.relpath(f, ROOT) for f in files]
+    files += ["include/ring_attn.h", "long_context_blockwise_amd/ring_attn.py", "long_context_blockwise_amd/inputs.py",
+              "bench.py"]
+    return _digest(files)
+
+
+def git_revision():
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        return r.stdout.strip() or None if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def measured_traffic(name):
@@ -155,6 +192,54 @@ def measured_traffic(name):
     if name not in MEASURED_TRAFFIC or kernel_digest() != MEASURED_TRAFFIC["digest"]:
         return None
     return MEASURED_TRAFFIC[name]
+
+
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def sample_sclk_mhz():
+    """Current shader clock of GPU 0 in MHz as amd-smi reports it (mean over
+    the XCDs it lists), or None.  Runs amd-smi as a child process."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True, text=True,
+                           timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    if r.returncode != 0:
+        return None
+    try:
+        data = json.loads(r.stdout)
+    except ValueError:
+        return None
+    vals = []
+
+    def walk(x, key=""):
+        if isinstance(x, dict):
+            if key.lower().startswith("gfx") and "clk" in x:
+                v = x["clk"]
+                v = v.get("value") if isinstance(v, dict) else v
+                try:
+                    vals.append(float(v))
+                except (TypeError, ValueError):
+                    pass
+                return
+            for k, v in x.items():
+                walk(v, str(k))
+        elif isinstance(x, list):
+            for v in x:
+                walk(v, key)
+    walk(data)
+    return round(sum(vals) / len(vals), 1) if vals else None
 
 
 def algorithmic(wl):
@@ -173,7 +258,7 @@ def algorithmic(wl):
 class WorkloadRun:
     """Inputs resident on the GPU plus the exact call bench.py times."""
 
-    def __init__(self, name, device="cuda:0"):
+    def __init__(self, name, device="cuda:0", inplace=False):
         import torch
 
         from long_context_blockwise_amd import inputs
@@ -182,6 +267,7 @@ class WorkloadRun:
         self.ra = ra
         self.torch = torch
         self.wl = inputs.WORKLOADS[name]
+        self.label = ("inplace:" if inplace else "") + name
         wl = self.wl
         self.decode = wl.Lq <= 16
         self.x = inputs.make(wl, device)
@@ -191,7 +277,7 @@ class WorkloadRun:
         else:
             dev_index = wl.q_offset // wl.chunk_len  # this device's chunk index
             self.order = ra.ring_attn_ring_order(dev_index, wl.P)
-            self.flags = ra.RA_FLAG_STAGE
+            self.flags = ra.RA_FLAG_NO_SPLIT_KV if inplace else ra.RA_FLAG_STAGE
         self.chunks = self.x.chunks(self.order)
         q_seg, k_segs = inputs.segment_labels(wl, device)
         # local window, anchors and segment labels of the workload (if any)
@@ -203,58 +289,84 @@ class WorkloadRun:
         self.ctx = ra.RingAttnContext(torch.device(device).index or 0)
         cls = ra.ring_attn_plan(wl.Lq, wl.q_offset, wl.causal, [c[2] for c in self.chunks],
                                 [c[0].shape[1] for c in self.chunks], window=wl.window, anchor=wl.anchor)
-        computed = sum(1 for c in cls if c != ra.RA_CHUNK_SKIP)
-        # kernel launches of the dominant kernel per step
-        self.launches = 1 if self.decode else computed
+        computed = [c for c, k in zip(self.chunks, cls) if k != ra.RA_CHUNK_SKIP]
+        # kernel launches of the dominant kernel per step: one per computed
+        # chunk when staged; in place, chunks of one length share a launch
+        if self.decode:
+            self.launches = 1
+        elif inplace:
+            self.launches = len({c[0].shape[1] for c in computed}) if computed else 1
+        else:
+            self.launches = max(1, len(computed))
         self.flops, self.bytes = algorithmic(wl)
 
     def step(self):
         self.ra.ring_attn_fwd(self.x.q, self.chunks, self.wl.causal, self.wl.q_offset,
                               flags=self.flags, out=self.out, ctx=self.ctx, workspace=self.ws, **self.masks)
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, during=None):
+        """Mean wall time per step and the per-step HIP-event times (ms) on
+        the launch stream; `during` runs on a host thread meanwhile."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
+        th = threading.Thread(target=during, daemon=True) if during else None
         t0 = time.perf_counter()
+        if th:
+            th.start()
         for i in range(steps):
             ev[i][0].record()
             self.step()
             ev[i][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if th:
+            th.join(timeout=60)
         ev_ms = [a.elapsed_time(b) for (a, b) in ev]
-        return wall / steps, sum(ev_ms) / len(ev_ms)
+        return wall / steps, ev_ms
+
+    def _timing(self, sec_per_step, ev_ms):
+        return dict(ms_per_step=round(sec_per_step * 1e3, 4),
+                    ms_per_step_events_mean=round(statistics.fmean(ev_ms), 4),
+                    ms_per_step_median=round(statistics.median(ev_ms), 4),
+                    ms_per_step_min=round(min(ev_ms), 4))
 
     def result(self, sec_per_step, ev_ms):
         wl = self.wl
         tflops = self.flops / sec_per_step / 1e12
         gbs = self.bytes / sec_per_step / 1e9
-        launch_s = ev_ms / 1e3 / self.launches
+        launch_s = statistics.fmean(ev_ms) / 1e3 / self.launches
         if self.decode:
             achieved = self.bytes / self.launches / launch_s / 1e9
             roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name))
+                        frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(self.label))
             metric, value, unit = "decode HBM GB/s at 1M KV", gbs, "GB/s"
             if wl.kv_dtype == "fp8":
                 metric = "decode HBM GB/s at 1M KV (8-bit KV cache)"
+        elif wl.dtype == "fp32":
+            # a latency-bound 16-workgroup launch on the fp32 vector ALUs
+            achieved = self.flops / self.launches / launch_s / 1e12
+            roof = dict(bound="alu", achieved=round(achieved, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / PEAK_FP32_TFLOPS, 5), traffic=measured_traffic(self.label))
+            metric, value, unit = "attn fwd TFLOP/s, fp32 inputs (latency-bound tiny ring)", tflops, "TFLOP/s"
         else:
             achieved = self.flops / self.launches / launch_s / 1e12
-            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
-                        frac=round(achieved / peak, 4), traffic=measured_traffic(wl.name))
+            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(self.label))
             metric, value, unit = "causal attn fwd TFLOP/s (% MFMA peak) per GPU", tflops, "TFLOP/s"
             if wl.window or wl.anchor:
                 metric = "local-window + anchor attn fwd TFLOP/s over visible pairs per GPU"
             elif wl.doc_mean:
                 metric = "packed-document attn fwd TFLOP/s over visible pairs per GPU"
-        return dict(workload=wl.name, metric=metric, value=round(value, 2), unit=unit,
-                    ms_per_step=round(sec_per_step * 1e3, 4),
+        mode = "split-KV + merge" if self.decode else ("in place" if self.label.startswith("inplace:")
+                                                      else "staged ring (side-stream double buffer)")
+        return dict(workload=self.label, mode=mode, metric=metric, value=round(value, 2), unit=unit,
+                    **self._timing(sec_per_step, ev_ms),
                     tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1),
-                    tflops=round(tflops, 2), gbs=round(gbs, 1),
+                    tflops=round(tflops, 3), gbs=round(gbs, 1),
                     launches_per_step=self.launches, roofline=roof)
 
 
@@ -268,6 +380,7 @@ class BackwardRun(WorkloadRun):
         torch, ra, wl = self.torch, self.ra, self.wl
         from long_context_blockwise_amd import inputs
 
+        self.label = "bwd:" + name
         self.out, self.state = ra.ring_attn_fwd(self.x.q, self.chunks, wl.causal, wl.q_offset,
                                                 flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True, ctx=self.ctx,
                                                 **self.masks)
@@ -290,32 +403,45 @@ class BackwardRun(WorkloadRun):
     def result(self, sec_per_step, ev_ms):
         wl = self.wl
         tflops = self.flops / sec_per_step / 1e12
-        achieved = self.flops / (ev_ms / 1e3) / 1e12
+        achieved = self.flops / (statistics.fmean(ev_ms) / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("bwd:" + wl.name),
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(self.label),
                     kernels="bwd_pre + bwd_dq + bwd_dkdv per step (traffic: per step)")
         metric = "causal attn bwd TFLOP/s (dQ, dK, dV) per GPU"
         if wl.doc_mean:
             metric = "packed-document attn bwd TFLOP/s (dQ, dK, dV) over visible pairs per GPU"
         elif wl.window or wl.anchor:
             metric = "local-window + anchor attn bwd TFLOP/s (dQ, dK, dV) over visible pairs per GPU"
-        return dict(workload="bwd:" + wl.name, metric=metric,
-                    value=round(tflops, 2), unit="TFLOP/s", ms_per_step=round(sec_per_step * 1e3, 4),
+        return dict(workload=self.label, mode="in place", metric=metric,
+                    value=round(tflops, 2), unit="TFLOP/s", **self._timing(sec_per_step, ev_ms),
                     tokens_per_s=round(wl.B * wl.Lq / sec_per_step, 1), tflops=round(tflops, 2),
                     launches_per_step=2 + len(self.chunks), roofline=roof)
 
 
-def cpu_baseline(name, budget_s=20.0):
+def make_run(label):
+    if label.startswith("bwd:"):
+        return BackwardRun(label[4:])
+    if label.startswith("inplace:"):
+        return WorkloadRun(label[8:], inplace=True)
+    return WorkloadRun(label)
+
+
+def cpu_baseline(name, x=None, budget_s=20.0):
     """Time the CPU oracle on a bounded, stratified row sample of a workload
-    (all heads and batches of the sampled rows) and scale to TFLOP/s."""
+    (all heads and batches of the sampled rows), scale to TFLOP/s, and
+    extrapolate the full workload's time from the sampled pairs.  `x` are the
+    workload's inputs (device tensors are copied to the host); by default
+    they are drawn on the host."""
     import numpy as np
 
     import oracle
     from long_context_blockwise_amd import inputs
 
     wl = inputs.WORKLOADS[name]
-    x = inputs.make(wl, "cpu")
-    chunks = x.chunks()
+    if x is None:
+        x = inputs.make(wl, "cpu")
+    q = x.q.cpu()
+    chunks = [tuple(t.cpu() if hasattr(t, "cpu") else t for t in c) for c in x.chunks()]
     rows_all = inputs.sample_rows(wl.Lq, tile=max(1, wl.Lq // 2048), seed=1)
     rng = np.random.default_rng(0)
     rng.shuffle(rows_all)
@@ -323,7 +449,7 @@ def cpu_baseline(name, budget_s=20.0):
     while spent < budget_s / 2 and len(done_rows) < len(rows_all):
         rows = sorted(rows_all[len(done_rows):len(done_rows) + n])
         t0 = time.perf_counter()
-        oracle.attention(x.q, chunks, wl.q_offset, wl.causal, rows=rows)
+        oracle.attention(q, chunks, wl.q_offset, wl.causal, rows=rows)
         dt = time.perf_counter() - t0
         done_rows += rows
         t_total += dt
@@ -331,10 +457,210 @@ def cpu_baseline(name, budget_s=20.0):
         n *= 2
     pairs = visible_pairs(wl, done_rows) * wl.Hq
     flops = pairs * 2 * (wl.d_qk + wl.d_v)
+    full_flops, _ = algorithmic(wl)
+    model, affinity = host_cpu()
     return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=oracle.threads(),
                 kind="oracle",
-                sample=f"{len(done_rows)} of {wl.Lq} query rows (all {wl.B}x{wl.Hq} batch-heads) of "
-                       f"{wl.name}, fp64 C oracle, {t_total:.1f} s, {flops / 1e9:.1f} GFLOP")
+                sample=f"{len(done_rows)} of {wl.Lq} query rows (stratified, all {wl.B}x{wl.Hq} batch-heads) of "
+                       f"{wl.name}, fp64 C oracle, {t_total:.1f} s, {flops / 1e9:.1f} GFLOP",
+                extrapolated_full_s=round(t_total * full_flops / flops, 1),
+                host_cpu=model, affinity_cores=affinity)
+
+
+# --------------------------------------------------------------------------- #
+# rocprofv3 harness (--profile)
+# --------------------------------------------------------------------------- #
+# Counter groups: one rocprofv3 run each (at most 8 SQ and 2 GRBM counters
+# per run; FETCH_SIZE and WRITE_SIZE take 3 and 2 of the 4 TCC slots, so
+# each has a run of its own).
+PMC_PIPES = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU "
+             "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA")
+PMC_LDS = "GRBM_GUI_ACTIVE SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_WAVES"
+PMC_FETCH = "FETCH_SIZE"
+PMC_WRITE = "WRITE_SIZE"
+
+# The kernel each workload's roofline is priced on (a substring of the
+# demangled name rocprofv3 reports), and whether it is priced in flops or bytes.
+DOMINANT = {
+    "ring_1m_gqa32x8_d128": ("fwd_bf16_kernel<128, 64, 4, 1, 2, 0>", "mfma"),
+    "prefill_bf16_h32_d128": ("fwd_bf16_kernel<128, 64, 4, 1, 2, 0>", "mfma"),
+    "mla_h16_d512": ("fwd_bf16_half_kernel", "mfma"),
+    "decode_b4_gqa32x8_cache1m": ("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>", "hbm"),
+    "decode_b4_gqa32x8_cache1m_fp8": ("fwd_fp8kv_kernel", "hbm"),
+    "bwd:prefill_bf16_h32_d128": ("bwd_", "mfma"),
+}
+
+
+def _rocprof_run(args, outdir, tag, child, timeout):
+    """One rocprofv3 run of `child` (argv of this script) with `args`;
+    returns the output directory of the run."""
+    d = os.path.join(outdir, "raw", tag)
+    os.makedirs(d, exist_ok=True)
+    cmd = ["rocprofv3", *args, "-d", d, "-o", tag, "--output-format", "csv", "--", sys.executable, *child]
+    print("[profile] " + " ".join(shlex.quote(c) for c in cmd), file=sys.stderr, flush=True)
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    r = subprocess.run(cmd, cwd=ROOT, env=env, timeout=timeout, capture_output=True, text=True)
+    with open(os.path.join(d, "rocprof.log"), "w") as f:
+        f.write(r.stdout + "\n---- stderr ----\n" + r.stderr)
+    if r.returncode != 0:
+        # rocprofv3 may exit non-zero after a complete run; the CSVs decide
+        print(f"[profile] rocprofv3 exit {r.returncode} ({tag}); see {d}/rocprof.log", file=sys.stderr, flush=True)
+    return d, " ".join(shlex.quote(c) for c in cmd)
+
+
+def _csv_rows(d, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _counters(d, pattern):
+    """{counter: [value per dispatch]} and the dispatch durations (ns) of the
+    kernels whose name contains `pattern`."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if pattern not in r.get("Kernel_Name", ""):
+            continue
+        key = r["Dispatch_Id"]
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    vals = {}
+    for disp in per.values():
+        for k, v in disp.items():
+            vals.setdefault(k, []).append(v)
+    return vals, len(per)
+
+
+def profile(names, outdir, steps):
+    os.makedirs(outdir, exist_ok=True)
+    me = os.path.relpath(os.path.abspath(__file__), ROOT)
+    # copy calibration: a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB)
+    cal_bytes = 1 << 30
+    calib = {}
+    for tag, grp in (("copy_fetch", PMC_FETCH), ("copy_write", PMC_WRITE)):
+        d, _ = _rocprof_run(["--pmc", *grp.split()], outdir, tag, [me, "--copy-calibration", str(cal_bytes)], 300)
+        vals, _n = _counters(d, "neg")
+        name = grp.split()[0]
+        if vals.get(name):
+            calib[name] = cal_bytes / (max(vals[name]) * 1024.0)  # true bytes per counted byte
+    summary = {"calibration": calib, "workloads": {}}
+    for name in names:
+        base = name.split(":", 1)[-1]
+        child = [me, "--workload", name, "--secondary", "", "--no-cpu", "--steps", str(steps), "--warmup", "1",
+                 "--no-clock"]
+        tagb = name.replace(":", "_")
+        runs = {}
+        runs["trace"] = _rocprof_run(["--kernel-trace", "--stats"], outdir, tagb + "_trace", child, 900)
+        for key, grp in (("pipes", PMC_PIPES), ("lds", PMC_LDS), ("fetch", PMC_FETCH), ("write", PMC_WRITE)):
+            runs[key] = _rocprof_run(["--pmc", *grp.split()], outdir, f"{tagb}_{key}", child, 900)
+        summary["workloads"][name] = write_profile_summary(name, runs, calib, outdir, steps)
+    with open(os.path.join(outdir, "profile_summary.json"), "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary), flush=True)
+
+
+def write_profile_summary(name, runs, calib, outdir, steps):
+    from long_context_blockwise_amd import inputs
+
+    pattern, bound = DOMINANT.get(name, ("", "mfma"))
+    base = name.split(":", 1)[-1]
+    wl = inputs.WORKLOADS[base]
+    stats = _csv_rows(runs["trace"][0], "kernel_stats.csv")
+    traces = [r for r in _csv_rows(runs["trace"][0], "kernel_trace.csv") if pattern in r.get("Kernel_Name", "")]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in traces]
+    avg_ns = statistics.fmean(durs) if durs else float("nan")
+    pipes, n_disp = _counters(runs["pipes"][0], pattern)
+    lds, _ = _counters(runs["lds"][0], pattern)
+    fetch, _ = _counters(runs["fetch"][0], pattern)
+    write, _ = _counters(runs["write"][0], pattern)
+    mean = lambda v: statistics.fmean(v) if v else float("nan")
+    flops, kv_bytes = algorithmic(wl)
+    if name.startswith("bwd:"):
+        flops = visible_pairs(wl) * wl.Hq * 2 * (3 * wl.d_qk + 2 * wl.d_v)
+    # launches of the dominant kernel per step (the trace covers warmup + steps)
+    n_steps = steps + 1
+    per_step = len(durs) / n_steps if durs else float("nan")
+    grbm = mean(pipes.get("GRBM_GUI_ACTIVE", [])) / N_XCD  # cycles (the counter sums the XCDs)
+    clock_ghz = grbm / avg_ns if durs else float("nan")
+    mfma_busy = mean(pipes.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (grbm * N_SIMD)
+    valu_busy = mean(pipes.get("SQ_ACTIVE_INST_VALU", [])) / (grbm * N_CU)
+    coexec = mean(pipes.get("SQ_VALU_MFMA_COEXEC_CYCLES", [])) / (grbm * N_SIMD)
+    mops = mean(pipes.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512.0
+    lds_busy = mean(lds.get("SQ_ACTIVE_INST_LDS", [])) / (grbm * N_CU)
+    fb = mean(fetch.get("FETCH_SIZE", [])) * 1024.0 * calib.get("FETCH_SIZE", float("nan"))
+    wb = mean(write.get("WRITE_SIZE", [])) * 1024.0 * calib.get("WRITE_SIZE", float("nan"))
+    if name.startswith("bwd:"):
+        launches = 1.0  # priced per step over all its kernels (pattern "bwd_")
+        alg_flops_launch = flops
+        alg_bytes_launch = kv_bytes
+    else:
+        launches = per_step if per_step == per_step else 1.0
+        alg_flops_launch = flops / launches
+        alg_bytes_launch = kv_bytes / launches
+    if name.startswith("bwd:"):
+        step_ns = sum(durs) / n_steps if durs else float("nan")
+        achieved_tflops = alg_flops_launch / step_ns / 1e3
+        fb_step, wb_step = fb * per_step, wb * per_step
+    else:
+        achieved_tflops = alg_flops_launch / avg_ns / 1e3
+        fb_step, wb_step = fb, wb
+    achieved_gbs = alg_bytes_launch / avg_ns
+    kname = traces[0]["Kernel_Name"] if traces else pattern
+    short = kname.replace("void ", "").replace("ra::(anonymous namespace)::", "").split("(")[0].replace(" ", "")
+    if name.startswith("bwd:"):
+        short = "bwd_pre+bwd_dq+bwd_dkdv"
+    fname = "".join(c if c.isalnum() or c in "_-" else "_" for c in short.split("<")[0]) + "_" + name.replace(":", "_")
+    path = os.path.join(outdir, fname + ".md")
+    lines = [f"# {short} on `{name}`", "",
+             f"Workload: {wl.name} (B={wl.B}, Hq={wl.Hq}, Hkv={wl.Hkv}, d={wl.d_qk}, {wl.P} chunks of "
+             f"{wl.chunk_len}, Lq={wl.Lq}, q_offset={wl.q_offset}, causal={wl.causal}, "
+             f"kv={wl.kv_dtype or wl.dtype}).", "",
+             "Made by `python bench.py --profile " + name + "`, which ran:", ""]
+    for key, (_d, cmd) in runs.items():
+        lines.append(f"- {key}: `{cmd}`")
+    lines += ["", "## Kernel trace (rocprofv3 --stats, raw rows)", "",
+              "| Name | Calls | TotalDurationNs | AverageNs | MinNs | MaxNs |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r.get('Name', '')[:110]}` | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
+                     f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} |")
+    fmt = lambda v, p=3: "n/a" if v != v else f"{v:.{p}g}" if abs(v) < 1e4 else f"{v:.4e}"
+    lines += ["", f"## Dominant kernel `{short}` (derived; {len(durs)} dispatches in the trace, "
+                  f"{n_disp} in each counter run)", "",
+              "| Quantity | Value | How |", "|---|---|---|",
+              f"| average duration | {fmt(avg_ns / 1e3, 5)} µs | kernel trace, dispatches matching `{pattern}` |",
+              f"| launches per step | {fmt(per_step)} | dispatches / ({steps} timed + 1 warmup steps) |",
+              f"| shader clock | {fmt(clock_ghz, 4)} GHz | GRBM_GUI_ACTIVE / {N_XCD} XCDs / average duration |",
+              f"| MFMA busy | {fmt(100 * mfma_busy, 4)} % | SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/{N_XCD} x "
+              f"{N_SIMD} SIMDs) |",
+              f"| VALU active | {fmt(100 * valu_busy, 4)} % | SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE/{N_XCD} x "
+              f"{N_CU} CUs) |",
+              f"| MFMA and VALU together | {fmt(100 * coexec, 4)} % | SQ_VALU_MFMA_COEXEC_CYCLES / "
+              f"(GRBM_GUI_ACTIVE/{N_XCD} x {N_SIMD}) |",
+              f"| LDS active | {fmt(100 * lds_busy, 4)} % | SQ_ACTIVE_INST_LDS / (GRBM_GUI_ACTIVE/{N_XCD} x {N_CU}) |",
+              f"| MFMA flops executed per dispatch | {fmt(mops)} | SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 |",
+              f"| algorithmic flops per launch | {fmt(alg_flops_launch)} | visible pairs x 2(d_qk+d_v) per head |",
+              f"| VALU instructions per MFMA | {fmt(mean(pipes.get('SQ_INSTS_VALU', [])) / max(mean(pipes.get('SQ_INSTS_MFMA', [])), 1))} | SQ_INSTS_VALU / SQ_INSTS_MFMA |",
+              f"| transcendental (exp) per MFMA | {fmt(mean(lds.get('SQ_INSTS_VALU_TRANS_F32', [])) / max(mean(pipes.get('SQ_INSTS_MFMA', [])), 1))} | SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA |",
+              f"| LDS bank conflicts / LDS instructions | {fmt(mean(lds.get('SQ_LDS_BANK_CONFLICT', [])) / max(mean(lds.get('SQ_INSTS_LDS', [])), 1))} | cycles per instruction |",
+              f"| HBM read bytes per dispatch | {fmt(fb)} | FETCH_SIZE KiB x 1024 x {fmt(calib.get('FETCH_SIZE', float('nan')), 4)} (copy calibration) |",
+              f"| HBM write bytes per dispatch | {fmt(wb)} | WRITE_SIZE KiB x 1024 x {fmt(calib.get('WRITE_SIZE', float('nan')), 4)} (copy calibration) |",
+              f"| algorithmic K/V+Q+out bytes per launch | {fmt(alg_bytes_launch)} | K+V once, Q, out |"]
+    if bound == "mfma":
+        lines += [f"| **achieved (algorithmic)** | **{fmt(achieved_tflops, 5)} TFLOP/s = "
+                  f"{fmt(100 * achieved_tflops / PEAK_BF16_TFLOPS, 4)} % of {PEAK_BF16_TFLOPS}** | "
+                  "algorithmic flops per launch / average duration |"]
+    else:
+        lines += [f"| **achieved (algorithmic)** | **{fmt(achieved_gbs, 5)} GB/s = "
+                  f"{fmt(100 * achieved_gbs / PEAK_HBM_GBS, 4)} % of {PEAK_HBM_GBS:.0f}** | "
+                  "algorithmic bytes per launch / average duration |",
+                  f"| measured HBM rate | {fmt((fb + wb) / avg_ns, 5)} GB/s | (read + write bytes) / average duration |"]
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return dict(file=path, kernel=short, avg_us=avg_ns / 1e3, launches_per_step=per_step, clock_ghz=clock_ghz,
+                mfma_busy=mfma_busy, valu_busy=valu_busy, coexec=coexec, lds_busy=lds_busy,
+                fetch_bytes=fb_step, write_bytes=wb_step, traffic_bytes=fb_step + wb_step,
+                achieved_tflops=achieved_tflops, achieved_gbs=achieved_gbs, kernel_digest=kernel_digest())
 
 
 def main():
@@ -344,7 +670,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--secondary", default=SECONDARY, help="comma list, '' for none")
+    ap.add_argument("--secondary-steps", type=int, default=0, help="timed steps of each secondary (default steps/2)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-clock", action="store_true", help="do not sample the board clock")
+    ap.add_argument("--profile", default="", metavar="NAMES",
+                    help="run the rocprofv3 harness on these workloads (comma list) and write summaries")
+    ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--profile-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run one plain elementwise copy of BYTES bytes (reads BYTES, writes "
                          "BYTES) to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -353,6 +685,9 @@ def main():
         print("bench.py measures one device's ring share on one GPU; --gpus must be 1 "
               "(the multi-GPU ring is not part of this build)", file=sys.stderr)
         sys.exit(2)
+    if args.profile:  # the parent only starts rocprofv3 runs; it never touches the GPU itself
+        profile([s for s in args.profile.split(",") if s], args.profile_out, args.profile_steps)
+        return
 
     import torch
 
@@ -367,28 +702,52 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
         return
     props = torch.cuda.get_device_properties(0)
-    run = WorkloadRun(args.workload)
-    sec, ev_ms = run.time(args.steps, args.warmup)
+    run = make_run(args.workload)
+    clock = {}
+
+    def sample():  # the board clock half a second into the timed steps
+        time.sleep(0.5)
+        t0 = time.perf_counter()
+        clock["sclk_mhz"] = sample_sclk_mhz()
+        clock["t"] = (t0, time.perf_counter())
+    t_start = time.perf_counter()
+    sec, ev_ms = run.time(args.steps, args.warmup, during=None if args.no_clock else sample)
+    t_end = time.perf_counter()
     head = run.result(sec, ev_ms)
     print(f"[bench] {head}", file=sys.stderr, flush=True)
+    x_head = None if args.no_cpu else run.x
+    run.x = None
     del run
     torch.cuda.empty_cache()
+    # was the clock read while the timed steps were still running?
+    t_timed0 = t_end - sec * args.steps
+    clock_inside = bool(clock.get("t")) and clock["t"][0] >= t_timed0 and clock["t"][1] <= t_end
 
     secondary = []
+    sec_steps = args.secondary_steps or max(3, args.steps // 2)
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = BackwardRun(name[4:]) if name.startswith("bwd:") else WorkloadRun(name)
-        s2, e2 = r.time(max(3, args.steps // 2), max(1, args.warmup))
+        r = make_run(name)
+        s2, e2 = r.time(sec_steps, max(1, args.warmup))
         res = r.result(s2, e2)
         print(f"[bench] {res}", file=sys.stderr, flush=True)
         secondary.append(res)
         del r
         torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu else cpu_baseline(args.workload)
-    wl = head
+    cpu = None
+    if not args.no_cpu:
+        from long_context_blockwise_amd import inputs
+
+        wl0 = inputs.WORKLOADS[args.workload.split(":", 1)[-1]]
+        host = inputs.Inputs(wl0, x_head.q.cpu(), [k.cpu() for k in x_head.ks], [v.cpu() for v in x_head.vs],
+                             x_head.starts)
+        del x_head
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(wl0.name, host)
     from long_context_blockwise_amd import inputs
 
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.WORKLOADS[args.workload.split(":", 1)[-1]]
+    model, affinity = host_cpu()
     line = {
         "metric": head["metric"],
         "value": head["value"],
@@ -402,12 +761,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk,
+        "config": {"workload": head["workload"], "mode": head["mode"], "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk,
                    "chunk_len": w.chunk_len, "P": w.P, "Lq": w.Lq, "q_offset": w.q_offset,
                    "causal": w.causal, "tokens_per_s": head["tokens_per_s"],
-                   "gpu": props.name, "cus": props.multi_processor_count},
+                   "ms_per_step_median": head["ms_per_step_median"], "ms_per_step_min": head["ms_per_step_min"]},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "run_info": {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+                     "cus": props.multi_processor_count, "sclk_mhz_sampled": clock.get("sclk_mhz"),
+                     "sclk_sampled_during_timed_steps": clock_inside,
+                     "sclk_max_mhz": 2400, "host_cpu": model, "host_affinity_cores": affinity,
+                     "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                     "source_digest": source_digest(), "git_rev": git_revision()},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
