@@ -247,6 +247,32 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
                   float *l_out, float *O_out, void *workspace,
                   size_t ws_bytes, void *stream);
 
+/* Bytes of the static device scratch behind ring_attn_fwd_noalloc (96 MiB
+ * per GPU). */
+#define RA_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+/* ring_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It allocates nothing: the
+ * scratch ring_attn_fwd would take from `workspace` (staging buffers,
+ * the carried state, split-KV partials) comes from a file-scope device
+ * array of RA_NOALLOC_SCRATCH_BYTES, one per GPU, placed when the library
+ * is loaded on that GPU and held until the process ends; its address is
+ * looked up when a context is created on the device.  Arguments, results,
+ * ownership of the caller's buffers and the errors are those of
+ * ring_attn_fwd, plus RA_ERR_WORKSPACE (nothing enqueued) when the call
+ * needs more scratch than RA_NOALLOC_SCRATCH_BYTES (ring_attn_workspace_size
+ * tells how much), and RA_ERR_HIP when the scratch of ctx's device could
+ * not be found.  Every call on one GPU shares that GPU's scratch and
+ * leaves its contents behind (no call relies on it being zero): calls
+ * whose device work overlaps -- on different streams without ordering
+ * between them, or from several host threads -- race on it. */
+int ring_attn_fwd_noalloc(ra_ctx *ctx, const ra_desc *d, const void *q,
+                          int64_t Lq, const ra_kv_chunk *chunks, int P,
+                          int causal, int64_t q_offset, uint32_t flags,
+                          void *out, float *m_out, float *l_out,
+                          float *O_out, void *stream);
+
 /* Gradients of one KV chunk (fp32, dense [B, len, Hkv, d], device). */
 typedef struct ra_kv_grad {
     float *dk; /* [B, len, Hkv, d_qk] */

@@ -24,12 +24,14 @@ from .ring_attn import (  # noqa: F401
     RA_FLAG_STAGE,
     RA_FP8_E4M3,
     RA_KV_SCALE_BLOCK,
+    RA_NOALLOC_SCRATCH_BYTES,
     RA_OK,
     RingAttnContext,
     RingAttnError,
     ring_attn_bwd,
     ring_attn_bwd_workspace_size,
     ring_attn_fwd,
+    ring_attn_fwd_noalloc,
     ring_attn_last_error,
     ring_attn_merge,
     ring_attn_plan,

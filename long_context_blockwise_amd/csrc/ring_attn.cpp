@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -37,9 +38,36 @@ struct ra_ctx {
     hipEvent_t join;      // side stream's last copy
 };
 
+// Scratch of ring_attn_fwd_noalloc: a file-scope device array, one copy per
+// GPU (the loader places it when the library's code object is loaded on the
+// device, and it stays until the process ends).  Host code never passes the
+// array's name to a kernel or a copy: that name is a host-side stand-in.  The
+// device address of each GPU's copy is looked up once per device, with that
+// device current, when a context is created there, and kept below.
+static __device__ __align__(256) char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;           // device address of this GPU's copy of `scratch`
+    hipError_t err = hipSuccess;   // result of the lookup
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+// Look up this device's copy of `scratch` (the device must be current).
+void scratch_lookup(int device) {
+    if (device < 0 || device >= kMaxScratchDevices) return;
+    ScratchSlot &sl = g_scratch[device];
+    std::call_once(sl.once, [&sl] {
+        void *p = nullptr;
+        sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        sl.ptr = sl.err == hipSuccess ? p : nullptr;
+    });
+}
 
 int fail(int code, const char *fmt, ...) {
     char buf[512];
@@ -421,6 +449,9 @@ int ring_attn_ctx_create(int device, ra_ctx **out) {
             return hip_fail(e, "hipEventCreateWithFlags");
         }
     }
+    // the static scratch of ring_attn_fwd_noalloc on this device (its failure
+    // only disables that entry point, which reports it)
+    scratch_lookup(device);
     *out = c;
     return RA_OK;
 }
@@ -471,9 +502,14 @@ int ring_attn_workspace_size(const ra_desc *d, int64_t Lq, const ra_kv_chunk *ch
     return RA_OK;
 }
 
-int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, const ra_kv_chunk *chunks, int P,
-                  int causal, int64_t q_offset, uint32_t flags, void *out, float *m_out, float *l_out, float *O_out,
-                  void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// The forward of ring_attn_fwd and ring_attn_fwd_noalloc: validation, the
+// plan, then the launches, with `workspace` as scratch.  Enqueues nothing
+// on error and allocates nothing.
+static int fwd_impl(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, const ra_kv_chunk *chunks, int P,
+                    int causal, int64_t q_offset, uint32_t flags, void *out, float *m_out, float *l_out,
+                    float *O_out, void *workspace, size_t ws_bytes, void *stream, bool noalloc) {
     if (!ctx) return fail(RA_ERR_INVALID_ARG, "ctx is NULL");
     Strides st;
     int rc = check_desc(d, Lq, &st);
@@ -495,6 +531,10 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     if ((rc = check_labels(d, Lq, chunks, P))) return rc;
     Plan pl;
     if ((rc = make_plan(d, Lq, chunks, P, causal, q_offset, flags, have_state, &pl))) return rc;
+    if (noalloc && pl.total > ws_bytes)
+        return fail(RA_ERR_WORKSPACE,
+                    "these arguments need %zu bytes of scratch; the static scratch of ring_attn_fwd_noalloc "
+                    "holds %zu (use ring_attn_fwd with a workspace)", pl.total, ws_bytes);
     if (pl.total > 0 && (!workspace || ws_bytes < pl.total))
         return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total, ws_bytes);
     if (pl.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
@@ -657,6 +697,29 @@ int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
         if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess) return hip_fail(e, "join");
     }
     return RA_OK;
+}
+
+extern "C" {
+
+int ring_attn_fwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, const ra_kv_chunk *chunks, int P,
+                  int causal, int64_t q_offset, uint32_t flags, void *out, float *m_out, float *l_out, float *O_out,
+                  void *workspace, size_t ws_bytes, void *stream) {
+    return fwd_impl(ctx, d, q, Lq, chunks, P, causal, q_offset, flags, out, m_out, l_out, O_out, workspace,
+                    ws_bytes, stream, false);
+}
+
+int ring_attn_fwd_noalloc(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, const ra_kv_chunk *chunks,
+                          int P, int causal, int64_t q_offset, uint32_t flags, void *out, float *m_out,
+                          float *l_out, float *O_out, void *stream) {
+    if (!ctx) return fail(RA_ERR_INVALID_ARG, "ctx is NULL");
+    if (ctx->device < 0 || ctx->device >= kMaxScratchDevices)
+        return fail(RA_ERR_UNSUPPORTED, "the static scratch covers devices 0..%d", kMaxScratchDevices - 1);
+    const ScratchSlot &sl = g_scratch[ctx->device];
+    if (!sl.ptr)
+        return fail(RA_ERR_HIP, "static scratch of device %d unavailable: %s", ctx->device,
+                    hipGetErrorString(sl.err));
+    return fwd_impl(ctx, d, q, Lq, chunks, P, causal, q_offset, flags, out, m_out, l_out, O_out, sl.ptr,
+                    (size_t)RA_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 // Row statistics of the backward: (lse2, D) per (b, h, t).

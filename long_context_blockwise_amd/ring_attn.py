@@ -35,7 +35,8 @@ RA_CHUNK_SKIP, RA_CHUNK_FULL, RA_CHUNK_DIAG = 0, 1, 2
 EXPORTS = ("ring_attn_version", "ring_attn_last_error", "ring_attn_ctx_create",
            "ring_attn_ctx_destroy", "ring_attn_ring_order", "ring_attn_plan",
            "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge",
-           "ring_attn_bwd_workspace_size", "ring_attn_bwd")
+           "ring_attn_bwd_workspace_size", "ring_attn_bwd", "ring_attn_fwd_noalloc")
+RA_NOALLOC_SCRATCH_BYTES = 96 << 20  # static scratch per GPU behind ring_attn_fwd_noalloc
 
 
 class RingAttnError(RuntimeError):
@@ -98,6 +99,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ring_attn_fwd.argtypes = [vp, ctypes.POINTER(ra_desc), vp, i64, ctypes.POINTER(ra_kv_chunk),
                                       ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp,
                                       vp, sz, vp]
+        lib.ring_attn_fwd_noalloc.argtypes = [vp, ctypes.POINTER(ra_desc), vp, i64, ctypes.POINTER(ra_kv_chunk),
+                                              ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp,
+                                              vp]
         lib.ring_attn_merge.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_int, vp]
         lib.ring_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(ra_desc), i64, ctypes.POINTER(sz)]
@@ -105,7 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp, vp,
                                       ctypes.POINTER(ra_kv_grad), vp, sz, vp]
         for name in ("ring_attn_ctx_create", "ring_attn_ctx_destroy", "ring_attn_ring_order",
-                     "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge",
+                     "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_fwd_noalloc",
+                     "ring_attn_merge",
                      "ring_attn_bwd_workspace_size", "ring_attn_bwd"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -316,6 +321,30 @@ def ring_attn_fwd(q, chunks, causal: bool = False, q_offset: int = 0, *, flags: 
                              int(bool(causal)), int(q_offset), int(flags), ptr(out), ptr(m), ptr(l),
                              ptr(O), ptr(workspace) if ws_bytes else None,
                              ws_bytes if ws_bytes else 0, stream.cuda_stream))
+    return out, state
+
+
+def ring_attn_fwd_noalloc(q, chunks, causal: bool = False, q_offset: int = 0, *, out, state=None,
+                          flags: int = 0, scale: float = 0.0, ctx: Optional[RingAttnContext] = None,
+                          stream=None, window: int = 0, anchor: int = 0, q_seg=None, k_segs=None):
+    """``ring_attn_fwd`` on the library's static per-GPU scratch: no workspace
+    and no device allocation in the call.  ``out`` (and ``state``, a tuple
+    ``(m, l, O)``, if wanted) are the caller's buffers and must be given;
+    returns ``(out, state)``."""
+    import torch
+
+    Lq = q.shape[1]
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    d, arr = make_desc(q, chunks, scale, out, window, anchor, q_seg, k_segs)
+    if ctx is None:
+        ctx = default_context(dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    m, l, O = state if state is not None else (None, None, None)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(load().ring_attn_fwd_noalloc(ctx.handle, ctypes.byref(d), q.data_ptr(), Lq, arr, len(chunks),
+                                        int(bool(causal)), int(q_offset), int(flags), ptr(out), ptr(m), ptr(l),
+                                        ptr(O), stream.cuda_stream))
     return out, state
 
 
