@@ -61,6 +61,14 @@
 #ifndef RA_TUNE_FUSE_VALU
 #define RA_TUNE_FUSE_VALU 7
 #endif
+// d = 512: 32-row waves over the whole head (1) or wave pairs splitting it
+// (0); VALU instructions placed after each O^T MFMA of the wide kernel.
+#ifndef RA_TUNE_WIDE
+#define RA_TUNE_WIDE 1
+#endif
+#ifndef RA_TUNE_WIDE_VALU
+#define RA_TUNE_WIDE_VALU 3
+#endif
 
 namespace ra {
 namespace {
@@ -683,6 +691,243 @@ void fwd_bf16_half_kernel(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide heads (d = 512): one wave per SIMD holding 32 query rows with the whole
+// head dimension -- Q as 32 B operands (128 VGPRs), O^T as 16 accumulator
+// blocks of 32x32 (256 AGPRs) -- so no wave needs another's partial scores
+// and every K/V fragment read from LDS feeds 32 rows.  Four waves (128 rows)
+// share each 32-key K/V tile.
+//
+// With one wave per SIMD nothing else fills the matrix cores while a wave
+// turns scores into probabilities, so the wave overlaps them itself: K runs
+// one tile ahead of V, and iteration j computes the scores of tile j+1 and
+// then the O^T MFMAs of tile j with the softmax of tile j+1 interleaved
+// between them.  The rare O rescale follows the MFMAs of tile j.  Every tile
+// of the workgroup's range is computed: keys a row may not see are masked to
+// zero probability (a branch around a tile would join two copies of O, which
+// the compiler would then copy out of the AGPRs on every tile).
+// ---------------------------------------------------------------------------
+namespace wide {
+using C = Cfg<512, 32, 4, 1>;
+static_assert(C::KB == 1, "one 32-key block per tile");
+
+// S^T = K Q^T of one 32-key tile over the whole head, in VGPRs.  Written as
+// inline asm so that the scores stay out of the AGPRs, which O fills (the
+// builtin's accumulator takes the AGPR form in this kernel, and there are no
+// 16 AGPRs to spare).  Consecutive MFMAs accumulate into the same registers,
+// which the hardware chains back to back; the s_nops after the last one
+// cover the wait states before a VALU instruction may read the result,
+// which the compiler does not see inside asm.
+__device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[C::DS], f32x16 &s) {
+    constexpr int N = C::DS;
+    constexpr int PF = C::PF;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF; ++n) fr[n] = kfrag<C>(kt, kaddr, n, 0);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        if (n == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "v"(qf[0]));
+        else if (n < N - 1)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "v"(qf[n]));
+        else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+                         : "+v"(s)
+                         : "v"(fr[n % PF]), "v"(qf[n]));
+        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, n + PF, 0);
+    }
+}
+
+// O^T += V^T P^T of tile j (pf, vt) with the softmax of tile j+1 (its
+// masked scores s1) interleaved: row maximum, new reference and the
+// probabilities pn.  Returns the rescale factor alpha of O, which the caller
+// applies after these MFMAs.  Program order is kept exactly (a scheduling
+// barrier after every step): each step issues one MFMA, the LDS reads of the
+// fragment PF steps ahead, and a few vector instructions of the softmax, so
+// the reads are in flight while the MFMAs run and the vector work fills the
+// issue slots between them.
+template <int... Ns>
+__device__ inline void pv_softmax_steps(std::integer_sequence<int, Ns...>, const char *vt,
+                                        const int (&vaddr)[2][C::NVD], const bf16x8 (&pf)[2], f32x16 (&o)[C::DB],
+                                        const f32x16 &s1, float c2, float &m_run, float &m_true, float &lsum,
+                                        bf16x8 (&pn)[2], float &alpha) {
+    constexpr int N = 2 * C::DB;  // 32 MFMAs: step n is (ks = n / DB, db = n % DB)
+    constexpr int PF = C::PF;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF; ++n) fr[n] = vfrag<C>(vt, vaddr, n / C::DB, n % C::DB);
+    float mx = kNegInf, mref = 0.f, ls = 0.f;
+    float e[16];
+    u32x4 pk[2];
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](auto nn) {
+        constexpr int n = decltype(nn)::value;
+        o[n % C::DB] = mfma(fr[n % PF], pf[n / C::DB], o[n % C::DB]);
+        if constexpr (n + PF < N) fr[n % PF] = vfrag<C>(vt, vaddr, (n + PF) / C::DB, (n + PF) % C::DB);
+        if constexpr (n < 5) {  // row maximum of the tile: 16 scores in the lane ...
+            constexpr int i0 = 3 * n;
+            if constexpr (i0 + 2 < 16) mx = fmaxf(fmaxf(mx, s1[i0]), fmaxf(s1[i0 + 1], s1[i0 + 2]));
+            else mx = fmaxf(mx, s1[15]);
+        } else if constexpr (n == 5) {  // ... and its partner lane
+            mx = max_pair(fmaxf(mx, s1[15]));
+        } else if constexpr (n == 6) {  // new reference (moves rarely) and the rescale factor of O and l
+            const float mt = mx * c2;
+            m_true = fmaxf(m_true, mt);
+            const bool need = mt > m_run + kRescaleThreshold;
+            alpha = need ? exp2_fast(m_run - mt) : 1.f;
+            m_run = need ? mt : m_run;
+            mref = m_run == kNegInf ? 0.f : m_run;
+        } else if constexpr (n >= 7 && n < 23) {  // one probability per step
+            e[n - 7] = exp2_fast(__builtin_fmaf(s1[n - 7], c2, -mref));
+        } else if constexpr (n >= 23 && n < 31) {  // bf16 pairs and their sum
+            constexpr int k = n - 23;
+            ls += e[2 * k] + e[2 * k + 1];
+            pk[k / 4][k % 4] = pack_bf16(e[2 * k], e[2 * k + 1]);
+        } else if constexpr (n == 31) {
+            lsum = lsum * alpha + ls;
+            pn[0] = to_bf16x8(pk[0]);
+            pn[1] = to_bf16x8(pk[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    (step(ic<Ns>{}), ...);
+}
+
+__device__ inline void pv_softmax(const char *vt, const int (&vaddr)[2][C::NVD], const bf16x8 (&pf)[2],
+                                  f32x16 (&o)[C::DB], const f32x16 &s1, float c2, float &m_run, float &m_true,
+                                  float &lsum, bf16x8 (&pn)[2], float &alpha) {
+    static_assert(2 * C::DB == 32, "the softmax steps are laid out for 32 MFMAs");
+    pv_softmax_steps(std::make_integer_sequence<int, 2 * C::DB>{}, vt, vaddr, pf, o, s1, c2, m_run, m_true, lsum,
+                     pn, alpha);
+}
+
+// O *= alpha where the matrix cores keep it (AGPRs), for the rows that need it.
+__device__ inline void rescale_o(f32x16 (&o)[C::DB], float alpha) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x = o[db][i], t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t)
+                         : "v"(alpha));
+            o[db][i] = x;
+        }
+    asm volatile("s_nop 7" ::: "memory");
+}
+}  // namespace wide
+
+template <int NS_UNUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_wide_kernel(const FwdArgs a) {
+    using C = wide::C;
+    constexpr int D = 512, BN = 32;
+    constexpr int LPT = C::LOADS_PER_WAVE;  // loads of one K (or V) tile per wave
+    // V (two reads per fragment) in the low 64 KiB, where the ds_read offset
+    // field reaches every byte without an address add (the compiler lays the
+    // arrays out in the order of their names)
+    __shared__ __attribute__((aligned(1024))) char lds_a_v0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_a_v1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_b_k0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_b_k1[C::TILE];
+    auto kbuf = [&](auto u) -> char * {
+        if constexpr (decltype(u)::value % 2 == 0) return lds_b_k0;
+        else return lds_b_k1;
+    };
+    auto vbuf = [&](auto u) -> char * {
+        if constexpr (decltype(u)::value % 2 == 0) return lds_a_v0;
+        else return lds_a_v1;
+    };
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;
+    token_range(a, wt.p0 + 32 * w, wt.p0 + 32 * w + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * w + l32);
+
+    bf16x8 qf[C::DS];
+    load_q(a, wt, row, g, 0, qf);
+    f32x16 oacc[C::DB];
+    float m_run, m_true, lsum;
+    load_state<D>(a, row, g, true, 0, oacc, m_run, m_true, lsum);
+    const float c2 = a.scale_log2;
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+
+    int c_begin = 0, c_end = a.n_chunks, sub = 0;
+    if (a.split_mode) {
+        c_begin = wt.split / a.n_sub;
+        sub = wt.split % a.n_sub;
+        c_end = c_begin + 1;
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        // tiles past the end load nothing and zero-fill their buffer, so every
+        // iteration issues the same loads
+        auto tile_k0 = [&](int t) {
+            const int64_t k0 = kbeg + (int64_t)t * BN;
+            return k0 < kend ? k0 : kend;
+        };
+        auto load_k = [&](auto u, int t) { load_tile<C>(kbase, a.k_ss, tile_k0(t), kend, kbuf(u), w, lane); };
+        auto load_v = [&](auto u, int t) { load_tile<C>(vbase, a.v_ss, tile_k0(t), kend, vbuf(u), w, lane); };
+        auto full_of = [&](int t) {
+            return keys_all_seen(a, ch.start, kbeg + (int64_t)t * BN, BN, kend, wv_tlo, wv_thi);
+        };
+
+        // prologue: K and V of tile 0, K of tile 1; the softmax of tile 0
+        tile_barrier();  // the previous chunk's tiles are no longer read
+        load_k(ic<0>{}, 0);
+        load_v(ic<0>{}, 0);
+        load_k(ic<1>{}, 1);
+        wait_tiles_in_flight<LPT>(0);
+        f32x16 s1;
+        wide::scores(kbuf(ic<0>{}), kaddr, qf, s1);
+        if (!full_of(0)) mask_scores<C>(*reinterpret_cast<f32x16(*)[1]>(&s1), vis, 0, g);
+        {
+            f32x16 st[1] = {s1};
+            update_max_agpr<C>(st, c2, m_run, m_true, lsum, oacc);
+        }
+        bf16x8 pf[2];
+        {
+            f32x16 st[1] = {s1};
+            probabilities<C>(st, c2, m_run, lsum, pf);
+        }
+        // iteration j: loads of K(j+2) and V(j+1); scores of tile j+1; O^T of
+        // tile j with the softmax of tile j+1 between its MFMAs
+        for_tiles<2>(ntiles - 1, [&](auto u, int j) {
+            constexpr int U = decltype(u)::value;
+            load_k(ic<U>{}, j + 2);
+            load_v(ic<U ^ 1>{}, j + 1);
+            wide::scores(kbuf(ic<U ^ 1>{}), kaddr, qf, s1);
+            if (!full_of(j + 1)) mask_scores<C>(*reinterpret_cast<f32x16(*)[1]>(&s1), vis, (j + 1) * BN, g);
+            bf16x8 pn[2];
+            float alpha;
+            wide::pv_softmax(vbuf(ic<U>{}), vaddr, pf, oacc, s1, c2, m_run, m_true, lsum, pn, alpha);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) wide::rescale_o(oacc, alpha);
+            pf[0] = pn[0];
+            pf[1] = pn[1];
+            wait_tiles_in_flight<LPT>(0);  // K(j+2), V(j+1)
+        });
+        // the last tile's O^T (its V buffer chosen at run time: no loads are
+        // in flight any more, and two code paths would join two copies of O)
+        accumulate_pv<C>((ntiles - 1) % 2 == 0 ? lds_a_v0 : lds_a_v1, vaddr, pf, oacc);
+    }
+
+    renormalise(m_run, m_true, lsum, oacc);
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    write_results<D>(a, wt, row, g, 0, true, oacc, m_true, ltot);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 queries against an 8-bit KV cache (OCP FP8 E4M3 codes, one
 // power-of-two scale per 64 tokens of a (batch, KV head)), d = 128, split-KV
 // decoding.  Tiles of 128 keys go HBM -> LDS as raw bytes (16 KiB for K and
@@ -943,7 +1188,7 @@ hipError_t launch(K kernel, const FwdArgs &a, hipStream_t s) {
 int fwd_bf16_row_tile(int d, bool split_mode) {
     if (d == 64) return Cfg<64, 64, 4, 1>::BM;
     if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, RA_TUNE_BN128, 4, 1>::BM;
-    if (d == 512) return CfgHalf<512, 32, 2>::BM;
+    if (d == 512) return RA_TUNE_WIDE ? wide::C::BM : CfgHalf<512, 32, 2>::BM;
     return 0;
 }
 
@@ -969,7 +1214,12 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t
     case 128:
         if (split_mode) return launch_masked<128, 64, 4, 2, 2>(a, s);
         return launch_masked<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>(a, s);
-    case 512: return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2>, a, s);
+    case 512:
+        if constexpr (RA_TUNE_WIDE) {
+            return launch<wide::C>(fwd_bf16_wide_kernel<0>, a, s);
+        } else {
+            return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2>, a, s);
+        }
     default: return hipErrorInvalidValue;
     }
 }
