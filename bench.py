@@ -481,13 +481,18 @@ PMC_WRITE = "WRITE_SIZE"
 
 # The kernel each workload's roofline is priced on (a substring of the
 # demangled name rocprofv3 reports), and whether it is priced in flops or bytes.
+# (alternatives: the first one the trace holds is taken)
+PREFILL_D128 = ("fwd_bf16_pp_kernel", "fwd_bf16_kernel<128, 64, 4, 1, 2, 0>")
 DOMINANT = {
-    "ring_1m_gqa32x8_d128": ("fwd_bf16_kernel<128, 64, 4, 1, 2, 0>", "mfma"),
-    "prefill_bf16_h32_d128": ("fwd_bf16_kernel<128, 64, 4, 1, 2, 0>", "mfma"),
-    "mla_h16_d512": ("fwd_bf16_half_kernel", "mfma"),
-    "decode_b4_gqa32x8_cache1m": ("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>", "hbm"),
-    "decode_b4_gqa32x8_cache1m_fp8": ("fwd_fp8kv_kernel", "hbm"),
-    "bwd:prefill_bf16_h32_d128": ("bwd_", "mfma"),
+    "ring_1m_gqa32x8_d128": (PREFILL_D128, "mfma"),
+    "prefill_bf16_h32_d128": (PREFILL_D128, "mfma"),
+    "inplace:ring_1m_gqa32x8_d128": (PREFILL_D128, "mfma"),
+    "inplace:prefill_bf16_h32_d128": (PREFILL_D128, "mfma"),
+    "mla_h16_d512": (("fwd_bf16_wide_kernel", "fwd_bf16_half_kernel"), "mfma"),
+    "inplace:mla_h16_d512": (("fwd_bf16_wide_kernel", "fwd_bf16_half_kernel"), "mfma"),
+    "decode_b4_gqa32x8_cache1m": (("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>",), "hbm"),
+    "decode_b4_gqa32x8_cache1m_fp8": (("fwd_fp8kv_kernel",), "hbm"),
+    "bwd:prefill_bf16_h32_d128": (("bwd_",), "mfma"),
 }
 
 
@@ -563,11 +568,13 @@ def profile(names, outdir, steps):
 def write_profile_summary(name, runs, calib, outdir, steps):
     from long_context_blockwise_amd import inputs
 
-    pattern, bound = DOMINANT.get(name, ("", "mfma"))
+    patterns, bound = DOMINANT.get(name, (("",), "mfma"))
     base = name.split(":", 1)[-1]
     wl = inputs.WORKLOADS[base]
     stats = _csv_rows(runs["trace"][0], "kernel_stats.csv")
-    traces = [r for r in _csv_rows(runs["trace"][0], "kernel_trace.csv") if pattern in r.get("Kernel_Name", "")]
+    all_traces = _csv_rows(runs["trace"][0], "kernel_trace.csv")
+    pattern = next((p for p in patterns if any(p in r.get("Kernel_Name", "") for r in all_traces)), patterns[0])
+    traces = [r for r in all_traces if pattern in r.get("Kernel_Name", "")]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in traces]
     avg_ns = statistics.fmean(durs) if durs else float("nan")
     pipes, n_disp = _counters(runs["pipes"][0], pattern)
@@ -646,6 +653,26 @@ def write_profile_summary(name, runs, calib, outdir, steps):
               f"| HBM read bytes per dispatch | {fmt(fb)} | FETCH_SIZE KiB x 1024 x {fmt(calib.get('FETCH_SIZE', float('nan')), 4)} (copy calibration) |",
               f"| HBM write bytes per dispatch | {fmt(wb)} | WRITE_SIZE KiB x 1024 x {fmt(calib.get('WRITE_SIZE', float('nan')), 4)} (copy calibration) |",
               f"| algorithmic K/V+Q+out bytes per launch | {fmt(alg_bytes_launch)} | K+V once, Q, out |"]
+    # the staging copies of the ring stand-in: their time and how much of it
+    # overlaps the attention kernels (kernel-trace intervals)
+    copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in all_traces
+              if "copyBuffer" in r.get("Kernel_Name", "")]
+    attn = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in traces)
+    copy_ns = sum(e - b for b, e in copies)
+    over_ns = 0
+    for b, e in copies:
+        for ab, ae in attn:
+            if ab >= e:
+                break
+            over_ns += max(0, min(e, ae) - max(b, ab))
+    stage = dict(copies=len(copies), copy_ns=copy_ns, overlap_ns=over_ns,
+                 copy_frac_of_kernel_time=copy_ns / max(sum(durs), 1))
+    if copies:
+        lines += [f"| staging copies (ring stand-in) | {len(copies)} copies, {fmt(copy_ns / 1e3, 5)} µs in all, "
+                  f"{fmt(100 * over_ns / max(copy_ns, 1), 4)} % of it while an attention kernel ran | "
+                  f"kernel trace: `copyBuffer` intervals against `{pattern}` intervals |",
+                  f"| staging copy time / attention kernel time | {fmt(100 * copy_ns / max(sum(durs), 1), 4)} % | "
+                  "both from the kernel trace (copies run on the side stream) |"]
     if bound == "mfma":
         lines += [f"| **achieved (algorithmic)** | **{fmt(achieved_tflops, 5)} TFLOP/s = "
                   f"{fmt(100 * achieved_tflops / PEAK_BF16_TFLOPS, 4)} % of {PEAK_BF16_TFLOPS}** | "
@@ -660,7 +687,8 @@ def write_profile_summary(name, runs, calib, outdir, steps):
     return dict(file=path, kernel=short, avg_us=avg_ns / 1e3, launches_per_step=per_step, clock_ghz=clock_ghz,
                 mfma_busy=mfma_busy, valu_busy=valu_busy, coexec=coexec, lds_busy=lds_busy,
                 fetch_bytes=fb_step, write_bytes=wb_step, traffic_bytes=fb_step + wb_step,
-                achieved_tflops=achieved_tflops, achieved_gbs=achieved_gbs, kernel_digest=kernel_digest())
+                achieved_tflops=achieved_tflops, achieved_gbs=achieved_gbs, staging=stage,
+                kernel_digest=kernel_digest())
 
 
 def main():

@@ -165,6 +165,23 @@ const char *ring_attn_last_error(void);
 int ring_attn_ctx_create(int device, ra_ctx **out);
 int ring_attn_ctx_destroy(ra_ctx *ctx);
 
+/* Perturbations of the staged ring (RA_FLAG_STAGE) for checking its
+ * ordering -- page "Ring Attention：百万 Token 上下文的秘密", §3.2
+ * 通信-计算重叠: a step reads a received chunk only after it has arrived,
+ * and a buffer is refilled only after the step reading it has finished.
+ * With them on, ring_attn_fwd delays the side stream before each staging
+ * copy (DELAY_COPY) and the caller's stream before each launch
+ * (DELAY_COMPUTE) with a one-wave spin of spin_us microseconds that always
+ * ends, and overwrites each staging buffer with NaN right after the step
+ * that read it (POISON, a fill kernel).  Correct ordering gives bit-identical
+ * results with any of them.  They cost time and are meant for tests only.
+ * RA_ERR_INVALID_ARG for unknown bits or spin_us > RA_CHECK_MAX_SPIN_US. */
+#define RA_CHECK_DELAY_COPY 1u
+#define RA_CHECK_DELAY_COMPUTE 2u
+#define RA_CHECK_POISON 4u
+#define RA_CHECK_MAX_SPIN_US 100000
+int ring_attn_ctx_set_check(ra_ctx *ctx, uint32_t checks, uint32_t spin_us);
+
 /* Order in which ring device `device_index` of `P` meets the KV chunks when
  * every step receives the chunk of the previous device (page "Ring
  * Attention：百万 Token 上下文的秘密", §3.1: receive from the left

@@ -10,6 +10,10 @@ library is missing.
 from .ring_attn import (  # noqa: F401
     EXPORTS,
     RA_BF16,
+    RA_CHECK_DELAY_COMPUTE,
+    RA_CHECK_DELAY_COPY,
+    RA_CHECK_MAX_SPIN_US,
+    RA_CHECK_POISON,
     RA_CHUNK_DIAG,
     RA_CHUNK_FULL,
     RA_CHUNK_SKIP,

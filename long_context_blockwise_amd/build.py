@@ -21,7 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libringattn.so")
 ARCH = os.environ.get("RING_ATTN_ARCH", "gfx950")
 
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "merge.hip", "ring_attn.cpp"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "merge.hip", "stage_check.hip",
+           "ring_attn.cpp"]
 
 # Packed-fp32 VALU forms are disabled in all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -61,14 +61,7 @@
 #ifndef RA_TUNE_FUSE_VALU
 #define RA_TUNE_FUSE_VALU 7
 #endif
-// d = 512: 32-row waves over the whole head (1) or wave pairs splitting it
-// (0); VALU instructions placed after each O^T MFMA of the wide kernel.
-#ifndef RA_TUNE_WIDE
-#define RA_TUNE_WIDE 1
-#endif
-#ifndef RA_TUNE_WIDE_VALU
-#define RA_TUNE_WIDE_VALU 3
-#endif
+
 
 namespace ra {
 namespace {
@@ -533,164 +526,6 @@ void fwd_bf16_kernel(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide heads (d = 512): two waves share each 32-row block, each holding half
-// of the query dimensions and half of the output dimensions, so neither the
-// resident Q nor the O accumulator of a wave outgrows the register file.  Per
-// tile each wave computes the scores over its half of d_qk, the pair swaps
-// these partial scores through LDS and adds them (the sum is commutative, so
-// both waves hold bitwise the same scores and run the same softmax), and each
-// wave multiplies the probabilities into its half of O.
-//
-// The partial scores of tile j+1 are computed and published in the iteration
-// that finishes tile j, so one barrier per tile both publishes them and
-// frees the tile buffers: K runs one tile ahead of V, each with two LDS
-// buffers, and the partial scores have two buffers of their own.
-// ---------------------------------------------------------------------------
-template <int D, int BN, int NRB>
-struct CfgHalf : Cfg<D, BN, 2 * NRB, 1> {
-    static constexpr int BM = 32 * NRB;  // query rows per workgroup
-    static constexpr int DSH = D / 32;   // reduction steps of a half of d_qk
-    static constexpr int DBH = D / 64;   // 32-wide O^T blocks of a half of d_v
-};
-
-template <int D, int BN, int NRB>
-__global__ __launch_bounds__(NRB * 128) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_bf16_half_kernel(const FwdArgs a) {
-    using C = CfgHalf<D, BN, NRB>;
-    static_assert(C::KB == 1, "one 32-key block per tile");
-    static_assert((D / 16) % C::SWB == 0, "each half of a row covers whole swizzle windows");
-    constexpr int LPT = C::LOADS_PER_WAVE;  // loads of one K (or V) tile per wave
-    // K and V tiles in arrays of their own, two of each: iteration j reads K
-    // tile j+1 and V tile j and loads K tile j+2 and V tile j+1
-    __shared__ __attribute__((aligned(1024))) char ks0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char ks1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char vs0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char vs1[C::TILE];
-    // partial scores of each wave for two tiles, [row block][half][4 x 64
-    // lanes] of f32x4 per tile parity: two arrays, so the compiler can tell
-    // their accesses from the loads in flight into the tile buffers
-    __shared__ __attribute__((aligned(16))) f32x4 xs0[NRB][2][4 * 64];
-    __shared__ __attribute__((aligned(16))) f32x4 xs1[NRB][2][4 * 64];
-    auto kbuf = [&](auto u) -> char * {
-        if constexpr (decltype(u)::value % 2 == 0) return ks0;
-        else return ks1;
-    };
-    auto vbuf = [&](auto u) -> char * {
-        if constexpr (decltype(u)::value % 2 == 0) return vs0;
-        else return vs1;
-    };
-    auto xsb = [&](auto u) -> f32x4 (*)[2][4 * 64] {
-        if constexpr (decltype(u)::value % 2 == 0) return xs0;
-        else return xs1;
-    };
-
-    const int lane = threadIdx.x & 63, w = wave_index();
-    const int rb = w >> 1, hf = w & 1;
-    const int l32 = lane & 31, g = lane >> 5;
-    const WorkTile wt = work_tile<C>(a);
-    int64_t wv_tlo, wv_thi;
-    token_range(a, wt.p0 + 32 * rb, wt.p0 + 32 * rb + 32, wv_tlo, wv_thi);
-    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * rb + l32);
-
-    bf16x8 qf[C::DSH];
-    load_q(a, wt, row, g, hf * (D / 2), qf);
-    f32x16 oacc[C::DBH];
-    float m_run, m_true, lsum;
-    load_state<D>(a, row, g, true, hf * (D / 2), oacc, m_run, m_true, lsum);
-    const float c2 = a.scale_log2;
-    int kaddr[C::NKA];
-    k_addrs<C>(0, l32, g, kaddr);
-    int vaddr[2][C::NVD];
-    v_addrs<C>(0, lane, vaddr);
-    // byte offset of this wave's half of every K and V row: D/2 bf16 values,
-    // whole swizzle windows, so the per-lane addresses carry over unchanged
-    const int half_off = hf * D;
-
-    int c_begin = 0, c_end = a.n_chunks, sub = 0;
-    if (a.split_mode) {
-        c_begin = wt.split / a.n_sub;
-        sub = wt.split % a.n_sub;
-        c_end = c_begin + 1;
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-        int64_t kbeg, kend;
-        int ntiles;
-        if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
-        const ChunkArg ch = a.chunks[c];
-        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
-        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
-        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
-        // Tiles past the end load nothing and zero-fill their buffer, so
-        // every iteration issues the same loads and the compiler's own waits
-        // for the buffers a phase reads stay partial.
-        auto tile_k0 = [&](int t) {
-            const int64_t k0 = kbeg + (int64_t)t * BN;
-            return k0 < kend ? k0 : kend;
-        };
-        auto load_k = [&](auto u, int t) { load_tile<C>(kbase, a.k_ss, tile_k0(t), kend, kbuf(u), w, lane); };
-        auto load_v = [&](auto u, int t) { load_tile<C>(vbase, a.v_ss, tile_k0(t), kend, vbuf(u), w, lane); };
-        // this wave's partial scores (its half of d_qk) of the tile in K
-        // buffer u, kept in sp and published to the partner wave in xsb(u)
-        auto partial = [&](auto u, f32x16 &sp) {
-            f32x16 s1[1];
-            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-            scores<C>(kbuf(u) + half_off, kaddr, qf, s1);
-            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                xsb(u)[rb][hf][i4 * 64 + lane] = f32x4{s1[0][4 * i4], s1[0][4 * i4 + 1], s1[0][4 * i4 + 2], s1[0][4 * i4 + 3]};
-            sp = s1[0];
-        };
-
-        // prologue: K and V of tile 0, K of tile 1; partial scores of tile 0
-        tile_barrier();  // the previous chunk's tiles and partial scores are no longer read
-        load_k(ic<0>{}, 0);
-        load_v(ic<0>{}, 0);
-        load_k(ic<1>{}, 1);
-        wait_tiles_in_flight<LPT>(0);
-        f32x16 sp[2];  // this wave's partial scores by tile parity
-        partial(ic<0>{}, sp[0]);
-        tile_barrier();  // partial scores of tile 0 published; K tile 0 read
-        for_tiles<2>(ntiles, [&](auto u, int j) {
-            constexpr int U = decltype(u)::value;
-            load_k(ic<U>{}, j + 2);
-            load_v(ic<U ^ 1>{}, j + 1);
-            // scores of tile j: this wave's part plus the partner's (addition
-            // commutes, so both waves hold the same scores bitwise)
-            f32x16 s[1];
-            s[0] = sp[U];
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 o = xsb(u)[rb][hf ^ 1][i4 * 64 + lane];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) s[0][4 * i4 + jj] += o[jj];
-            }
-            // every tile of the range is computed: tiles no row of the block
-            // sees (at most the last of a diagonal chunk) are masked to zero
-            // probabilities, since a branch around them would join two copies
-            // of O and the compiler would copy O out of the AGPRs on every tile
-            const int64_t k0 = kbeg + (int64_t)j * BN;
-            const bool full = keys_all_seen(a, ch.start, k0, BN, kend, wv_tlo, wv_thi);
-            if (!full) mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
-            update_max_agpr<C>(s, c2, m_run, m_true, lsum, oacc);
-            // partial scores of tile j+1 (after the last tile: of a zero-filled
-            // buffer, never read) while the probabilities of tile j are formed
-            partial(ic<U ^ 1>{}, sp[U ^ 1]);
-            bf16x8 pf[2];
-            probabilities<C>(s, c2, m_run, lsum, pf);
-            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(1);
-            accumulate_pv<C>(vbuf(u) + half_off, vaddr, pf, oacc);
-            if constexpr (RA_TUNE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-            wait_tiles_in_flight<LPT>(0);  // K tile j+2, V tile j+1 and the partial scores of j+1
-        });
-    }
-
-    renormalise(m_run, m_true, lsum, oacc);
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    write_results<D>(a, wt, row, g, hf * (D / 2), hf == 0, oacc, m_true, ltot);
-}
-
-// ---------------------------------------------------------------------------
 // Wide heads (d = 512): one wave per SIMD holding 32 query rows with the whole
 // head dimension -- Q as 32 B operands (128 VGPRs), O^T as 16 accumulator
 // blocks of 32x32 (256 AGPRs) -- so no wave needs another's partial scores
@@ -817,7 +652,6 @@ __device__ inline void rescale_o(f32x16 (&o)[C::DB], float alpha) {
 }
 }  // namespace wide
 
-template <int NS_UNUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_wide_kernel(const FwdArgs a) {
     using C = wide::C;
@@ -1188,7 +1022,7 @@ hipError_t launch(K kernel, const FwdArgs &a, hipStream_t s) {
 int fwd_bf16_row_tile(int d, bool split_mode) {
     if (d == 64) return Cfg<64, 64, 4, 1>::BM;
     if (d == 128) return split_mode ? Cfg<128, 64, 4, 2>::BM : Cfg<128, RA_TUNE_BN128, 4, 1>::BM;
-    if (d == 512) return RA_TUNE_WIDE ? wide::C::BM : CfgHalf<512, 32, 2>::BM;
+    if (d == 512) return wide::C::BM;
     return 0;
 }
 
@@ -1214,12 +1048,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool split_mode, hipStream_t
     case 128:
         if (split_mode) return launch_masked<128, 64, 4, 2, 2>(a, s);
         return launch_masked<128, RA_TUNE_BN128, 4, 1, RA_TUNE_NS>(a, s);
-    case 512:
-        if constexpr (RA_TUNE_WIDE) {
-            return launch<wide::C>(fwd_bf16_wide_kernel<0>, a, s);
-        } else {
-            return launch<CfgHalf<512, 32, 2>>(fwd_bf16_half_kernel<512, 32, 2>, a, s);
-        }
+    case 512: return launch<wide::C>(fwd_bf16_wide_kernel, a, s);
     default: return hipErrorInvalidValue;
     }
 }

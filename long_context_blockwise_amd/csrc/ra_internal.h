@@ -89,6 +89,10 @@ hipError_t launch_fwd_fp8kv(const FwdArgs &a, hipStream_t s);
 int fwd_f32_row_tile(int d);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+// Checks of the staged ring's ordering: a bounded spin of one wave, and a
+// NaN fill of a staging buffer (a kernel, so it can be captured in a graph).
+hipError_t launch_spin(uint32_t microseconds, hipStream_t s);
+hipError_t launch_fill_nan(void *p, size_t bytes, hipStream_t s);
 // Backward, bf16 with d = 64 or 128: row statistics, dQ over the chunks of
 // a.f (rows tiled like the forward, bwd_dq_row_tile rows per workgroup), and
 // dK/dV of chunk a.chunk.

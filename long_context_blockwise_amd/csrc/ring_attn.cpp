@@ -31,6 +31,8 @@ static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct ra_ctx {
     int device;
+    uint32_t check;        // RA_CHECK_* perturbations of the staged ring
+    uint32_t check_us;     // their spin length
     hipStream_t side;
     hipEvent_t start;     // caller stream reached the call
     hipEvent_t ready[2];  // staging buffer b holds its chunk
@@ -456,6 +458,16 @@ int ring_attn_ctx_create(int device, ra_ctx **out) {
     return RA_OK;
 }
 
+int ring_attn_ctx_set_check(ra_ctx *c, uint32_t checks, uint32_t spin_us) {
+    if (!c) return fail(RA_ERR_INVALID_ARG, "ctx is NULL");
+    if (checks & ~(uint32_t)(RA_CHECK_DELAY_COPY | RA_CHECK_DELAY_COMPUTE | RA_CHECK_POISON))
+        return fail(RA_ERR_INVALID_ARG, "unknown check bits 0x%x", checks);
+    if (spin_us > RA_CHECK_MAX_SPIN_US) return fail(RA_ERR_INVALID_ARG, "spin_us above %d", RA_CHECK_MAX_SPIN_US);
+    c->check = checks;
+    c->check_us = spin_us;
+    return RA_OK;
+}
+
 int ring_attn_ctx_destroy(ra_ctx *c) {
     if (!c) return RA_OK;
     DeviceGuard guard(c->device);
@@ -632,16 +644,26 @@ static int fwd_impl(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, co
         // copy the chunk of launch `step` into staging buffer step % 2 on the side stream
         const ra_kv_chunk &ch = chunks[launches[step][0]];
         char *dst = ws + pl.off_stage[step & 1];
+        if (ctx->check & RA_CHECK_DELAY_COPY) {
+            const hipError_t r = ra::launch_spin(ctx->check_us, ctx->side);
+            if (r != hipSuccess) return r;
+        }
         int64_t ks[3], vs[3];
         chunk_strides(d->k_strides, ch.len, d->Hkv, d->d_qk, ks);
         chunk_strides(d->v_strides, ch.len, d->Hkv, d->d_v, vs);
         const size_t krow = (size_t)ch.len * d->Hkv * d->d_qk * es;
         const size_t vrow = (size_t)ch.len * d->Hkv * d->d_v * es;
-        hipError_t r = hipMemcpy2DAsync(dst, krow, ch.k, (size_t)ks[0] * es, krow, d->B, hipMemcpyDeviceToDevice,
-                                        ctx->side);
+        // one linear copy per tensor when its batches are contiguous, else a
+        // strided (2D) copy of B rows
+        auto copy = [&](char *to, const void *from, size_t row, int64_t stride) -> hipError_t {
+            if ((size_t)stride * es == row || d->B == 1)
+                return hipMemcpyAsync(to, from, (size_t)d->B * row, hipMemcpyDeviceToDevice, ctx->side);
+            return hipMemcpy2DAsync(to, row, from, (size_t)stride * es, row, d->B, hipMemcpyDeviceToDevice,
+                                    ctx->side);
+        };
+        hipError_t r = copy(dst, ch.k, krow, ks[0]);
         if (r != hipSuccess) return r;
-        r = hipMemcpy2DAsync(dst + (size_t)d->B * krow, vrow, ch.v, (size_t)vs[0] * es, vrow, d->B,
-                             hipMemcpyDeviceToDevice, ctx->side);
+        r = copy(dst + (size_t)d->B * krow, ch.v, vrow, vs[0]);
         if (r != hipSuccess) return r;
         return hipEventRecord(ctx->ready[step & 1], ctx->side);
     };
@@ -688,7 +710,13 @@ static int fwd_impl(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, co
         a.store_out = li + 1 == nl && out != nullptr;
         if ((a.load_state || a.store_state) && !a.m)
             return fail(RA_ERR_WORKSPACE, "internal state buffer missing");
+        if ((ctx->check & RA_CHECK_DELAY_COMPUTE) && (e = ra::launch_spin(ctx->check_us, s)) != hipSuccess)
+            return hip_fail(e, "check spin");
         if ((e = launch_fwd(a, d, false, s)) != hipSuccess) return hip_fail(e, "forward launch");
+        // the step is done with its staging buffer: poison it before it may be refilled
+        if (staged && (ctx->check & RA_CHECK_POISON) &&
+            (e = ra::launch_fill_nan(ws + pl.off_stage[li & 1], pl.stage_bytes, s)) != hipSuccess)
+            return hip_fail(e, "check fill");
         if (staged && li + 2 < nl)
             if ((e = hipEventRecord(ctx->freed[li & 1], s)) != hipSuccess) return hip_fail(e, "event record");
     }

@@ -31,11 +31,13 @@ RA_FLAG_SPLIT_KV = 2
 RA_FLAG_NO_SPLIT_KV = 4
 RA_FLAG_ACCUMULATE = 8
 RA_CHUNK_SKIP, RA_CHUNK_FULL, RA_CHUNK_DIAG = 0, 1, 2
+RA_CHECK_DELAY_COPY, RA_CHECK_DELAY_COMPUTE, RA_CHECK_POISON = 1, 2, 4  # staged-ring ordering checks
+RA_CHECK_MAX_SPIN_US = 100000
 
 EXPORTS = ("ring_attn_version", "ring_attn_last_error", "ring_attn_ctx_create",
            "ring_attn_ctx_destroy", "ring_attn_ring_order", "ring_attn_plan",
            "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_merge",
-           "ring_attn_bwd_workspace_size", "ring_attn_bwd", "ring_attn_fwd_noalloc")
+           "ring_attn_bwd_workspace_size", "ring_attn_bwd", "ring_attn_fwd_noalloc", "ring_attn_ctx_set_check")
 RA_NOALLOC_SCRATCH_BYTES = 96 << 20  # static scratch per GPU behind ring_attn_fwd_noalloc
 
 
@@ -90,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ring_attn_last_error.restype = ctypes.c_char_p
         lib.ring_attn_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
         lib.ring_attn_ctx_destroy.argtypes = [vp]
+        lib.ring_attn_ctx_set_check.argtypes = [vp, ctypes.c_uint32, ctypes.c_uint32]
         lib.ring_attn_ring_order.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i32)]
         lib.ring_attn_plan.argtypes = [i64, i64, ctypes.c_int, i64, i64, ctypes.c_int, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i32)]
@@ -108,7 +111,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ring_attn_bwd.argtypes = [vp, ctypes.POINTER(ra_desc), vp, i64, ctypes.POINTER(ra_kv_chunk),
                                       ctypes.c_int, ctypes.c_int, i64, ctypes.c_uint32, vp, vp, vp, vp, vp,
                                       ctypes.POINTER(ra_kv_grad), vp, sz, vp]
-        for name in ("ring_attn_ctx_create", "ring_attn_ctx_destroy", "ring_attn_ring_order",
+        for name in ("ring_attn_ctx_create", "ring_attn_ctx_destroy", "ring_attn_ctx_set_check", "ring_attn_ring_order",
                      "ring_attn_plan", "ring_attn_workspace_size", "ring_attn_fwd", "ring_attn_fwd_noalloc",
                      "ring_attn_merge",
                      "ring_attn_bwd_workspace_size", "ring_attn_bwd"):
@@ -154,6 +157,10 @@ class RingAttnContext:
         h = ctypes.c_void_p()
         _check(load().ring_attn_ctx_create(device, ctypes.byref(h)))
         self.handle = h
+
+    def set_check(self, checks: int, spin_us: int = 0):
+        """Turn the staged-ring ordering checks (RA_CHECK_* bits) on or off."""
+        _check(load().ring_attn_ctx_set_check(self.handle, int(checks), int(spin_us)))
 
     def close(self):
         if self.handle:

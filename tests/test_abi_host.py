@@ -307,6 +307,16 @@ def test_bwd_workspace_and_validation(lib):
 
 
 
+def test_ctx_check_validation(lib):
+    """The staged-ring checks take only known bits and a bounded spin."""
+    ctx = ctypes.create_string_buffer(256)  # its check fields are written, nothing else
+    assert lib.ring_attn_ctx_set_check(None, 0, 0) == rb.RA_ERR_INVALID_ARG
+    assert lib.ring_attn_ctx_set_check(ctx, 8, 0) == rb.RA_ERR_INVALID_ARG
+    assert lib.ring_attn_ctx_set_check(ctx, 7, rb.RA_CHECK_MAX_SPIN_US + 1) == rb.RA_ERR_INVALID_ARG
+    assert lib.ring_attn_ctx_set_check(ctx, 7, rb.RA_CHECK_MAX_SPIN_US) == 0
+    assert lib.ring_attn_ctx_set_check(ctx, 0, 0) == 0
+
+
 def test_anchor_and_label_validation(lib):
     """Anchors and labels: negative strides are rejected; d = 512 and the
     8-bit cache are not built for them; labels come for the queries and
