@@ -61,6 +61,13 @@
 #ifndef RA_TUNE_FUSE_VALU
 #define RA_TUNE_FUSE_VALU 7
 #endif
+// Scores of the d <= 128 kernel come out of the MFMAs already in log2 units
+// and relative to the softmax reference (queries pre-scaled, the reference
+// folded into the accumulator's start), so p = exp2(s) (1), or p = exp2(s*c -
+// m_ref) with one FMA per score (0).
+#ifndef RA_TUNE_BIAS
+#define RA_TUNE_BIAS 1
+#endif
 
 
 namespace ra {
@@ -250,6 +257,173 @@ __device__ inline void renormalise(float m_run, float m_true, float &lsum, f32x1
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
 }
 
+// ---------------------------------------------------------------------------
+// Biased scores.  The queries are multiplied by c = scale*log2(e) once, when
+// they are loaded (rounded to bf16: a relative change below 2^-9 per
+// element), and every score chain of a tile starts from the accumulator
+// value -m_ref instead of 0, so the MFMAs deliver s = c q.k - m_ref and the
+// probability is exp2(s) with no vector work per score beyond the exp.  The
+// reference starts at 0 and moves only when a tile maximum exceeds it by more
+// than the threshold (up) or the running maximum falls more than 64 below it
+// (down, so that probabilities keep their precision); the true maximum is
+// tracked as before and the state is renormalised to it at the end.
+// ---------------------------------------------------------------------------
+constexpr float kRefFloor = 64.f;  // log2 units below the reference that move it down
+
+// Query fragments times c, rounded to bf16.
+template <int NDS>
+__device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0, float c,
+                                     bf16x8 (&qf)[NDS]) {
+    load_q(a, wt, r, g, d0, qf);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        const u32x4 u = __builtin_bit_cast(u32x4, qf[ds]);
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = __builtin_bit_cast(float, u[j] << 16), hi = __builtin_bit_cast(float, u[j] & 0xffff0000u);
+            v[j] = pack_bf16(lo * c, hi * c);
+        }
+        qf[ds] = to_bf16x8(v);
+    }
+}
+
+// Starting state for biased scores: the reference is 0 unless a loaded
+// state's maximum lies outside [-kRefFloor, threshold] (log2 units); a
+// loaded O and l are rescaled to the reference.
+template <int DV, int NDB>
+__device__ inline void load_state_biased(const FwdArgs &a, const LaneRow &r, int g, bool owner, int dv0,
+                                         f32x16 (&o)[NDB], float &m_run, float &m_true, float &lsum) {
+    load_state<DV, NDB>(a, r, g, owner, dv0, o, m_run, m_true, lsum);
+    if (m_true == kNegInf) {
+        m_run = 0.f;
+        return;
+    }
+    if (m_true < -kRefFloor || m_true > kRescaleThreshold) return;  // keep the loaded maximum as reference
+    const float alpha = exp2_fast(m_true);
+    m_run = 0.f;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+}
+
+template <class C>
+__device__ inline f32x16 bias_block(float m_run) {
+    f32x16 b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = -m_run;
+    return b;
+}
+
+// S^T = K Q^T + bias for the KB key blocks of a tile (the chains start from
+// the bias block instead of zero).
+template <class C, int NDS>
+__device__ inline void scores_biased(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[NDS],
+                                     const f32x16 &bias, f32x16 (&s)[C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = bias;
+    constexpr int N = NDS * C::KB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = kfrag<C>(kt, kaddr, n / C::KB, n % C::KB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        s[n % C::KB] = mfma(fr[n % PF], qf[n / C::KB], s[n % C::KB]);
+        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, (n + PF) / C::KB, (n + PF) % C::KB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// update_max for biased scores: the tile maximum is max(s) + m_ref.  When
+// the reference moves, O and l are rescaled, this tile's scores shifted and
+// the bias block rebuilt.
+template <class C, int NDB>
+__device__ inline void update_max_biased(f32x16 (&s)[C::KB], float &m_run, float &m_true, float &lsum,
+                                         f32x16 (&o)[NDB], f32x16 &bias) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_pair(mx);
+    const float mt = mx + m_run;
+    m_true = fmaxf(m_true, mt);
+    const bool up = mt > m_run + kRescaleThreshold;
+    const bool down = m_true != kNegInf && m_true < m_run - kRefFloor;
+    if (__builtin_amdgcn_ballot_w64(up || down)) {
+        const float ref = up ? mt : (down ? m_true : m_run);
+        const float alpha = exp2_fast(m_run - ref);
+        const float shift = ref - m_run;
+        m_run = ref;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] -= shift;
+        bias = bias_block<C>(m_run);
+    }
+}
+
+// prob_step / softmax_pv / probabilities for biased scores: p = exp2(s).
+template <class C>
+__device__ inline bf16x8 prob_step_biased(const f32x16 (&s)[C::KB], int ks, float &lsum) {
+    const int kb = ks / 2, hh = ks % 2;
+    u32x4 pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float e0 = exp2_fast(s[kb][8 * hh + 2 * j]);
+        const float e1 = exp2_fast(s[kb][8 * hh + 2 * j + 1]);
+        lsum += e0 + e1;
+        pk[j] = pack_bf16(e0, e1);
+    }
+    return to_bf16x8(pk);
+}
+
+template <class C, int NDB>
+__device__ inline void softmax_pv_biased(const f32x16 (&s)[C::KB], float &lsum, const char *vt,
+                                         const int (&vaddr)[2][C::NVD], f32x16 (&o)[NDB]) {
+    constexpr int NK = 2 * C::KB;
+    bf16x8 fr[2][NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) fr[0][db] = vfrag<C>(vt, vaddr, 0, db);
+    bf16x8 p = prob_step_biased<C>(s, 0, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    prio_mfma();
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 1 < NK) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) fr[(ks + 1) & 1][db] = vfrag<C>(vt, vaddr, ks + 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma(fr[ks & 1][db], p, o[db]);
+        if (ks + 1 < NK) {
+            p = prob_step_biased<C>(s, ks + 1, lsum);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, RA_TUNE_FUSE_VALU, 0);  // VALU
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    prio_valu();
+}
+
+template <class C>
+__device__ inline void probabilities_biased(const f32x16 (&s)[C::KB], float &lsum, bf16x8 (&pf)[2 * C::KB]) {
+#pragma unroll
+    for (int ks = 0; ks < 2 * C::KB; ++ks) pf[ks] = prob_step_biased<C>(s, ks, lsum);
+}
+
 // Final (or partial) results of output dimensions dv0 .. dv0 + 32*NDB - 1 of
 // rows with d_v = DV: the state (or a split partial) and/or the normalised
 // output; m and l are written by the lanes with write_ml.
@@ -329,11 +503,19 @@ void fwd_bf16_kernel(const FwdArgs a) {
     f32x16 oacc[C::DB];
     float m_run, m_true, lsum;
     bool live = !LAB;
-    if constexpr (!LAB) {
-        load_q(a, wt, row, g, 0, qf);
-        load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
-    }
     const float c2 = a.scale_log2;
+    f32x16 bias;  // -m_run in every element (biased scores)
+    auto start = [&]() {
+        if constexpr (RA_TUNE_BIAS) {
+            load_q_scaled(a, wt, row, g, 0, c2, qf);
+            load_state_biased<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+            bias = bias_block<C>(m_run);
+        } else {
+            load_q(a, wt, row, g, 0, qf);
+            load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+        }
+    };
+    if constexpr (!LAB) start();
     int kaddr[C::NKA];
     k_addrs<C>(wk * C::KW, l32, g, kaddr);
     int vaddr[2][C::NVD];
@@ -383,8 +565,7 @@ void fwd_bf16_kernel(const FwdArgs a) {
             if (ntiles == 0) continue;
             if (LAB && !live) {  // uniform
                 live = true;
-                load_q(a, wt, row, g, 0, qf);
-                load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+                start();
             }
         } else {
             if (!chunk_range(a, wt, c, sub, kbeg, kend, ntiles, BN)) continue;  // uniform
@@ -436,7 +617,8 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 if constexpr (LAB) lk = reinterpret_cast<const int *>(lab)[lane];
                 prio_mfma();
                 f32x16 s[C::KB];
-                scores<C>(kst(u), kaddr, qf, s);
+                if constexpr (RA_TUNE_BIAS) scores_biased<C>(kst(u), kaddr, qf, bias, s);
+                else scores<C>(kst(u), kaddr, qf, s);
                 prio_valu();
                 LabelTest lt{true, false, false, true};
                 if constexpr (LAB) {
@@ -458,15 +640,28 @@ void fwd_bf16_kernel(const FwdArgs a) {
                             mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
                         }
                     }
-                    update_max<C>(s, c2, m_run, m_true, lsum, oacc);
-                    if constexpr (RA_TUNE_FUSE) {
-                        softmax_pv<C>(s, c2, m_run, lsum, vst(u), vaddr, oacc);
+                    if constexpr (RA_TUNE_BIAS) {
+                        update_max_biased<C>(s, m_run, m_true, lsum, oacc, bias);
+                        if constexpr (RA_TUNE_FUSE) {
+                            softmax_pv_biased<C>(s, lsum, vst(u), vaddr, oacc);
+                        } else {
+                            bf16x8 pf[2 * C::KB];
+                            probabilities_biased<C>(s, lsum, pf);
+                            prio_mfma();
+                            accumulate_pv<C>(vst(u), vaddr, pf, oacc);
+                            prio_valu();
+                        }
                     } else {
-                        bf16x8 pf[2 * C::KB];
-                        probabilities<C>(s, c2, m_run, lsum, pf);
-                        prio_mfma();
-                        accumulate_pv<C>(vst(u), vaddr, pf, oacc);
-                        prio_valu();
+                        update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                        if constexpr (RA_TUNE_FUSE) {
+                            softmax_pv<C>(s, c2, m_run, lsum, vst(u), vaddr, oacc);
+                        } else {
+                            bf16x8 pf[2 * C::KB];
+                            probabilities<C>(s, c2, m_run, lsum, pf);
+                            prio_mfma();
+                            accumulate_pv<C>(vst(u), vaddr, pf, oacc);
+                            prio_valu();
+                        }
                     }
                 }
             }
@@ -479,7 +674,8 @@ void fwd_bf16_kernel(const FwdArgs a) {
 
     if (!live) {  // uniform
         if (a.load_state && a.store_state && !a.store_out && !a.split_mode) return;  // the state is the result
-        load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+        if constexpr (RA_TUNE_BIAS) load_state_biased<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+        else load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
     }
     renormalise(m_run, m_true, lsum, oacc);
     if constexpr (KSPLIT > 1) {
