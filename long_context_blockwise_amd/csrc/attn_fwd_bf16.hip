@@ -272,9 +272,7 @@ constexpr float kRefFloor = 64.f;  // log2 units below the reference that move i
 
 // Query fragments times c, rounded to bf16.
 template <int NDS>
-__device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0, float c,
-                                     bf16x8 (&qf)[NDS]) {
-    load_q(a, wt, r, g, d0, qf);
+__device__ inline void scale_q(bf16x8 (&qf)[NDS], float c) {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
         const u32x4 u = __builtin_bit_cast(u32x4, qf[ds]);
@@ -286,6 +284,12 @@ __device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const
         }
         qf[ds] = to_bf16x8(v);
     }
+}
+template <int NDS>
+__device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0, float c,
+                                     bf16x8 (&qf)[NDS]) {
+    load_q(a, wt, r, g, d0, qf);
+    scale_q(qf, c);
 }
 
 // Starting state for biased scores: the reference is 0 unless a loaded
@@ -1058,10 +1062,13 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
             qf[ds] = to_bf16x8(v);
         }
     }
+    const float c2 = a.scale_log2;
+    // biased scores, as in the bf16 kernel: s = c q.k - m_ref out of the MFMAs
+    scale_q(qf, c2);
     f32x16 oacc[C::DB];
     float m_run, m_true, lsum;
-    load_state<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
-    const float c2 = a.scale_log2;
+    load_state_biased<D>(a, row, g, wk == 0, 0, oacc, m_run, m_true, lsum);
+    f32x16 bias = bias_block<C>(m_run);
 
     // per-lane LDS byte addresses (tile-relative)
     int kaddr[D / 32];  // K: row wk*64 + l32, units 2c + g
@@ -1136,8 +1143,7 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
                 f32x16 s[C::KB];
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+                    s[kb] = bias;
 #pragma unroll
                     for (int cc = 0; cc < D / 32; ++cc) {
                         const u32x4 raw = *reinterpret_cast<const u32x4 *>(kt + kaddr[cc] + kb * 32 * ROWB);
@@ -1146,9 +1152,9 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
                     }
                 }
                 if (!full) mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
-                update_max<C>(s, c2, m_run, m_true, lsum, oacc);
+                update_max_biased<C>(s, m_run, m_true, lsum, oacc, bias);
                 bf16x8 pf[2 * C::KB];
-                probabilities<C>(s, c2, m_run, lsum, pf);
+                probabilities_biased<C>(s, lsum, pf);
 #pragma unroll
                 for (int kss = 0; kss < 2 * C::KB; ++kss)
 #pragma unroll
