@@ -576,6 +576,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
         }
         const ChunkArg ch = a.chunks[c];
         const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        // tile tests as integer bounds (tiles are evenly spaced unless anchor
+        // tiles follow the main range)
+        TileSpan span{0, 0, 0, 0};
+        if constexpr (!ANC) span = tile_span(a, ch.start, kbeg, kend, BN, wk * C::KW, C::KW, wv_tlo, wv_thi, ntiles);
         Anchors an{kNoKey, kNoKey, kNoKey};
         if constexpr (ANC) an = row_anchors(a, row.qpos, ch.start, tr.kbase, kbeg, kend);
         const int32_t *kseg = LAB && ch.kseg ? ch.kseg + wt.b * ch.len : nullptr;
@@ -606,8 +610,14 @@ void fwd_bf16_kernel(const FwdArgs a) {
             // this wave's keys k0 + wk*KW .. + KW-1
             const int64_t k0 = tile_start(it);
             const int64_t wk0 = k0 + wk * C::KW;
-            bool skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
-            bool full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
+            bool skip, full;
+            if constexpr (ANC) {
+                skip = keys_unseen(a, ch.start, wk0, C::KW, wv_tlo, wv_thi);
+                full = keys_all_seen(a, ch.start, wk0, C::KW, kend, wv_tlo, wv_thi);
+            } else {
+                skip = span.unseen(it);
+                full = span.all_seen(it);
+            }
             const char *lab = kst(u) + C::TILE + 256 * w;
             if constexpr (ANC) {
                 if (skip && tile_has_anchor(a, ch.start, wk0, C::KW, wv_tlo, wv_thi)) skip = false;

@@ -348,6 +348,47 @@ __device__ inline bool keys_all_seen(const FwdArgs &a, int64_t cstart, int64_t k
     return true;
 }
 
+// keys_unseen / keys_all_seen for every tile of a chunk at once.  A wave
+// walks keys kbeg + t*step + woff .. + n-1 for tiles t = 0, 1, ...; both
+// tests are monotone in t (each condition holds below or above one bound),
+// so once per chunk they reduce to tile-index bounds:
+//   unseen(t)   <=>  t < un_lo || t >= un_hi
+//   all_seen(t) <=>  fu_lo <= t < fu_hi
+// and the tile loop compares 32-bit integers instead of positions.
+struct TileSpan {
+    int un_lo, un_hi, fu_lo, fu_hi;
+    __device__ bool unseen(int t) const { return t < un_lo || t >= un_hi; }
+    __device__ bool all_seen(int t) const { return t >= fu_lo && t < fu_hi; }
+};
+
+__device__ inline TileSpan tile_span(const FwdArgs &a, int64_t cstart, int64_t kbeg, int64_t kend, int64_t step,
+                                     int64_t woff, int64_t n, int64_t tlo, int64_t thi, int ntiles) {
+    // tiles t >= 0 with t*step <= v, and the first t with t*step >= v
+    auto upto = [&](int64_t v) -> int64_t { return v < 0 ? 0 : v / step + 1; };
+    auto from = [&](int64_t v) -> int64_t { return v <= 0 ? 0 : (v + step - 1) / step; };
+    auto clamp = [&](int64_t t) -> int { return (int)(t < 0 ? 0 : (t > ntiles ? ntiles : t)); };
+    const int64_t base = cstart + kbeg + woff;  // absolute position of the wave's first key of tile 0
+    const int64_t W = a.window;
+    int64_t un_lo = 0, un_hi = from(kend - kbeg - woff);  // tiles at or past kend hold no key of the wave
+    int64_t fu_lo = 0, fu_hi = upto(kend - kbeg - woff - n);
+    if (a.causal) {
+        un_hi = un_hi < upto(a.q_offset + thi - base) ? un_hi : upto(a.q_offset + thi - base);
+        const int64_t f = upto(a.q_offset + tlo - base - n + 1);
+        fu_hi = fu_hi < f ? fu_hi : f;
+    }
+    if (W > 0) {
+        un_lo = from(a.q_offset + tlo - W - base - n + 1);
+        fu_lo = from(a.q_offset + thi - W - base);
+        if (!a.causal) {
+            const int64_t u = upto(a.q_offset + thi + W - base);
+            un_hi = un_hi < u ? un_hi : u;
+            const int64_t f = upto(a.q_offset + tlo + W - base - n + 1);
+            fu_hi = fu_hi < f ? fu_hi : f;
+        }
+    }
+    return TileSpan{clamp(un_lo), clamp(un_hi), clamp(fu_lo), clamp(fu_hi)};
+}
+
 // ---------------------------------------------------------------------------
 // Anchor tokens and segment labels (kernels instantiated with EXT)
 // ---------------------------------------------------------------------------
