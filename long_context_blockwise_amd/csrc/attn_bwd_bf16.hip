@@ -11,7 +11,12 @@
 // device's query chunk, dK and dV travel with the KV chunk they belong to.
 //
 // Three kernels.  bwd_pre turns the forward's final state into the per-row
-// log-sum-exp (log2 units) and computes D.  bwd_dq keeps a tile of query rows
+// log-sum-exp (log2 units) and computes D; it stores both negated, as the
+// starting values of the score chains: with one operand of S pre-scaled by
+// scale*log2(e), the chain of S that starts from -lse2 ends at the exponent of
+// P (P = exp2 of it), and the chain of dP that starts from -D ends at dP - D,
+// so no vector work per score remains besides the exp and one multiply for
+// dS.  bwd_dq keeps a tile of query rows
 // resident and walks the key tiles like the forward kernel: with S^T = K Q^T
 // in the lane-per-row layout, P^T needs only the lane's own lse, dP^T = V dO^T
 // reads V exactly as the forward reads K, and dS^T is the B operand of
@@ -67,8 +72,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A) {
     if (row < rows && sub == 0) {
         const float l = A.l[row];
         const int64_t idx = ((b * a.Hq + h) * a.Lq + t) * 2;
-        A.ld[idx] = l > 0.f ? (A.m[row] + logf(l)) * kLog2e : kPosInf;
-        A.ld[idx + 1] = acc;
+        A.ld[idx] = l > 0.f ? -(A.m[row] + logf(l)) * kLog2e : -kPosInf;  // -lse2 (rows that see no key: P = 0)
+        A.ld[idx + 1] = -acc;                                                // -D
     }
 }
 
@@ -107,11 +112,14 @@ void bwd_dq_kernel(const BwdArgs A) {
             gf[ds] = to_bf16x8(v);
         }
     }
-    float lse2 = kPosInf, Drow = 0.f;  // rows past Lq get P = 0
+    // -lse2 and -D of the row (rows past Lq get P = 0).  (Starting the score
+    // chains from them, as the dK/dV kernel does, would take 16 registers per
+    // splat, which this kernel does not have at two waves per SIMD.)
+    float nl = -kPosInf, nd = 0.f;
     if (row.ok) {
         const int64_t idx = (((int64_t)wt.b * a.Hq + row.h) * a.Lq + row.t) * 2;
-        lse2 = A.ld[idx];
-        Drow = A.ld[idx + 1];
+        nl = A.ld[idx];
+        nd = A.ld[idx + 1];
     }
     const float c2 = a.scale_log2;
     f32x16 acc[C::DB];
@@ -231,9 +239,9 @@ void bwd_dq_kernel(const BwdArgs A) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int i0 = 8 * hh + 2 * j, i1 = i0 + 1;
-                            const float p0 = exp2_fast(__builtin_fmaf(s[kb][i0], c2, -lse2));
-                            const float p1 = exp2_fast(__builtin_fmaf(s[kb][i1], c2, -lse2));
-                            pk[j] = pack_bf16(p0 * (dp[kb][i0] - Drow), p1 * (dp[kb][i1] - Drow));
+                            const float p0 = exp2_fast(__builtin_fmaf(s[kb][i0], c2, nl));
+                            const float p1 = exp2_fast(__builtin_fmaf(s[kb][i1], c2, nl));
+                            pk[j] = pack_bf16(p0 * (dp[kb][i0] + nd), p1 * (dp[kb][i1] + nd));
                         }
                         pf[2 * kb + hh] = to_bf16x8(pk);
                     }
@@ -284,9 +292,53 @@ constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
 #define RA_TUNE_KV_RB 2
 #endif
 
+#ifndef RA_TUNE_KV_PF
+#define RA_TUNE_KV_PF 4  // Q and dO fragments read ahead of the S and dP MFMAs
+#endif
+#ifndef RA_TUNE_KV_ASM
+#define RA_TUNE_KV_ASM 1  // S and dP chains as inline asm (VGPR results, K and V fragments in AGPRs)
+#endif
+
+// S = Q (cK)^T - lse2 and dP = dO V^T - D of an RB-block row tile; s and dp
+// hold the chains' starting values.  MFMA n reduces step ds = n / 2RB of
+// block rb = (n/2) % RB, S for even n and dP for odd n; PF fragments of the
+// Q and dO tiles are read ahead.  As inline asm the results stay in VGPRs,
+// where the vector work reads them, and the resident K and V fragments in
+// AGPRs (the builtin would put every accumulator of this kernel in AGPRs and
+// copy the scores out); the s_nops after the last MFMA cover the wait states
+// before a vector instruction may touch a result, which the compiler does not
+// see inside asm.
+template <class C, int RB>
+__device__ inline void kv_scores(const char *qt, const char *gt, const int (&kaddr)[C::NKA],
+                                 const bf16x8 (&kf)[C::DS], const bf16x8 (&vf)[C::DS], f32x16 (&s)[RB],
+                                 f32x16 (&dp)[RB]) {
+    constexpr int N = 2 * RB * C::DS;
+    constexpr int PF = RA_TUNE_KV_PF;
+    auto frag = [&](int n) { return kfrag<C>((n & 1) ? gt : qt, kaddr, n / (2 * RB), (n / 2) % RB); };
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF; ++n) fr[n] = frag(n);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const int ds = n / (2 * RB), rb = (n / 2) % RB;
+        if constexpr (RA_TUNE_KV_ASM) {
+            if (n & 1)
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp[rb]) : "v"(fr[n % PF]), "a"(vf[ds]));
+            else
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s[rb]) : "v"(fr[n % PF]), "a"(kf[ds]));
+        } else {
+            if (n & 1) dp[rb] = mfma(fr[n % PF], vf[ds], dp[rb]);
+            else s[rb] = mfma(fr[n % PF], kf[ds], s[rb]);
+        }
+        if (n + PF < N) fr[n % PF] = frag(n + PF);
+        if (n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (RA_TUNE_KV_ASM) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+}
+
 // A tile is RB blocks of 32 query rows.  Stage u holds the Q tile (row-major,
-// swizzled), then each wave's copy of the rows' (lse2, D) pairs (256 bytes
-// per 32 rows per wave), then the dO tile: RA_STAGE_ARRAYS(NS, TILE + 1024 RB)
+// swizzled), then each wave's copy of the rows' -lse2 and -D (256 bytes per
+// 32 rows per wave: the 32 values of -lse2, then the 32 of -D), then the dO tile: RA_STAGE_ARRAYS(NS, TILE + 1024 RB)
 // gives 2 TILE + 2048 RB bytes a stage.  The RB row blocks are independent
 // chains of matrix-core work, which lets one wave overlap the softmax of one
 // block with the products of another.
@@ -296,7 +348,7 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     const FwdArgs &a = A.f;
     constexpr int RT = 32 * RB;              // query rows per tile
     using C = Cfg<D, RT, kKvWaves, 1>;       // RT-row tiles: TILE bytes each for Q and dO; KB = RB
-    constexpr int LDW = 256 * RB;            // bytes of (lse2, D) pairs per wave (row labels: half that)
+    constexpr int LDW = 256 * RB;            // bytes of (-lse2, -D) per wave (row labels: half that)
     // EXT: each wave's copy of the rows' segment labels follows the dO tile
     constexpr int LPT = 2 * C::LOADS_PER_WAVE + RB + (EXT ? 1 : 0);
     static_assert(!EXT || RT <= 64, "a wave's row labels are 64 dwords");
@@ -323,7 +375,7 @@ void bwd_dkdv_kernel(const BwdArgs A) {
 
     // resident B operands: K^T and V^T fragments of the lane's key (with EXT
     // read once the workgroup is known to have rows to visit)
-    bf16x8 kf[C::DS], vf[C::DS];
+    bf16x8 kf[C::DS], vf[C::DS], kfa[C::DS], vfa[C::DS];
     auto load_kv = [&]() {
         const uint16_t *kp = (const uint16_t *)ch.k + b * a.k_sb + key * a.k_ss + hk * a.k_sh + 8 * g;
         const uint16_t *vp = (const uint16_t *)ch.v + b * a.v_sb + key * a.v_ss + hk * a.v_sh + 8 * g;
@@ -336,6 +388,15 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             }
             kf[ds] = to_bf16x8(x);
             vf[ds] = to_bf16x8(y);
+        }
+        scale_q(kf, a.scale_log2);  // S comes out in log2 units
+        if constexpr (RA_TUNE_KV_ASM) {
+            // moved into AGPRs once: the asm operands then read them there
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds) {
+                asm volatile("" : "=a"(kfa[ds]) : "0"(kf[ds]));
+                asm volatile("" : "=a"(vfa[ds]) : "0"(vf[ds]));
+            }
         }
     };
     if constexpr (!EXT) load_kv();
@@ -444,7 +505,6 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     k_addrs<C>(0, l32, g, kaddr);
     int vaddr[2][C::NVD];
     v_addrs<C>(0, lane, vaddr);
-    const float c2 = a.scale_log2;
     const int64_t kpos = ch.start + key;
 
     auto tile_of = [&](int it, int &h, int64_t &t0) {
@@ -466,14 +526,18 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         const uint16_t *gb = (const uint16_t *)A.dout + b * a.o_sb + h * a.o_sh;
         load_tile<C>(qb, a.q_ss, t0, a.Lq, qtile(u), w, lane);
         load_tile<C>(gb, a.o_ss, t0, a.Lq, gtile(u), w, lane);
-        // (lse2, D) of rows t0 .. t0+RT-1: one dword per lane per 32 rows into the wave's own copy
+        // (-lse2, -D) of rows t0 .. t0+RT-1 into the wave's own copy, one
+        // dword per lane per 32 rows, split by kind: block rb holds -lse2 of
+        // its 32 rows, then their -D (lanes 0-31 read the first of each pair,
+        // lanes 32-63 the second)
         const int64_t nrows = a.Lq - t0 < RT ? a.Lq - t0 : RT;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(A.ld + (((int64_t)b * a.Hq + h) * a.Lq + t0) * 2), (short)0, (int)(nrows * 8), kBufferFlags);
+        const unsigned pair = (unsigned)(8 * l32 + 4 * g);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(ldtile(u) + LDW * w + 256 * rb), 4,
-                                                     (unsigned)(256 * rb + lane * 4), 0, 0, 0);
+                                                     (unsigned)(256 * rb) + pair, 0, 0, 0);
         if constexpr (EXT)  // the rows' segment labels (RT <= 64: one dword per lane)
             load_labels(a.q_seg ? a.q_seg + b * a.Lq : nullptr, t0, a.Lq, gtile(u) + C::TILE + 256 * w, lane);
     };
@@ -507,19 +571,22 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         }
         if (!skip) {
             const char *qt = qtile(u), *gt = gtile(u), *lt = ldtile(u) + LDW * w;
-            // S = Q K^T and dP = dO V^T per 32-row block: rows on M, this wave's keys on N
+            // S = Q (cK)^T - lse2 and dP = dO V^T - D per 32-row block: rows on
+            // M, this wave's keys on N.  Element i of block rb is row
+            // 32rb + 8(i/4) + 4g + i%4; its chains start from that row's -lse2
+            // and -D.
             f32x16 s[RB], dp[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[rb][i] = dp[rb][i] = 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 x = *(const f32x4 *)(lt + 256 * rb + 32 * j + 16 * g);
+                    const f32x4 y = *(const f32x4 *)(lt + 256 * rb + 128 + 32 * j + 16 * g);
 #pragma unroll
-            for (int ds = 0; ds < C::DS; ++ds)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    s[rb] = mfma(kfrag<C>(qt, kaddr, ds, rb), kf[ds], s[rb]);
-                    dp[rb] = mfma(kfrag<C>(gt, kaddr, ds, rb), vf[ds], dp[rb]);
+                    for (int e = 0; e < 4; ++e) s[rb][4 * j + e] = x[e], dp[rb][4 * j + e] = y[e];
                 }
+            if constexpr (RA_TUNE_KV_ASM) kv_scores<C, RB>(qt, gt, kaddr, kfa, vfa, s, dp);
+            else kv_scores<C, RB>(qt, gt, kaddr, kf, vf, s, dp);
             // element i of block rb is row t0 + 32rb + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
             if (!full) {
                 const int64_t big = 1 << 30;
@@ -582,26 +649,17 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                         }
                 }
             }
-            // P and dS of k-step ks (rows 16ks .. 16ks+15), packed as B operands
+            // P = exp2(S c - lse2) and dS = P (dP - D) of k-step ks (rows 16ks .. 16ks+15),
+            // packed as B operands
             auto p_ds = [&](int ks, bf16x8 &ppk, bf16x8 &pdk) {
                 const int rb = ks / 2, hh = ks % 2;
                 u32x4 a4, b4;
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    // rows 32rb + 16hh + 8jj + 4g + 0..3: their (lse2, D) pairs
-                    const char *lp = lt + 8 * (32 * rb + 16 * hh + 8 * jj + 4 * g);
-                    const f32x4 x = *(const f32x4 *)lp;
-                    const f32x4 y = *(const f32x4 *)(lp + 16);
-                    const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
-#pragma unroll
-                    for (int r2 = 0; r2 < 2; ++r2) {
-                        const int i0 = 8 * hh + 4 * jj + 2 * r2, i1 = i0 + 1;
-                        const float p0 = exp2_fast(__builtin_fmaf(s[rb][i0], c2, -l4[2 * r2]));
-                        const float p1 = exp2_fast(__builtin_fmaf(s[rb][i1], c2, -l4[2 * r2 + 1]));
-                        a4[2 * jj + r2] = pack_bf16(p0, p1);
-                        b4[2 * jj + r2] =
-                            pack_bf16(p0 * (dp[rb][i0] - d4[2 * r2]), p1 * (dp[rb][i1] - d4[2 * r2 + 1]));
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int i0 = 8 * hh + 2 * j, i1 = i0 + 1;
+                    const float p0 = exp2_fast(s[rb][i0]), p1 = exp2_fast(s[rb][i1]);
+                    a4[j] = pack_bf16(p0, p1);
+                    b4[j] = pack_bf16(p0 * dp[rb][i0], p1 * dp[rb][i1]);
                 }
                 ppk = to_bf16x8(a4);
                 pdk = to_bf16x8(b4);

@@ -68,6 +68,11 @@
 #ifndef RA_TUNE_BIAS
 #define RA_TUNE_BIAS 1
 #endif
+// keep the bias block live across tiles (a splat the compiler would rebuild
+// with 15 moves per tile)
+#ifndef RA_TUNE_BIASPIN
+#define RA_TUNE_BIASPIN 1
+#endif
 
 
 namespace ra {
@@ -270,21 +275,6 @@ __device__ inline void renormalise(float m_run, float m_true, float &lsum, f32x1
 // ---------------------------------------------------------------------------
 constexpr float kRefFloor = 64.f;  // log2 units below the reference that move it down
 
-// Query fragments times c, rounded to bf16.
-template <int NDS>
-__device__ inline void scale_q(bf16x8 (&qf)[NDS], float c) {
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-        const u32x4 u = __builtin_bit_cast(u32x4, qf[ds]);
-        u32x4 v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float lo = __builtin_bit_cast(float, u[j] << 16), hi = __builtin_bit_cast(float, u[j] & 0xffff0000u);
-            v[j] = pack_bf16(lo * c, hi * c);
-        }
-        qf[ds] = to_bf16x8(v);
-    }
-}
 template <int NDS>
 __device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const LaneRow &r, int g, int d0, float c,
                                      bf16x8 (&qf)[NDS]) {
@@ -319,26 +309,6 @@ __device__ inline f32x16 bias_block(float m_run) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) b[i] = -m_run;
     return b;
-}
-
-// S^T = K Q^T + bias for the KB key blocks of a tile (the chains start from
-// the bias block instead of zero).
-template <class C, int NDS>
-__device__ inline void scores_biased(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[NDS],
-                                     const f32x16 &bias, f32x16 (&s)[C::KB]) {
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = bias;
-    constexpr int N = NDS * C::KB;
-    constexpr int PF = C::PF > 0 ? C::PF : N;
-    bf16x8 fr[PF];
-#pragma unroll
-    for (int n = 0; n < PF && n < N; ++n) fr[n] = kfrag<C>(kt, kaddr, n / C::KB, n % C::KB);
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        s[n % C::KB] = mfma(fr[n % PF], qf[n / C::KB], s[n % C::KB]);
-        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, (n + PF) / C::KB, (n + PF) % C::KB);
-        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
 // update_max for biased scores: the tile maximum is max(s) + m_ref.  When
@@ -631,8 +601,12 @@ void fwd_bf16_kernel(const FwdArgs a) {
                 if constexpr (LAB) lk = reinterpret_cast<const int *>(lab)[lane];
                 prio_mfma();
                 f32x16 s[C::KB];
-                if constexpr (RA_TUNE_BIAS) scores_biased<C>(kst(u), kaddr, qf, bias, s);
-                else scores<C>(kst(u), kaddr, qf, s);
+                if constexpr (RA_TUNE_BIAS) {
+                    scores_biased<C>(kst(u), kaddr, qf, bias, s);
+                    if constexpr (RA_TUNE_BIASPIN) asm volatile("" : "+v"(bias));
+                } else {
+                    scores<C>(kst(u), kaddr, qf, s);
+                }
                 prio_valu();
                 LabelTest lt{true, false, false, true};
                 if constexpr (LAB) {

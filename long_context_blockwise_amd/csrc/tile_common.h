@@ -594,6 +594,41 @@ __device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const 
     }
 }
 
+// S^T = K Q^T + bias for the KB key blocks of a tile (the chains start from
+// the bias block instead of zero).
+template <class C, int NDS>
+__device__ inline void scores_biased(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[NDS],
+                                     const f32x16 &bias, f32x16 (&s)[C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = bias;
+    constexpr int N = NDS * C::KB;
+    constexpr int PF = C::PF > 0 ? C::PF : N;
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int n = 0; n < PF && n < N; ++n) fr[n] = kfrag<C>(kt, kaddr, n / C::KB, n % C::KB);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        s[n % C::KB] = mfma(fr[n % PF], qf[n / C::KB], s[n % C::KB]);
+        if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, (n + PF) / C::KB, (n + PF) % C::KB);
+        if (C::PF > 0 && n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Operand fragments (queries, keys) times c, rounded to bf16.
+template <int NDS>
+__device__ inline void scale_q(bf16x8 (&qf)[NDS], float c) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        const u32x4 u = __builtin_bit_cast(u32x4, qf[ds]);
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = __builtin_bit_cast(float, u[j] << 16), hi = __builtin_bit_cast(float, u[j] & 0xffff0000u);
+            v[j] = pack_bf16(lo * c, hi * c);
+        }
+        qf[ds] = to_bf16x8(v);
+    }
+}
 // O^T += V^T P^T over the wave's keys of an LDS tile, for the NDB output
 // blocks whose V units start at vt, PF fragments in flight.  (Any product
 // X^T += T^T Y^T of an LDS tile T with B operands Y^T in the P^T layout.)
