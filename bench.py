@@ -482,14 +482,14 @@ PMC_WRITE = "WRITE_SIZE"
 # The kernel each workload's roofline is priced on (a substring of the
 # demangled name rocprofv3 reports), and whether it is priced in flops or bytes.
 # (alternatives: the first one the trace holds is taken)
-PREFILL_D128 = ("fwd_bf16_pp_kernel", "fwd_bf16_kernel<128, 64, 4, 1, 2, 0>")
+PREFILL_D128 = ("fwd_bf16_kernel<128, 64, 4, 1, 2, 0>",)
 DOMINANT = {
     "ring_1m_gqa32x8_d128": (PREFILL_D128, "mfma"),
     "prefill_bf16_h32_d128": (PREFILL_D128, "mfma"),
     "inplace:ring_1m_gqa32x8_d128": (PREFILL_D128, "mfma"),
     "inplace:prefill_bf16_h32_d128": (PREFILL_D128, "mfma"),
-    "mla_h16_d512": (("fwd_bf16_wide_kernel", "fwd_bf16_half_kernel"), "mfma"),
-    "inplace:mla_h16_d512": (("fwd_bf16_wide_kernel", "fwd_bf16_half_kernel"), "mfma"),
+    "mla_h16_d512": (("fwd_bf16_wide_kernel",), "mfma"),
+    "inplace:mla_h16_d512": (("fwd_bf16_wide_kernel",), "mfma"),
     "decode_b4_gqa32x8_cache1m": (("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>",), "hbm"),
     "decode_b4_gqa32x8_cache1m_fp8": (("fwd_fp8kv_kernel",), "hbm"),
     "bwd:prefill_bf16_h32_d128": (("bwd_",), "mfma"),

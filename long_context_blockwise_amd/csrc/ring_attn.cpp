@@ -22,13 +22,6 @@
 #include "../../include/ring_attn.h"
 #include "ra_internal.h"
 
-// Staging copies of contiguous chunks go to the copy (DMA) engines (1) rather
-// than to a blit kernel (0), which would queue for compute units behind
-// attention kernels that fill every SIMD.
-#ifndef RA_TUNE_SDMA
-#define RA_TUNE_SDMA 1
-#endif
-
 using ra::BwdArgs;
 using ra::ChunkArg;
 using ra::FwdArgs;
@@ -664,9 +657,7 @@ static int fwd_impl(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, co
         // strided (2D) copy of B rows
         auto copy = [&](char *to, const void *from, size_t row, int64_t stride) -> hipError_t {
             if ((size_t)stride * es == row || d->B == 1)
-                return hipMemcpyAsync(to, from, (size_t)d->B * row,
-                                      RA_TUNE_SDMA ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice,
-                                      ctx->side);
+                return hipMemcpyAsync(to, from, (size_t)d->B * row, hipMemcpyDeviceToDevice, ctx->side);
             return hipMemcpy2DAsync(to, row, from, (size_t)stride * es, row, d->B, hipMemcpyDeviceToDevice,
                                     ctx->side);
         };
