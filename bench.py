@@ -67,7 +67,13 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "none",
+    "digest": "d69b39232e9cccb3",
+    "ring_1m_gqa32x8_d128": 3521316897,
+    "prefill_bf16_h32_d128": 599797635,
+    "mla_h16_d512": 4262798649,
+    "decode_b4_gqa32x8_cache1m": 17250133889,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661385684,
+    "bwd:prefill_bf16_h32_d128": 7906782487,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
