@@ -323,7 +323,8 @@ int ring_attn_bwd_workspace_size(const ra_desc *d, int64_t Lq, size_t *bytes);
  * The chunks given may be a subset of those the forward saw (one ring step
  * at a time, say): m and l carry the softmax normalisation over all of them.
  * Rows with l = 0 (no visible key) have zero gradients.  Supported: bf16
- * with d_qk == d_v in {64, 128}, bf16 keys and values; RA_ERR_UNSUPPORTED
+ * with d_qk == d_v in {64, 128, 512}, bf16 keys and values (at 512 without
+ * anchor tokens or segment labels, as the forward); RA_ERR_UNSUPPORTED
  * otherwise.  The call is deterministic (no atomics). */
 int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq,
                   const ra_kv_chunk *chunks, int P, int causal,

@@ -55,9 +55,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs A) {
         const uint16_t *o = (const uint16_t *)A.out + off;
         const uint16_t *g = (const uint16_t *)A.dout + off;
         uint16_t ov[EPL], gv[EPL];
-        if constexpr (EPL == 8) {
-            *(u32x4 *)ov = *(const u32x4 *)o;
-            *(u32x4 *)gv = *(const u32x4 *)g;
+        if constexpr (EPL % 8 == 0) {
+#pragma unroll
+            for (int k = 0; k < EPL / 8; ++k) {
+                *(u32x4 *)(ov + 8 * k) = *(const u32x4 *)(o + 8 * k);
+                *(u32x4 *)(gv + 8 * k) = *(const u32x4 *)(g + 8 * k);
+            }
         } else {
             *(u32x2 *)ov = *(const u32x2 *)o;
             *(u32x2 *)gv = *(const u32x2 *)g;
@@ -744,15 +747,432 @@ void bwd_dkdv_kernel(const BwdArgs A) {
         }
 }
 
+
+// ---------------------------------------------------------------------------
+// d = 512: the four waves of a workgroup split the head dimension
+// ---------------------------------------------------------------------------
+// A workgroup owns one 32-row (dQ) or 32-key (dK/dV) block; wave w owns
+// dimensions 128w .. 128w+127 of it: its slice of the resident operands and
+// of the gradient accumulators.  Per 32-key (or 32-row) tile each wave forms
+// the partial S and dP over its dimensions (8 MFMAs each), the four partials
+// meet in LDS and every wave adds them in the same order (so all hold the
+// same bits), and the wave then takes its slice of the gradient products
+// (dQ: 8 MFMAs; dK and dV: 8 each).  Tiles are 32 keys (rows) of 1024-byte
+// rows, two stages; the exchange buffer holds 4 x 8 KiB.  One workgroup per
+// CU, one wave per SIMD.
+namespace bwide {
+struct C : Cfg<512, 32, 4, 1> {
+    static constexpr int BM = 32;  // rows per workgroup (all four waves share them)
+};
+constexpr int SL = 128;       // dimensions per wave
+constexpr int SDS = SL / 16;  // reduction steps per wave
+constexpr int SDB = SL / 32;  // 32-wide gradient blocks per wave
+constexpr int XW = 2 * 16 * 64 * 4;  // bytes of one wave's partial S and dP
+
+// Partials: group j (elements 4j .. 4j+3) of block b (0: S, 1: dP) of wave w
+// at byte ((2w + b) * 4 + j) * 1024 + 16 * lane.
+__device__ inline void exchange_put(char *x, int w, int lane, const f32x16 &s, const f32x16 &dp) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<f32x4 *>(x + ((2 * w) * 4 + j) * 1024 + 16 * lane) =
+            f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+        *reinterpret_cast<f32x4 *>(x + ((2 * w + 1) * 4 + j) * 1024 + 16 * lane) =
+            f32x4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
+    }
+}
+// s, dp: in, the wave's own partials; out, the sums over the four waves in
+// the order 0, 1, 2, 3.
+__device__ inline void exchange_sum(const char *x, int w, int lane, f32x16 &s, f32x16 &dp) {
+    f32x16 ts, td;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        f32x16 ps, pd;
+        if (v == w) {
+            ps = s, pd = dp;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(x + ((2 * v) * 4 + j) * 1024 + 16 * lane);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(x + ((2 * v + 1) * 4 + j) * 1024 + 16 * lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ps[4 * j + e] = a[e], pd[4 * j + e] = b[e];
+            }
+        }
+        if (v == 0) {
+            ts = ps, td = pd;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ts[i] += ps[i], td[i] += pd[i];
+        }
+    }
+    s = ts, dp = td;
+}
+}  // namespace bwide
+
+// dQ for d = 512: 32 query rows per workgroup (S^T = K Q^T, rows on the lanes).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_wide_kernel(const BwdArgs A) {
+    using namespace bwide;
+    const FwdArgs &a = A.f;
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(2, C::TILE)
+    __shared__ __attribute__((aligned(1024))) char xch[4 * XW];
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int l32 = lane & 31, g = lane >> 5;
+    const WorkTile wt = work_tile<C>(a);
+    int64_t wv_tlo, wv_thi;  // the workgroup's rows (the same for every wave)
+    token_range(a, wt.p0, wt.p0 + 32, wv_tlo, wv_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + l32);
+
+    // the wave's slice of the row's queries and output gradients (B operands)
+    bf16x8 qf[SDS], gf[SDS];
+    load_q(a, wt, row, g, SL * w, qf);
+    {
+        const uint16_t *gp =
+            (const uint16_t *)A.dout + wt.b * a.o_sb + row.t * a.o_ss + row.h * a.o_sh + SL * w + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < SDS; ++ds) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row.ok) v = *(const u32x4 *)(gp + 16 * ds);
+            gf[ds] = to_bf16x8(v);
+        }
+    }
+    float nl = -kPosInf, nd = 0.f;  // -lse2 and -D of the row (rows past Lq: P = 0)
+    if (row.ok) {
+        const int64_t idx = (((int64_t)wt.b * a.Hq + row.h) * a.Lq + row.t) * 2;
+        nl = A.ld[idx];
+        nd = A.ld[idx + 1];
+    }
+    const float c2 = a.scale_log2;
+    f32x16 acc[SDB];
+#pragma unroll
+    for (int j = 0; j < SDB; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+
+    for (int c = 0; c < a.n_chunks; ++c) {
+        int64_t kbeg, kend;
+        int ntiles;
+        if (!chunk_range(a, wt, c, 0, kbeg, kend, ntiles, 32) || ntiles == 0) continue;  // uniform
+        const ChunkArg ch = a.chunks[c];
+        const VisRange vis = visible_range(a, row, ch.start, kbeg, kend);
+        const uint16_t *kbase = (const uint16_t *)ch.k + wt.b * a.k_sb + wt.hk * a.k_sh;
+        const uint16_t *vbase = (const uint16_t *)ch.v + wt.b * a.v_sb + wt.hk * a.v_sh;
+        auto issue = [&](auto u, int t) {
+            const int64_t k0 = kbeg + (int64_t)t * 32;
+            load_tile<C>(kbase, a.k_ss, k0, kend, kst(u), w, lane);
+            load_tile<C>(vbase, a.v_ss, k0, kend, vst(u), w, lane);
+        };
+        auto wait_for = [&](int need, int last) {
+            const int after = last - need;
+            wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+        };
+        tile_barrier();  // the previous chunk's tiles and partials are no longer read
+        issue(ic<0>{}, 0);
+        wait_for(0, 0);
+        for_tiles<2>(ntiles, [&](auto u, int it) {
+            constexpr int U = decltype(u)::value;
+            if (it + 1 < ntiles) issue(ic<(U + 1) % 2>{}, it + 1);
+            const int64_t k0 = kbeg + (int64_t)it * 32;
+            // (the same rows in every wave: the tests and the barrier below are uniform)
+            if (!keys_unseen(a, ch.start, k0, 32, wv_tlo, wv_thi)) {
+                const char *kt = kst(u), *vt = vst(u);
+                f32x16 s[1], dp;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[0][i] = 0.f, dp[i] = 0.f;
+#pragma unroll
+                for (int ds = 0; ds < SDS; ++ds) {
+                    s[0] = mfma(kfrag<C>(kt, kaddr, SDS * w + ds, 0), qf[ds], s[0]);
+                    dp = mfma(kfrag<C>(vt, kaddr, SDS * w + ds, 0), gf[ds], dp);
+                }
+                exchange_put(xch, w, lane, s[0], dp);
+                tile_barrier();
+                exchange_sum(xch, w, lane, s[0], dp);
+                if (!keys_all_seen(a, ch.start, k0, 32, kend, wv_tlo, wv_thi))
+                    mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
+                // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
+                bf16x8 pf[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    u32x4 pk;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i0 = 8 * hh + 2 * j, i1 = i0 + 1;
+                        const float p0 = exp2_fast(__builtin_fmaf(s[0][i0], c2, nl));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[0][i1], c2, nl));
+                        pk[j] = pack_bf16(p0 * (dp[i0] + nd), p1 * (dp[i1] + nd));
+                    }
+                    pf[hh] = to_bf16x8(pk);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int j = 0; j < SDB; ++j) acc[j] = mfma(vfrag<C>(kt, vaddr, ks, SDB * w + j), pf[ks], acc[j]);
+            }
+            // the next tile is in place; this stage and the partials are free
+            if (it + 1 < ntiles) wait_for(it + 1, it + 1);
+            else tile_barrier();
+        });
+    }
+
+    if (!row.ok) return;
+    // element i of block j in lane l is d = 128w + 32j + 8(i/4) + 4g + i%4; with
+    // ACCUMULATE every old value is loaded before any store
+    float *dq = A.dq + row.srow * 512 + SL * w + 4 * g;
+    f32x4 old[SDB][4];
+    if (A.accumulate) {
+#pragma unroll
+        for (int j = 0; j < SDB; ++j)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) old[j][i4] = *(const f32x4 *)(dq + 32 * j + 8 * i4);
+    }
+#pragma unroll
+    for (int j = 0; j < SDB; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = A.scale * acc[j][4 * i4 + e];
+            if (A.accumulate) v += old[j][i4];
+            *(f32x4 *)(dq + 32 * j + 8 * i4) = v;
+        }
+}
+
+// dK, dV for d = 512: 32 keys per workgroup (S = Q K^T, keys on the lanes),
+// the query rows that can see them walked in tiles of 32.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_wide_kernel(const BwdArgs A) {
+    using namespace bwide;
+    const FwdArgs &a = A.f;
+    constexpr int LPT = 2 * C::LOADS_PER_WAVE;
+    RA_STAGE_ARRAYS(2, C::TILE)  // stage u: the Q tile (kst), the dO tile (vst)
+    __shared__ __attribute__((aligned(1024))) char xch[4 * XW];
+
+    const int lane = threadIdx.x & 63, w = wave_index();
+    const int l32 = lane & 31, g = lane >> 5;
+    const ChunkArg ch = a.chunks[A.chunk];
+    const int64_t len = ch.len;
+    const int nkt = (int)((len + 31) / 32);
+    int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = lid % nkt;  // earliest keys (most rows under causal masking) first
+    lid /= nkt;
+    const int hk = lid % a.Hkv;
+    const int b = lid / a.Hkv;
+    const int64_t wk0 = (int64_t)kt * 32;  // the workgroup's first key
+    const int64_t key = wk0 + l32;         // this lane's key
+    const bool key_ok = key < len;
+
+    // the wave's slice of the key's K and V (B operands)
+    bf16x8 kf[SDS], vf[SDS];
+    {
+        const uint16_t *kp = (const uint16_t *)ch.k + b * a.k_sb + key * a.k_ss + hk * a.k_sh + SL * w + 8 * g;
+        const uint16_t *vp = (const uint16_t *)ch.v + b * a.v_sb + key * a.v_ss + hk * a.v_sh + SL * w + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < SDS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            if (key_ok) {
+                x = *(const u32x4 *)(kp + 16 * ds);
+                y = *(const u32x4 *)(vp + 16 * ds);
+            }
+            kf[ds] = to_bf16x8(x);
+            vf[ds] = to_bf16x8(y);
+        }
+    }
+    f32x16 dk[SDB], dv[SDB];
+#pragma unroll
+    for (int j = 0; j < SDB; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[j][i] = dv[j][i] = 0.f;
+
+    // query rows that can see any key of the workgroup
+    const int64_t kp_lo = ch.start + wk0;
+    const int64_t kp_hi = ch.start + (wk0 + 32 < len ? wk0 + 32 : len) - 1;
+    int64_t t_lo = 0, t_hi = a.Lq - 1;
+    if (a.causal) t_lo = kp_lo - a.q_offset > t_lo ? kp_lo - a.q_offset : t_lo;
+    if (a.window > 0) {
+        const int64_t hi = kp_hi + a.window - a.q_offset;
+        t_hi = hi < t_hi ? hi : t_hi;
+        if (!a.causal) {
+            const int64_t lo = kp_lo - a.window - a.q_offset;
+            t_lo = lo > t_lo ? lo : t_lo;
+        }
+    }
+    const bool no_rows = t_hi < t_lo;  // (rounding t_lo down must not revive an empty range)
+    t_lo = t_lo / 32 * 32;
+    const int n1 = no_rows ? 0 : (int)((t_hi - t_lo) / 32 + 1);
+    const int ntiles = n1 * a.G;
+
+    int kaddr[C::NKA];
+    k_addrs<C>(0, l32, g, kaddr);
+    int vaddr[2][C::NVD];
+    v_addrs<C>(0, lane, vaddr);
+    const float c2 = a.scale_log2;
+    const int64_t kpos = ch.start + key;
+
+    auto tile_of = [&](int it, int &h, int64_t &t0) {
+        h = hk * a.G + it / n1;
+        t0 = t_lo + 32 * (int64_t)(it % n1);
+    };
+    auto issue = [&](auto u, int it) {
+        int h;
+        int64_t t0;
+        tile_of(it, h, t0);
+        const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
+        const uint16_t *gb = (const uint16_t *)A.dout + b * a.o_sb + h * a.o_sh;
+        load_tile<C>(qb, a.q_ss, t0, a.Lq, kst(u), w, lane);
+        load_tile<C>(gb, a.o_ss, t0, a.Lq, vst(u), w, lane);
+    };
+    auto wait_for = [&](int need, int last) {
+        const int after = last - need;
+        wait_tiles_in_flight<LPT>(after < 0 ? 0 : after);
+    };
+
+    if (ntiles > 0) {
+        issue(ic<0>{}, 0);
+        wait_for(0, 0);
+    }
+    for_tiles<2>(ntiles, [&](auto u, int it) {
+        constexpr int U = decltype(u)::value;
+        int h;
+        int64_t t0;
+        tile_of(it, h, t0);
+        // -lse2 and -D of the tile's rows for this lane's elements: element
+        // i = 4j + e is row t0 + 8j + 4g + e, pairs (nl, nd) interleaved.
+        // Requested before the next tile's loads, so that waiting for them
+        // leaves those in flight; rows past Lq read 0 (and are masked).
+        f32x4 bx[4], by[4];
+        {
+            const int64_t nrows = a.Lq - t0 < 32 ? a.Lq - t0 : 32;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(A.ld + (((int64_t)b * a.Hq + h) * a.Lq + t0) * 2), (short)0, (int)(nrows * 8), kBufferFlags);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bx[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 8 * (8 * j + 4 * g), 0, 0));
+                by[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 8 * (8 * j + 4 * g) + 16, 0, 0));
+            }
+        }
+        if (it + 1 < ntiles) issue(ic<(U + 1) % 2>{}, it + 1);
+        const int64_t thi = t0 + 31 < a.Lq - 1 ? t0 + 31 : a.Lq - 1;
+        // (the same keys in every wave: the tests and the barrier below are uniform)
+        if (!(wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi))) {
+            const char *qt = kst(u), *gt = vst(u);
+            // partial S = Q K^T and dP = dO V^T over the wave's dimensions: rows on M, keys on N
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = 0.f, dp[i] = 0.f;
+#pragma unroll
+            for (int ds = 0; ds < SDS; ++ds) {
+                s = mfma(kfrag<C>(qt, kaddr, SDS * w + ds, 0), kf[ds], s);
+                dp = mfma(kfrag<C>(gt, kaddr, SDS * w + ds, 0), vf[ds], dp);
+            }
+            exchange_put(xch, w, lane, s, dp);
+            tile_barrier();
+            exchange_sum(xch, w, lane, s, dp);
+            if (!(t0 + 31 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi))) {
+                // element i is row t0 + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
+                const int64_t big = 1 << 30;
+                const int64_t base = a.q_offset + t0 + 4 * g - kpos;  // qpos - kpos at ro = 0
+                int64_t lo = -big, hi = a.Lq - t0 - 4 * g;
+                if (a.causal) lo = -base;
+                if (a.window > 0) {
+                    hi = a.window - base + 1 < hi ? a.window - base + 1 : hi;
+                    if (!a.causal) lo = -a.window - base;
+                }
+                if (!key_ok) lo = big;
+                lo = lo < -big ? -big : (lo > big ? big : lo);
+                hi = hi < -big ? -big : (hi > big ? big : hi);
+                const int lo32 = (int)lo, hi32 = (int)hi;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int ro = 8 * (i >> 2) + (i & 3);
+                    if (ro < lo32 || ro >= hi32) s[i] = kNegInf;
+                }
+            }
+            // P = exp2(S c - lse2) and dS = P (dP - D) of rows 16ks .. 16ks+15, as B operands
+            bf16x8 pp[2], pd[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 a4, b4;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const f32x4 x = bx[2 * ks + jj], y = by[2 * ks + jj];  // rows 16ks + 8jj + 4g + 0..3
+                    const float l4[4] = {x[0], x[2], y[0], y[2]}, d4[4] = {x[1], x[3], y[1], y[3]};
+#pragma unroll
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        const int i0 = 8 * ks + 4 * jj + 2 * r2, i1 = i0 + 1;
+                        const float p0 = exp2_fast(__builtin_fmaf(s[i0], c2, l4[2 * r2]));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[i1], c2, l4[2 * r2 + 1]));
+                        a4[2 * jj + r2] = pack_bf16(p0, p1);
+                        b4[2 * jj + r2] = pack_bf16(p0 * (dp[i0] + d4[2 * r2]), p1 * (dp[i1] + d4[2 * r2 + 1]));
+                    }
+                }
+                pp[ks] = to_bf16x8(a4);
+                pd[ks] = to_bf16x8(b4);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS over the wave's dimensions
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < SDB; ++j) {
+                    dv[j] = mfma(vfrag<C>(gt, vaddr, ks, SDB * w + j), pp[ks], dv[j]);
+                    dk[j] = mfma(vfrag<C>(qt, vaddr, ks, SDB * w + j), pd[ks], dk[j]);
+                }
+        }
+        // the next tile is in place; this stage and the partials are free
+        if (it + 1 < ntiles) wait_for(it + 1, it + 1);
+        else tile_barrier();
+    });
+
+    if (!key_ok) return;
+    // element i of block j in lane l is d = 128w + 32j + 8(i/4) + 4g + i%4 of the lane's key
+    const int64_t off = ((b * len + key) * a.Hkv + hk) * 512 + SL * w + 4 * g;
+    float *pk = A.dk + off, *pv = A.dv + off;
+    f32x4 ok[SDB][4], ov[SDB][4];
+    if (A.accumulate) {
+#pragma unroll
+        for (int j = 0; j < SDB; ++j)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                ok[j][i4] = *(const f32x4 *)(pk + 32 * j + 8 * i4);
+                ov[j][i4] = *(const f32x4 *)(pv + 32 * j + 8 * i4);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < SDB; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int e = 32 * j + 8 * i4;
+            f32x4 x, y;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[q] = A.scale * dk[j][4 * i4 + q];
+                y[q] = dv[j][4 * i4 + q];
+            }
+            if (A.accumulate) {
+                x += ok[j][i4];
+                y += ov[j][i4];
+            }
+            *(f32x4 *)(pk + e) = x;
+            *(f32x4 *)(pv + e) = y;
+        }
+}
+
 }  // namespace
 
-int bwd_dq_row_tile() { return 128; }
+int bwd_dq_row_tile(int d) { return d == 512 ? bwide::C::BM : 128; }
 
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s) {
     const int64_t rows = (int64_t)a.f.B * a.f.Lq * a.f.Hq;
     if (rows == 0) return hipSuccess;
     const unsigned grid = (unsigned)((rows * 16 + 255) / 256);
-    if (d == 128)
+    if (d == 512)
+        hipLaunchKernelGGL(bwd_pre_kernel<512>, dim3(grid), dim3(256), 0, s, a);
+    else if (d == 128)
         hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, s, a);
@@ -776,13 +1196,20 @@ static void launch_dq_ext(const BwdArgs &a, unsigned grid, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.f.n_rowtiles * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;
-    if (d == 128) launch_dq_ext<128>(a, grid, s);
+    if (d == 512) hipLaunchKernelGGL(bwd_dq_wide_kernel, dim3(grid), dim3(256), 0, s, a);
+    else if (d == 128) launch_dq_ext<128>(a, grid, s);
     else launch_dq_ext<64>(a, grid, s);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s) {
     const int64_t len = a.f.chunks[a.chunk].len;
+    if (d == 512) {
+        const unsigned grid = (unsigned)((len + 31) / 32 * a.f.Hkv * a.f.B);
+        if (grid == 0) return hipSuccess;
+        hipLaunchKernelGGL(bwd_dkdv_wide_kernel, dim3(grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const int64_t nkt = (len + kKvKeys - 1) / kKvKeys;
     const unsigned grid = (unsigned)(nkt * a.f.Hkv * a.f.B);
     if (grid == 0) return hipSuccess;

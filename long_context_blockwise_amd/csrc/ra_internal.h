@@ -61,7 +61,7 @@ struct BwdArgs {
     FwdArgs f;
     const void *out, *dout;  // [B, Lq, Hq, d_v] in the input dtype
     const float *m, *l;      // forward state after all chunks [B, Lq, Hq]
-    float *ld;               // workspace [B, Hq, Lq][2]: (m + ln l) log2(e), rowsum(dO * out)
+    float *ld;               // workspace [B, Hq, Lq][2]: -(m + ln l) log2(e), -rowsum(dO * out)
     float *dq;               // [B, Lq, Hq, d_qk] fp32, dense
     float *dk, *dv;          // dK/dV kernel: the launch's chunk, [B, len, Hkv, d] fp32, dense
     int chunk;               // dK/dV kernel: index into f.chunks
@@ -96,7 +96,7 @@ hipError_t launch_fill_nan(void *p, size_t bytes, hipStream_t s);
 // Backward, bf16 with d = 64 or 128: row statistics, dQ over the chunks of
 // a.f (rows tiled like the forward, bwd_dq_row_tile rows per workgroup), and
 // dK/dV of chunk a.chunk.
-int bwd_dq_row_tile();
+int bwd_dq_row_tile(int d);
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs &a, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, hipStream_t s);

@@ -756,8 +756,8 @@ static size_t bwd_ld_bytes(const ra_desc *d, int64_t Lq) { return align_up((size
 static int check_bwd(const ra_desc *d, int64_t Lq, Strides *st) {
     int rc = check_desc(d, Lq, st);
     if (rc) return rc;
-    if (d->dtype != RA_BF16 || (d->d_qk != 64 && d->d_qk != 128))
-        return fail(RA_ERR_UNSUPPORTED, "the backward is built for bf16 with d_qk = d_v in {64, 128}");
+    if (d->dtype != RA_BF16 || (d->d_qk != 64 && d->d_qk != 128 && d->d_qk != 512))
+        return fail(RA_ERR_UNSUPPORTED, "the backward is built for bf16 with d_qk = d_v in {64, 128, 512}");
     if (kv_fp8(d)) return fail(RA_ERR_UNSUPPORTED, "the backward takes bf16 keys and values");
     // 32-row tiles of q and dout are addressed with 32-bit offsets from a 64-bit base
     if (st->q[1] >= ((int64_t)1 << 24) || st->o[1] >= ((int64_t)1 << 24))
@@ -820,7 +820,7 @@ int ring_attn_bwd(ra_ctx *ctx, const ra_desc *d, const void *q, int64_t Lq, cons
     A.ld = (float *)workspace;
     A.dq = dq;
     A.scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->d_qk);
-    const int bm = ra::bwd_dq_row_tile();
+    const int bm = ra::bwd_dq_row_tile(d->d_qk);
     A.f.Lq_pad = A.f.Lq * A.f.G <= bm ? A.f.Lq : (A.f.Lq + bm - 1) / bm * bm;
     A.f.n_rowtiles = (int)(((int64_t)A.f.G * A.f.Lq_pad + bm - 1) / bm);
 

@@ -268,7 +268,9 @@ def test_bwd_workspace_and_validation(lib):
     assert n.value == 2 * 4 * 100 * 8  # 6400, already a multiple of 256
     assert lib.ring_attn_bwd_workspace_size(ctypes.byref(_desc(B=1, Hq=3, Hkv=3, d=64)), 5, ctypes.byref(n)) == 0
     assert n.value == 256
-    for bad in (_desc(dtype=ra.RA_F32), _desc(d=512)):
+    assert lib.ring_attn_bwd_workspace_size(ctypes.byref(_desc(B=1, Hq=16, Hkv=1, d=512)), 8, ctypes.byref(n)) == 0
+    assert n.value == 16 * 8 * 8  # 1024, a multiple of 256
+    for bad in (_desc(dtype=ra.RA_F32), _desc(d=256), _desc(d=512, dtype=ra.RA_F32)):
         assert lib.ring_attn_bwd_workspace_size(ctypes.byref(bad), 8, ctypes.byref(n)) == rb.RA_ERR_UNSUPPORTED
     f8 = _desc()
     f8.kv_dtype = rb.RA_FP8_E4M3

@@ -2,7 +2,9 @@
 attention definition, through the C ABI: causal and non-causal, windows,
 GQA, ragged chunks and tails, d = 64 and 128, rows that see no key; the
 accumulate flag, per-chunk calls, determinism, and a two-device ring whose
-dK/dV travel with their chunks.
+dK/dV travel with their chunks; 512-wide heads at small sizes, and the
+d = 512 workload at full size (dQ of sampled rows of one head against the
+oracle, dK and dV through identities that hold at any size).
 
 Tolerance: the kernels round P and dS to bf16 for the matrix cores (unit
 roundoff 2^-8) and accumulate in fp32; like the forward output this gives a
@@ -73,6 +75,11 @@ CASES = [
     (1, 128, 4, 2, (200, 170), 180, 100, False, 40),      # two-sided window
     (1, 64, 2, 2, (77, 130), 300, 0, False, 65),          # rows past every window: no key
     (1, 128, 4, 4, (256,), 255, 0, True, 0),              # diagonal at position 0
+    # 512-wide heads: four waves split the head dimension
+    (1, 512, 4, 1, (96, 160), 100, 150, True, 0),         # GQA 4, ragged, offset mid-chunk
+    (1, 512, 2, 1, (64, 33), 65, 0, True, 0),             # diagonal at position 0, 1-row tails
+    (1, 512, 16, 1, (64, 64), 40, 90, True, 30),          # GQA 16, causal window
+    (2, 512, 2, 2, (70,), 50, 10, False, 0),              # non-causal, two sequences
 ]
 
 
@@ -188,3 +195,44 @@ def test_bwd_full_size_head_slice():
     for c in range(len(chunks)):
         check_grad(grads[c][0][:, :, h:h + 1], dks[c], f"full-size dK[{c}] head {h}")
         check_grad(grads[c][1][:, :, h:h + 1], dvs[c], f"full-size dV[{c}] head {h}")
+
+
+def test_bwd_full_size_d512():
+    """The d = 512 workload's backward at full size (16 query heads on one KV
+    head, 8 x 16384 keys, query chunk 7, causal).  dQ of sampled rows of one
+    query head against the oracle run on those rows alone (a row's dQ needs
+    only its own softmax).  dK and dV through identities of the definition:
+    the dS of a row sums to 0 over the keys it sees, so the dK of all keys
+    sum to 0; its P sums to 1, so the dV of all keys sum to the dO of all
+    rows of the group."""
+    wl = inputs.WORKLOADS["mla_h16_d512"]
+    x = inputs.make(wl, DEV)
+    order = ra.ring_attn_ring_order(wl.q_offset // wl.chunk_len, wl.P)
+    chunks = x.chunks(order)
+    out, st = ra.ring_attn_fwd(x.q, chunks, True, wl.q_offset, flags=ra.RA_FLAG_NO_SPLIT_KV, want_state=True)
+    dout = inputs.output_grad(wl, DEV)
+    dq, grads = ra.ring_attn_bwd(x.q, chunks, out, dout, st, True, wl.q_offset)
+    torch.cuda.synchronize()
+    h = 5
+    rows = inputs.sample_rows(wl.Lq, tile=2048, seed=7, extra=(0, 31, 32, wl.Lq - 33, wl.Lq - 1))
+    print(f"[bwd d512] {len(rows)} sampled rows of head {h}", flush=True)
+    # (bf16 bits as uint16 arrays, converted once for all the per-row calls)
+    ch = [(k.cpu().view(torch.int16).numpy().view(np.uint16), v.cpu().view(torch.int16).numpy().view(np.uint16), st_)
+          for (k, v, st_) in chunks]
+    got = dq[0, rows, h].cpu().numpy()
+    want = []
+    for t in rows:
+        qt = x.q[:, t:t + 1, h:h + 1].cpu().contiguous()
+        gt = dout[:, t:t + 1, h:h + 1].cpu().contiguous()
+        dq_ref, _, _ = oracle.attention_bwd(qt, ch, gt, wl.q_offset + t, True)
+        want.append(dq_ref[0, 0, 0])
+    check_grad(got, np.stack(want), "full-size d512 dQ (sampled rows)")
+    dk_sum = sum(g[0].double().sum(dim=(0, 1)) for g in grads)  # [Hkv, d]
+    dk_abs = sum(g[0].double().abs().sum(dim=(0, 1)) for g in grads)
+    rel = float(dk_sum.norm() / dk_abs.norm())
+    assert rel <= 1e-2, f"sum of dK over all keys: {rel} of the summed magnitudes"
+    dv_sum = sum(g[1].double().sum(dim=(0, 1)) for g in grads)
+    do_sum = dout.double().sum(dim=(0, 1)).reshape(wl.Hkv, wl.Hq // wl.Hkv, -1).sum(dim=1)
+    e = errors(dv_sum.cpu().numpy(), do_sum.cpu().numpy())
+    assert e["rel_l2"] <= 1e-2, f"sum of dV over all keys against the sum of dO: {e}"
+    print(f"[bwd d512] dK sum {rel:.2e}, dV sum {e}", flush=True)
