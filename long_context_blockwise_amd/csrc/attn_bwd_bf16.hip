@@ -780,32 +780,57 @@ __device__ inline void exchange_put(char *x, int w, int lane, const f32x16 &s, c
             f32x4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
     }
 }
-// s, dp: in, the wave's own partials; out, the sums over the four waves in
-// the order 0, 1, 2, 3.
-__device__ inline void exchange_sum(const char *x, int w, int lane, f32x16 &s, f32x16 &dp) {
-    f32x16 ts, td;
+// The sums over the four waves' partials, in the order 0, 1, 2, 3 (the own
+// partial is read back too, so that the code is the same in every wave).
+__device__ inline void exchange_sum(const char *x, int lane, f32x16 &s, f32x16 &dp) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        f32x16 ps, pd;
-        if (v == w) {
-            ps = s, pd = dp;
-        } else {
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(x + ((2 * v) * 4 + j) * 1024 + 16 * lane);
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(x + ((2 * v + 1) * 4 + j) * 1024 + 16 * lane);
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(x + ((2 * v) * 4 + j) * 1024 + 16 * lane);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(x + ((2 * v + 1) * 4 + j) * 1024 + 16 * lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ps[4 * j + e] = a[e], pd[4 * j + e] = b[e];
+            for (int e = 0; e < 4; ++e) {
+                s[4 * j + e] = v == 0 ? a[e] : s[4 * j + e] + a[e];
+                dp[4 * j + e] = v == 0 ? b[e] : dp[4 * j + e] + b[e];
             }
         }
-        if (v == 0) {
-            ts = ps, td = pd;
-        } else {
+}
+
+// Partial S (A fragments from tile a) and dP (from tile b) over the wave's
+// SDS reduction steps, the B operands of step ds in AGPRs (bs[ds], bd[ds]):
+// inline-asm MFMAs whose results stay in VGPRs, where the exchange and the
+// vector work read them (the builtin's AGPR form would copy them out); the
+// s_nops cover the wait states before a vector instruction may read them.
+template <class KF>
+__device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[SDS], const bf16x8 (&bd)[SDS], f32x16 &s,
+                                      f32x16 &dp) {
+    constexpr int PF = 4;  // fragments read ahead
+    bf16x8 fr[PF];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ts[i] += ps[i], td[i] += pd[i];
-        }
+    for (int n = 0; n < PF; ++n) fr[n] = frag(n);
+#pragma unroll
+    for (int n = 0; n < 2 * SDS; ++n) {
+        const int ds = n / 2;
+        if (n == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "a"(bs[0]));
+        else if (n == 1)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(dp) : "v"(fr[1]), "a"(bd[0]));
+        else if (n % 2 == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "a"(bs[ds]));
+        else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp) : "v"(fr[n % PF]), "a"(bd[ds]));
+        if (n + PF < 2 * SDS) fr[n % PF] = frag(n + PF);
+        if (n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
     }
-    s = ts, dp = td;
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+}
+
+// Resident B operands moved into AGPRs once (the asm operands then read them there).
+template <int N>
+__device__ inline void to_agprs(const bf16x8 (&v)[N], bf16x8 (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "=a"(a[i]) : "0"(v[i]));
 }
 }  // namespace bwide
 
@@ -838,6 +863,9 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
             gf[ds] = to_bf16x8(v);
         }
     }
+    bf16x8 qa[SDS], ga[SDS];
+    to_agprs(qf, qa);
+    to_agprs(gf, ga);
     float nl = -kPosInf, nd = 0.f;  // -lse2 and -D of the row (rows past Lq: P = 0)
     if (row.ok) {
         const int64_t idx = (((int64_t)wt.b * a.Hq + row.h) * a.Lq + row.t) * 2;
@@ -883,16 +911,11 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
             if (!keys_unseen(a, ch.start, k0, 32, wv_tlo, wv_thi)) {
                 const char *kt = kst(u), *vt = vst(u);
                 f32x16 s[1], dp;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[0][i] = 0.f, dp[i] = 0.f;
-#pragma unroll
-                for (int ds = 0; ds < SDS; ++ds) {
-                    s[0] = mfma(kfrag<C>(kt, kaddr, SDS * w + ds, 0), qf[ds], s[0]);
-                    dp = mfma(kfrag<C>(vt, kaddr, SDS * w + ds, 0), gf[ds], dp);
-                }
+                partial_scores([&](int n) { return kfrag<C>(n % 2 ? vt : kt, kaddr, SDS * w + n / 2, 0); }, qa, ga,
+                               s[0], dp);
                 exchange_put(xch, w, lane, s[0], dp);
                 tile_barrier();
-                exchange_sum(xch, w, lane, s[0], dp);
+                exchange_sum(xch, lane, s[0], dp);
                 if (!keys_all_seen(a, ch.start, k0, 32, kend, wv_tlo, wv_thi))
                     mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
                 // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
@@ -983,6 +1006,9 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
             vf[ds] = to_bf16x8(y);
         }
     }
+    bf16x8 ka[SDS], va[SDS];
+    to_agprs(kf, ka);
+    to_agprs(vf, va);
     f32x16 dk[SDB], dv[SDB];
 #pragma unroll
     for (int j = 0; j < SDB; ++j)
@@ -1063,16 +1089,11 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
             const char *qt = kst(u), *gt = vst(u);
             // partial S = Q K^T and dP = dO V^T over the wave's dimensions: rows on M, keys on N
             f32x16 s, dp;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.f, dp[i] = 0.f;
-#pragma unroll
-            for (int ds = 0; ds < SDS; ++ds) {
-                s = mfma(kfrag<C>(qt, kaddr, SDS * w + ds, 0), kf[ds], s);
-                dp = mfma(kfrag<C>(gt, kaddr, SDS * w + ds, 0), vf[ds], dp);
-            }
+            partial_scores([&](int n) { return kfrag<C>(n % 2 ? gt : qt, kaddr, SDS * w + n / 2, 0); }, ka, va, s,
+                           dp);
             exchange_put(xch, w, lane, s, dp);
             tile_barrier();
-            exchange_sum(xch, w, lane, s, dp);
+            exchange_sum(xch, lane, s, dp);
             if (!(t0 + 31 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi))) {
                 // element i is row t0 + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
                 const int64_t big = 1 << 30;
