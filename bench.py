@@ -79,7 +79,7 @@ MEASURED_TRAFFIC = {
 HEADLINE = "ring_1m_gqa32x8_d128"
 SECONDARY = ("prefill_bf16_h32_d128,mla_h16_d512,decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,"
              "tiny_ring_fp32,bwd:prefill_bf16_h32_d128,inplace:prefill_bf16_h32_d128,inplace:ring_1m_gqa32x8_d128,"
-             "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128")
+             "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128,bwd:mla_h16_d512")
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -499,6 +499,7 @@ DOMINANT = {
     "decode_b4_gqa32x8_cache1m": (("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>",), "hbm"),
     "decode_b4_gqa32x8_cache1m_fp8": (("fwd_fp8kv_kernel",), "hbm"),
     "bwd:prefill_bf16_h32_d128": (("bwd_",), "mfma"),
+    "bwd:mla_h16_d512": (("bwd_",), "mfma"),
 }
 
 

@@ -802,15 +802,15 @@ __device__ inline void exchange_sum(const char *x, int lane, f32x16 &s, f32x16 &
 // inline-asm MFMAs whose results stay in VGPRs, where the exchange and the
 // vector work read them (the builtin's AGPR form would copy them out); the
 // s_nops cover the wait states before a vector instruction may read them.
-template <class KF>
-__device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[SDS], const bf16x8 (&bd)[SDS], f32x16 &s,
+template <int NS, class KF>
+__device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[NS], const bf16x8 (&bd)[NS], f32x16 &s,
                                       f32x16 &dp) {
     constexpr int PF = 4;  // fragments read ahead
     bf16x8 fr[PF];
 #pragma unroll
     for (int n = 0; n < PF; ++n) fr[n] = frag(n);
 #pragma unroll
-    for (int n = 0; n < 2 * SDS; ++n) {
+    for (int n = 0; n < 2 * NS; ++n) {
         const int ds = n / 2;
         if (n == 0)
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "a"(bs[0]));
@@ -820,7 +820,7 @@ __device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[SDS], const 
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "a"(bs[ds]));
         else
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp) : "v"(fr[n % PF]), "a"(bd[ds]));
-        if (n + PF < 2 * SDS) fr[n % PF] = frag(n + PF);
+        if (n + PF < 2 * NS) fr[n % PF] = frag(n + PF);
         if (n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
@@ -834,38 +834,54 @@ __device__ inline void to_agprs(const bf16x8 (&v)[N], bf16x8 (&a)[N]) {
 }
 }  // namespace bwide
 
-// dQ for d = 512: 32 query rows per workgroup (S^T = K Q^T, rows on the lanes).
+// dQ for d = 512: 64 query rows per workgroup in two 32-row blocks (S^T =
+// K Q^T, rows on the lanes).  Wave w = 2h + r takes row block r and the
+// head-dimension half h (256 dimensions): each K/V tile feeds 64 rows, and a
+// wave sums its partials with one partner's (wave w ^ 2).
+namespace bwq {
+struct C : Cfg<512, 32, 4, 1> {
+    static constexpr int BM = 64;  // rows per workgroup
+};
+constexpr int SL = 256;       // dimensions per wave
+constexpr int SDS = SL / 16;  // reduction steps per wave
+constexpr int SDB = SL / 32;  // 32-wide dQ blocks per wave
+}  // namespace bwq
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_wide_kernel(const BwdArgs A) {
-    using namespace bwide;
+    using bwq::C;
+    using bwq::SDB;
+    using bwq::SDS;
+    using bwq::SL;
     const FwdArgs &a = A.f;
     constexpr int LPT = 2 * C::LOADS_PER_WAVE;
     RA_STAGE_ARRAYS(2, C::TILE)
-    __shared__ __attribute__((aligned(1024))) char xch[4 * XW];
+    __shared__ __attribute__((aligned(1024))) char xch[4 * bwide::XW];
 
     const int lane = threadIdx.x & 63, w = wave_index();
+    const int r = w & 1, hf = w >> 1;
     const int l32 = lane & 31, g = lane >> 5;
     const WorkTile wt = work_tile<C>(a);
-    int64_t wv_tlo, wv_thi;  // the workgroup's rows (the same for every wave)
-    token_range(a, wt.p0, wt.p0 + 32, wv_tlo, wv_thi);
-    const LaneRow row = lane_row(a, wt, wt.p0 + l32);
+    int64_t wg_tlo, wg_thi;  // the workgroup's rows: tile tests are the same in every wave
+    token_range(a, wt.p0, wt.p0 + 64, wg_tlo, wg_thi);
+    const LaneRow row = lane_row(a, wt, wt.p0 + 32 * r + l32);
 
-    // the wave's slice of the row's queries and output gradients (B operands)
-    bf16x8 qf[SDS], gf[SDS];
-    load_q(a, wt, row, g, SL * w, qf);
+    // the wave's half of the row's queries and output gradients (B operands, moved to AGPRs)
+    bf16x8 qa[SDS], ga[SDS];
     {
+        bf16x8 qf[SDS], gf[SDS];
+        load_q(a, wt, row, g, SL * hf, qf);
         const uint16_t *gp =
-            (const uint16_t *)A.dout + wt.b * a.o_sb + row.t * a.o_ss + row.h * a.o_sh + SL * w + 8 * g;
+            (const uint16_t *)A.dout + wt.b * a.o_sb + row.t * a.o_ss + row.h * a.o_sh + SL * hf + 8 * g;
 #pragma unroll
         for (int ds = 0; ds < SDS; ++ds) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (row.ok) v = *(const u32x4 *)(gp + 16 * ds);
             gf[ds] = to_bf16x8(v);
         }
+        bwide::to_agprs(qf, qa);
+        bwide::to_agprs(gf, ga);
     }
-    bf16x8 qa[SDS], ga[SDS];
-    to_agprs(qf, qa);
-    to_agprs(gf, ga);
     float nl = -kPosInf, nd = 0.f;  // -lse2 and -D of the row (rows past Lq: P = 0)
     if (row.ok) {
         const int64_t idx = (((int64_t)wt.b * a.Hq + row.h) * a.Lq + row.t) * 2;
@@ -907,16 +923,26 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
             constexpr int U = decltype(u)::value;
             if (it + 1 < ntiles) issue(ic<(U + 1) % 2>{}, it + 1);
             const int64_t k0 = kbeg + (int64_t)it * 32;
-            // (the same rows in every wave: the tests and the barrier below are uniform)
-            if (!keys_unseen(a, ch.start, k0, 32, wv_tlo, wv_thi)) {
+            if (!keys_unseen(a, ch.start, k0, 32, wg_tlo, wg_thi)) {
                 const char *kt = kst(u), *vt = vst(u);
                 f32x16 s[1], dp;
-                partial_scores([&](int n) { return kfrag<C>(n % 2 ? vt : kt, kaddr, SDS * w + n / 2, 0); }, qa, ga,
-                               s[0], dp);
-                exchange_put(xch, w, lane, s[0], dp);
+                bwide::partial_scores([&](int n) { return kfrag<C>(n % 2 ? vt : kt, kaddr, SDS * hf + n / 2, 0); },
+                                      qa, ga, s[0], dp);
+                bwide::exchange_put(xch, w, lane, s[0], dp);
                 tile_barrier();
-                exchange_sum(xch, lane, s[0], dp);
-                if (!keys_all_seen(a, ch.start, k0, 32, kend, wv_tlo, wv_thi))
+                // the sums of the row block's two halves, half 0 first (the same bits in both waves)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(xch + ((2 * r) * 4 + j) * 1024 + 16 * lane);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(xch + ((2 * r + 1) * 4 + j) * 1024 + 16 * lane);
+                    const f32x4 a1 =
+                        *reinterpret_cast<const f32x4 *>(xch + ((2 * (r + 2)) * 4 + j) * 1024 + 16 * lane);
+                    const f32x4 b1 =
+                        *reinterpret_cast<const f32x4 *>(xch + ((2 * (r + 2) + 1) * 4 + j) * 1024 + 16 * lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[0][4 * j + e] = a0[e] + a1[e], dp[4 * j + e] = b0[e] + b1[e];
+                }
+                if (!keys_all_seen(a, ch.start, k0, 32, kend, wg_tlo, wg_thi))
                     mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
                 // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
                 bf16x8 pf[2];
@@ -935,7 +961,7 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int j = 0; j < SDB; ++j) acc[j] = mfma(vfrag<C>(kt, vaddr, ks, SDB * w + j), pf[ks], acc[j]);
+                    for (int j = 0; j < SDB; ++j) acc[j] = mfma(vfrag<C>(kt, vaddr, ks, SDB * hf + j), pf[ks], acc[j]);
             }
             // the next tile is in place; this stage and the partials are free
             if (it + 1 < ntiles) wait_for(it + 1, it + 1);
@@ -944,16 +970,9 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
     }
 
     if (!row.ok) return;
-    // element i of block j in lane l is d = 128w + 32j + 8(i/4) + 4g + i%4; with
+    // element i of block j in lane l is d = 256h + 32j + 8(i/4) + 4g + i%4; with
     // ACCUMULATE every old value is loaded before any store
-    float *dq = A.dq + row.srow * 512 + SL * w + 4 * g;
-    f32x4 old[SDB][4];
-    if (A.accumulate) {
-#pragma unroll
-        for (int j = 0; j < SDB; ++j)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) old[j][i4] = *(const f32x4 *)(dq + 32 * j + 8 * i4);
-    }
+    float *dq = A.dq + row.srow * 512 + SL * hf + 4 * g;
 #pragma unroll
     for (int j = 0; j < SDB; ++j)
 #pragma unroll
@@ -961,7 +980,7 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = A.scale * acc[j][4 * i4 + e];
-            if (A.accumulate) v += old[j][i4];
+            if (A.accumulate) v += *(const f32x4 *)(dq + 32 * j + 8 * i4);
             *(f32x4 *)(dq + 32 * j + 8 * i4) = v;
         }
 }
@@ -1089,8 +1108,8 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
             const char *qt = kst(u), *gt = vst(u);
             // partial S = Q K^T and dP = dO V^T over the wave's dimensions: rows on M, keys on N
             f32x16 s, dp;
-            partial_scores([&](int n) { return kfrag<C>(n % 2 ? gt : qt, kaddr, SDS * w + n / 2, 0); }, ka, va, s,
-                           dp);
+            partial_scores<SDS>([&](int n) { return kfrag<C>(n % 2 ? gt : qt, kaddr, SDS * w + n / 2, 0); }, ka, va,
+                                s, dp);
             exchange_put(xch, w, lane, s, dp);
             tile_barrier();
             exchange_sum(xch, lane, s, dp);
@@ -1185,7 +1204,7 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
 
 }  // namespace
 
-int bwd_dq_row_tile(int d) { return d == 512 ? bwide::C::BM : 128; }
+int bwd_dq_row_tile(int d) { return d == 512 ? bwq::C::BM : 128; }
 
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, hipStream_t s) {
     const int64_t rows = (int64_t)a.f.B * a.f.Lq * a.f.Hq;
