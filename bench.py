@@ -79,7 +79,8 @@ MEASURED_TRAFFIC = {
 HEADLINE = "ring_1m_gqa32x8_d128"
 SECONDARY = ("prefill_bf16_h32_d128,mla_h16_d512,decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,"
              "tiny_ring_fp32,bwd:prefill_bf16_h32_d128,inplace:prefill_bf16_h32_d128,inplace:ring_1m_gqa32x8_d128,"
-             "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128,bwd:mla_h16_d512")
+             "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128,bwd:mla_h16_d512,"
+             "decode_b4_gqa32x8_cache1m_bhsd,decode_b4_gqa32x8_cache1m_fp8_bhsd")
 
 
 def visible_pairs_per_head(wl, rows=None):
@@ -352,6 +353,8 @@ class WorkloadRun:
             metric, value, unit = "decode HBM GB/s at 1M KV", gbs, "GB/s"
             if wl.kv_dtype == "fp8":
                 metric = "decode HBM GB/s at 1M KV (8-bit KV cache)"
+            if wl.kv_heads_major:
+                metric = metric.replace("at 1M KV", "at 1M KV, head-major cache")
         elif wl.dtype == "fp32":
             # a latency-bound 16-workgroup launch on the fp32 vector ALUs
             achieved = self.flops / self.launches / launch_s / 1e12
@@ -498,6 +501,8 @@ DOMINANT = {
     "inplace:mla_h16_d512": (("fwd_bf16_wide_kernel",), "mfma"),
     "decode_b4_gqa32x8_cache1m": (("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>",), "hbm"),
     "decode_b4_gqa32x8_cache1m_fp8": (("fwd_fp8kv_kernel",), "hbm"),
+    "decode_b4_gqa32x8_cache1m_bhsd": (("fwd_bf16_kernel<128, 64, 4, 2, 2, 0>",), "hbm"),
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": (("fwd_fp8kv_kernel",), "hbm"),
     "bwd:prefill_bf16_h32_d128": (("bwd_",), "mfma"),
     "bwd:mla_h16_d512": (("bwd_",), "mfma"),
 }

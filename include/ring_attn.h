@@ -46,7 +46,11 @@
  * the other three strides are given in ELEMENTS per tensor (all-zero strides
  * mean dense BSHD).  bf16 tensors need 16-byte aligned base pointers and
  * strides that are multiples of 8 elements; fp32 tensors need 16-byte
- * aligned pointers and strides that are multiples of 4 elements.
+ * aligned pointers and strides that are multiples of 4 elements.  The token
+ * strides of k and v must be below 2^24 elements (a key tile is addressed
+ * with 32-bit offsets); any other order of the three strides works, e.g. a
+ * head-major KV cache [B, H, S, d] passed as BSHD with strides
+ * (H*S*d, d, S*d).
  * Softmax state buffers are dense fp32: m and l are [B, Lq, Hq], O is
  * [B, Lq, Hq, d_v]; m is in natural-log units of the scaled logits, l is
  * sum(exp(s - m)) and O is sum(exp(s - m) * v), so out = O / l and the

@@ -29,6 +29,9 @@ Workloads (one device's share of the ring, shapes from the pages' settings):
 * ``decode_b4_gqa32x8_cache1m_fp8``: the same decode with the KV cache held
   in 8 bits (OCP FP8 E4M3, one power-of-two scale per 64 tokens of a
   (batch, KV head)); queries stay bf16.
+* ``decode_b4_gqa32x8_cache1m_bhsd``, ``decode_b4_gqa32x8_cache1m_fp8_bhsd``:
+  the same two decodes with the cache stored head-major (the same values;
+  memory order [B, Hkv, len, d], passed as BSHD with strides).
 
 8-bit KV caches are drawn like the others and then quantised block by block
 (input preparation, not the method): each block of 64 tokens x d values of
@@ -70,6 +73,7 @@ class Workload:
     window: int = 0     # local window half-width in tokens (0: none)
     anchor: int = 0     # anchor stride in tokens (0: none)
     doc_mean: int = 0   # packed documents of this mean length carry segment labels (0: none)
+    kv_heads_major: bool = False  # K/V stored head-major ([B, Hkv, len, d] memory, BSHD strides)
 
     @property
     def torch_dtype(self):
@@ -123,6 +127,11 @@ WORKLOADS = {
                                               q_offset=1048560, causal=True, std=0.5,
                                               seed=5, kv_dtype="fp8"),
 }
+# the two decode caches stored head-major ([B, Hkv, len, d] in memory): each
+# (sequence, KV head) reads one contiguous range instead of 128- or 256-byte
+# rows at the stride of all heads
+for _n in ("decode_b4_gqa32x8_cache1m", "decode_b4_gqa32x8_cache1m_fp8"):
+    WORKLOADS[_n + "_bhsd"] = replace(WORKLOADS[_n], name=_n + "_bhsd", kv_heads_major=True)
 
 KV_SCALE_BLOCK = 64  # tokens per shared exponent of an 8-bit KV cache
 FP8_MAX = 448.0      # largest finite OCP FP8 E4M3 value
@@ -231,6 +240,9 @@ def make(wl: Workload, device="cpu", q_std: Optional[float] = None) -> Inputs:
             v, ve = quantize_fp8(v)
             kes.append(ke)
             ves.append(ve)
+        if wl.kv_heads_major:  # the same values, each head's tokens contiguous
+            k = k.transpose(1, 2).contiguous().transpose(1, 2)
+            v = v.transpose(1, 2).contiguous().transpose(1, 2)
         ks.append(k)
         vs.append(v)
     return Inputs(wl, q, ks, vs, wl.starts(), kes, ves)

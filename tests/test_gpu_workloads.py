@@ -35,6 +35,8 @@ CASES = {
     "docs4096_h32_d128": (128, list(range(32)), None),
     "decode_b4_gqa32x8_cache1m": (1, [0, 3, 7], [0, 1, 3]),
     "decode_b4_gqa32x8_cache1m_fp8": (1, [0, 3, 7], [0, 1, 3]),
+    "decode_b4_gqa32x8_cache1m_bhsd": (1, [1, 6], [0, 2]),
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": (1, [1, 6], [0, 2]),
 }
 
 
