@@ -259,6 +259,18 @@ def test_fp8_kv_validation(lib):
     assert _ws(lib, st, 4, fp8_chunks([64]), 1, 0, 0, 0, 1)[0] == 0
 
 
+def test_kv_stride_limits(lib):
+    """Only the k/v token stride is limited (a key tile is addressed with
+    32-bit offsets): a head-major cache of 2^24 elements per sequence passes,
+    a token stride of 2^24 does not."""
+    d = _desc(B=2, Hq=4, Hkv=2, d=128)
+    arr = _chunks([1 << 16])
+    d.k_strides[:] = d.v_strides[:] = (2 * (1 << 16) * 128, 128, (1 << 16) * 128)  # batch stride 2^24
+    assert _ws(lib, d, 16, arr, 1, 1, (1 << 16) - 16, 0, 1)[0] == 0
+    d.k_strides[:] = (2 * (1 << 24), 1 << 24, 128)
+    assert _ws(lib, d, 16, arr, 1, 1, (1 << 16) - 16, 0, 1)[0] == rb.RA_ERR_UNSUPPORTED
+
+
 def test_bwd_workspace_and_validation(lib):
     """Backward: workspace = the rows' (lse, D) pairs; what is not built is
     rejected; bad arguments are rejected before anything touches the device
