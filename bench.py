@@ -67,13 +67,15 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "d69b39232e9cccb3",
-    "ring_1m_gqa32x8_d128": 3521316897,
-    "prefill_bf16_h32_d128": 599797635,
-    "mla_h16_d512": 4262798649,
-    "decode_b4_gqa32x8_cache1m": 17250133889,
-    "decode_b4_gqa32x8_cache1m_fp8": 8661385684,
-    "bwd:prefill_bf16_h32_d128": 7906782487,
+    "digest": "a21bed424096e64b",
+    "ring_1m_gqa32x8_d128": 3521724843,
+    "prefill_bf16_h32_d128": 591587833,
+    "mla_h16_d512": 4264079734,
+    "decode_b4_gqa32x8_cache1m": 17250218622,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661358398,
+    "bwd:prefill_bf16_h32_d128": 7718205095,
+    "bwd:mla_h16_d512": 103890225166,
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661562872,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
