@@ -80,6 +80,7 @@ CASES = [
     (1, 512, 2, 1, (64, 33), 65, 0, True, 0),             # diagonal at position 0, 1-row tails
     (1, 512, 16, 1, (64, 64), 40, 90, True, 30),          # GQA 16, causal window
     (2, 512, 2, 2, (70,), 50, 10, False, 0),              # non-causal, two sequences
+    (1, 512, 2, 2, (77, 50), 200, 0, False, 40),          # two-sided window; rows past every key see none
 ]
 
 
@@ -91,13 +92,14 @@ def test_bwd_matches_oracle(B, d, Hq, Hkv, lens, Lq, q_off, causal, window):
              order)
 
 
-def test_bwd_accumulate_chunkwise_and_deterministic():
+@pytest.mark.parametrize("d", [128, 512])
+def test_bwd_accumulate_chunkwise_and_deterministic(d):
     """Per-chunk calls adding into dq equal the all-chunk call; ACCUMULATE on
     the same inputs doubles every gradient (exactly for dK/dV, which one
     launch per chunk writes; dq of chunks of different lengths is summed
     over several launches, so its additions round in another order);
     repeated calls are bitwise equal."""
-    x = inputs.make(_wl(lens=(256, 192, 256), Lq=256, q_offset=448, causal=True), DEV)
+    x = inputs.make(_wl(d=d, lens=(256, 192, 256), Lq=256, q_offset=448, causal=True), DEV)
     chunks = x.chunks()
     out, st = forward(x, True, 448, 0)
     dout = inputs.output_grad(x.wl, DEV)
