@@ -70,6 +70,9 @@
 #endif
 // keep the bias block live across tiles (a splat the compiler would rebuild
 // with 15 moves per tile)
+#ifndef RA_TUNE_KEEPREF
+#define RA_TUNE_KEEPREF 1
+#endif
 #ifndef RA_TUNE_BIASPIN
 #define RA_TUNE_BIASPIN 1
 #endif
@@ -282,9 +285,11 @@ __device__ inline void load_q_scaled(const FwdArgs &a, const WorkTile &wt, const
     scale_q(qf, c);
 }
 
-// Starting state for biased scores: the reference is 0 unless a loaded
-// state's maximum lies outside [-kRefFloor, threshold] (log2 units); a
-// loaded O and l are rescaled to the reference.
+// Starting state for biased scores: a loaded state keeps its maximum as the
+// reference, so O is first read by the first P V product, which hides its
+// load behind the first tile's scores (RA_TUNE_KEEPREF 0: the reference is 0
+// unless the loaded maximum lies outside [-kRefFloor, threshold] (log2
+// units), and a loaded O and l are rescaled to it).  No state: reference 0.
 template <int DV, int NDB>
 __device__ inline void load_state_biased(const FwdArgs &a, const LaneRow &r, int g, bool owner, int dv0,
                                          f32x16 (&o)[NDB], float &m_run, float &m_true, float &lsum) {
@@ -293,7 +298,9 @@ __device__ inline void load_state_biased(const FwdArgs &a, const LaneRow &r, int
         m_run = 0.f;
         return;
     }
-    if (m_true < -kRefFloor || m_true > kRescaleThreshold) return;  // keep the loaded maximum as reference
+    // keep the loaded maximum as reference (always with RA_TUNE_KEEPREF: O is
+    // then first touched by the first P V product, which hides its load)
+    if (RA_TUNE_KEEPREF || m_true < -kRefFloor || m_true > kRescaleThreshold) return;
     const float alpha = exp2_fast(m_true);
     m_run = 0.f;
     lsum *= alpha;
