@@ -507,6 +507,8 @@ DOMINANT = {
     "decode_b4_gqa32x8_cache1m_fp8_bhsd": (("fwd_fp8kv_kernel",), "hbm"),
     "bwd:prefill_bf16_h32_d128": (("bwd_",), "mfma"),
     "bwd:mla_h16_d512": (("bwd_",), "mfma"),
+    "local_w4096_s4096_h32_d128": (("fwd_bf16_kernel<128, 64, 4, 1, 2, 1>",), "mfma"),
+    "docs4096_h32_d128": (("fwd_bf16_kernel<128, 64, 4, 1, 2, 2>",), "mfma"),
 }
 
 
