@@ -250,10 +250,10 @@ void bwd_dq_kernel(const BwdArgs A) {
                     }
                 accumulate_pv<C>(kst(u), vaddr, pf, acc);
             }
-            if (it + 1 < ntiles) {
-                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-                wait_for(it + 1, last);
-            }
+            // (also after the last tile: every path round the loop then leaves no
+            // load in flight, which lets the compiler see that the next tile's
+            // reads need not wait for the loads issued before them)
+            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
         });
     }
 
@@ -583,8 +583,8 @@ void bwd_dkdv_kernel(const BwdArgs A) {
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f32x4 x = *(const f32x4 *)(lt + 256 * rb + 32 * j + 16 * g);
-                    const f32x4 y = *(const f32x4 *)(lt + 256 * rb + 128 + 32 * j + 16 * g);
+                    const f32x4 x = __builtin_bit_cast(f32x4, lds_read_b128(lt, 256 * rb + 32 * j + 16 * g));
+                    const f32x4 y = __builtin_bit_cast(f32x4, lds_read_b128(lt, 256 * rb + 128 + 32 * j + 16 * g));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[rb][4 * j + e] = x[e], dp[rb][4 * j + e] = y[e];
                 }
@@ -706,10 +706,10 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (it + 1 < ntiles) {
-            const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-            wait_for(it + 1, last);
-        }
+        // (also after the last tile: every path round the loop then leaves no
+        // load in flight, which lets the compiler see that the next tile's
+        // reads need not wait for the loads issued before them)
+        wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
     });
 
     if (!key_ok) return;

@@ -797,13 +797,25 @@ __device__ inline void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_
 
 // Wait until at most `tiles` tiles' loads (LPT load instructions each) of
 // this wave are still in flight, then synchronise the workgroup.
+// The wait is the s_waitcnt builtin rather than asm: the compiler's own wait
+// insertion then knows which loads have landed, and does not add a wait for
+// every load in flight (the next tile's prefetch included) before the first
+// LDS read after a loop back edge.
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+    // gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
 template <int LPT>
 __device__ inline void wait_tiles_in_flight(int tiles) {
     switch (tiles) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory"); break;
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LPT>(); break;
+    case 2: wait_vmcnt<2 * LPT>(); break;
+    default: wait_vmcnt<3 * LPT>(); break;
     }
     tile_barrier();
 }
