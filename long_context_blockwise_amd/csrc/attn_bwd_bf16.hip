@@ -250,10 +250,10 @@ void bwd_dq_kernel(const BwdArgs A) {
                     }
                 accumulate_pv<C>(kst(u), vaddr, pf, acc);
             }
-            // (also after the last tile: every path round the loop then leaves no
-            // load in flight, which lets the compiler see that the next tile's
-            // reads need not wait for the loads issued before them)
-            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
         });
     }
 
@@ -510,21 +510,26 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     v_addrs<C>(0, lane, vaddr);
     const int64_t kpos = ch.start + key;
 
-    auto tile_of = [&](int it, int &h, int64_t &t0) {
-        if constexpr (EXT) {
-            const int gq = it / nseg, j = it % nseg;
-            h = hk * a.G + gq;
-            t0 = j < n1 ? t_lo + RT * (int64_t)j : s2 + RT * (int64_t)(j - n1);
-        } else {
-            const int gq = it / n1;
-            h = hk * a.G + gq;
-            t0 = t_lo + RT * (int64_t)(it % n1);
-        }
+    // tile -> (query head, first row): the group's heads outer, the row
+    // segments inner.  Two cursors walk the tiles, one for the tile computed
+    // and one for the tile loaded NS-1 ahead, so no tile needs a division.
+    struct Cursor {
+        int gq, j;
     };
-    auto issue = [&](auto u, int it) {
+    auto tile_at = [&](const Cursor &c, int &h, int64_t &t0) {
+        h = hk * a.G + c.gq;
+        if constexpr (EXT) t0 = c.j < n1 ? t_lo + RT * (int64_t)c.j : s2 + RT * (int64_t)(c.j - n1);
+        else t0 = t_lo + RT * (int64_t)c.j;
+    };
+    auto advance = [&](Cursor &c) {
+        if (++c.j == nseg) c.j = 0, ++c.gq;
+    };
+    Cursor cur{0, 0}, nxt{0, 0};
+    auto issue = [&](auto u) {
         int h;
         int64_t t0;
-        tile_of(it, h, t0);
+        tile_at(nxt, h, t0);
+        advance(nxt);
         const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
         const uint16_t *gb = (const uint16_t *)A.dout + b * a.o_sb + h * a.o_sh;
         load_tile<C>(qb, a.q_ss, t0, a.Lq, qtile(u), w, lane);
@@ -550,14 +555,15 @@ void bwd_dkdv_kernel(const BwdArgs A) {
     };
 
     const int pre = ntiles < NS - 1 ? ntiles : NS - 1;
-    for_tiles<NS>(pre, [&](auto u, int t) { issue(u, t); });
+    for_tiles<NS>(pre, [&](auto u, int) { issue(u); });
     wait_for(0, pre - 1);
     for_tiles<NS>(ntiles, [&](auto u, int it) {
         constexpr int U = decltype(u)::value;
-        if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{}, it + NS - 1);
+        if (it + NS - 1 < ntiles) issue(ic<(U + NS - 1) % NS>{});
         int h;
         int64_t t0;
-        tile_of(it, h, t0);
+        tile_at(cur, h, t0);
+        advance(cur);
         const int64_t thi = t0 + RT - 1 < a.Lq - 1 ? t0 + RT - 1 : a.Lq - 1;
         bool skip = wk0 >= len || keys_unseen(a, ch.start, wk0, 32, t0, thi);
         bool full = t0 + RT - 1 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi);
@@ -706,10 +712,10 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // (also after the last tile: every path round the loop then leaves no
-        // load in flight, which lets the compiler see that the next tile's
-        // reads need not wait for the loads issued before them)
-        wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
+        if (it + 1 < ntiles) {
+            const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+            wait_for(it + 1, last);
+        }
     });
 
     if (!key_ok) return;

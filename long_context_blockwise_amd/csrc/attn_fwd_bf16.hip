@@ -660,10 +660,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
                     }
                 }
             }
-            // (also after the last tile: every path round the loop then leaves no
-            // load in flight, which lets the compiler see that the next tile's
-            // reads need not wait for the loads issued before them)
-            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
         });
     }
 
@@ -1156,10 +1156,10 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
                         oacc[db] = mfma(widen(raw, vs), pf[kss], oacc[db]);
                     }
             }
-            // (also after the last tile: every path round the loop then leaves no
-            // load in flight, which lets the compiler see that the next tile's
-            // reads need not wait for the loads issued before them)
-            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
+            if (it + 1 < ntiles) {
+                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
+                wait_for(it + 1, last);
+            }
         });
     }
 
