@@ -250,10 +250,10 @@ void bwd_dq_kernel(const BwdArgs A) {
                     }
                 accumulate_pv<C>(kst(u), vaddr, pf, acc);
             }
-            if (it + 1 < ntiles) {
-                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-                wait_for(it + 1, last);
-            }
+            // (after the last tile too, where nothing is in flight: every path
+            // round the loop then ends with a wait the compiler can see, and it
+            // adds no wait for the next tile's loads before this tile's reads)
+            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
         });
     }
 
@@ -712,10 +712,10 @@ void bwd_dkdv_kernel(const BwdArgs A) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (it + 1 < ntiles) {
-            const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-            wait_for(it + 1, last);
-        }
+        // (after the last tile too, where nothing is in flight: every path
+        // round the loop then ends with a wait the compiler can see, and it
+        // adds no wait for the next tile's loads before this tile's reads)
+        wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
     });
 
     if (!key_ok) return;
@@ -970,8 +970,9 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
                     for (int j = 0; j < SDB; ++j) acc[j] = mfma(vfrag<C>(kt, vaddr, ks, SDB * hf + j), pf[ks], acc[j]);
             }
             // the next tile is in place; this stage and the partials are free
-            if (it + 1 < ntiles) wait_for(it + 1, it + 1);
-            else tile_barrier();
+            // (after the last tile too, where nothing is in flight: every path
+            // round the loop then ends with a wait the compiler can see)
+            wait_for(it + 1, it + 1);
         });
     }
 
@@ -1170,8 +1171,9 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
                 }
         }
         // the next tile is in place; this stage and the partials are free
-        if (it + 1 < ntiles) wait_for(it + 1, it + 1);
-        else tile_barrier();
+        // (after the last tile too, where nothing is in flight: every path
+        // round the loop then ends with a wait the compiler can see)
+        wait_for(it + 1, it + 1);
     });
 
     if (!key_ok) return;

@@ -660,10 +660,10 @@ void fwd_bf16_kernel(const FwdArgs a) {
                     }
                 }
             }
-            if (it + 1 < ntiles) {
-                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-                wait_for(it + 1, last);
-            }
+            // (after the last tile too, where nothing is in flight: every path
+            // round the loop then ends with a wait the compiler can see, and it
+            // adds no wait for the next tile's loads before this tile's reads)
+            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
         });
     }
 
@@ -1156,10 +1156,10 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
                         oacc[db] = mfma(widen(raw, vs), pf[kss], oacc[db]);
                     }
             }
-            if (it + 1 < ntiles) {
-                const int last = it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1;
-                wait_for(it + 1, last);
-            }
+            // (after the last tile too, where nothing is in flight: every path
+            // round the loop then ends with a wait the compiler can see, and it
+            // adds no wait for the next tile's loads before this tile's reads)
+            wait_for(it + 1, it + NS - 1 < ntiles ? it + NS - 1 : ntiles - 1);
         });
     }
 
