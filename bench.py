@@ -67,15 +67,18 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "a21bed424096e64b",
-    "ring_1m_gqa32x8_d128": 3521724843,
-    "prefill_bf16_h32_d128": 591587833,
-    "mla_h16_d512": 4264079734,
-    "decode_b4_gqa32x8_cache1m": 17250218622,
-    "decode_b4_gqa32x8_cache1m_fp8": 8661358398,
-    "bwd:prefill_bf16_h32_d128": 7718205095,
-    "bwd:mla_h16_d512": 103890225166,
-    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661562872,
+    "digest": "4bc7078947482471",
+    "ring_1m_gqa32x8_d128": 3518228644,
+    "prefill_bf16_h32_d128": 597125977,
+    "mla_h16_d512": 4261983591,
+    "decode_b4_gqa32x8_cache1m": 17249843572,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661259940,
+    "decode_b4_gqa32x8_cache1m_bhsd": 17250037549,
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661455867,
+    "local_w4096_s4096_h32_d128": 951516396,
+    "docs4096_h32_d128": 190456000,
+    "bwd:prefill_bf16_h32_d128": 10649250326,
+    "bwd:mla_h16_d512": 105461362777,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
@@ -689,6 +692,22 @@ def write_profile_summary(name, runs, calib, outdir, steps):
                   f"kernel trace: `copyBuffer` intervals against `{pattern}` intervals |",
                   f"| staging copy time / attention kernel time | {fmt(100 * copy_ns / max(sum(durs), 1), 4)} % | "
                   "both from the kernel trace (copies run on the side stream) |"]
+    # the bench's own HIP-event timing of the traced command (its JSON line),
+    # the figure the bench line reports, for comparison with the trace
+    ev = None
+    try:
+        with open(os.path.join(runs["trace"][0], "rocprof.log")) as f:
+            out = f.read().split("---- stderr ----")[0]
+        js = [json.loads(l) for l in out.splitlines() if l.startswith("{")]
+        ev = js[-1].get("roofline", {}).get("achieved") if js else None
+    except (OSError, ValueError):
+        ev = None
+    if ev:
+        ev_ns = (alg_flops_launch / ev * 1e-3) if bound == "mfma" else (alg_bytes_launch / ev)
+        unit = "TFLOP/s" if bound == "mfma" else "GB/s"
+        what = "step" if name.startswith("bwd:") else "launch"
+        lines += [f"| bench events in the traced command | {fmt(ev_ns / 1e3, 5)} µs per {what} ({fmt(ev, 5)} {unit}) | "
+                  "HIP events on the launch stream around the timed steps of the trace run (its JSON line) |"]
     if bound == "mfma":
         lines += [f"| **achieved (algorithmic)** | **{fmt(achieved_tflops, 5)} TFLOP/s = "
                   f"{fmt(100 * achieved_tflops / PEAK_BF16_TFLOPS, 4)} % of {PEAK_BF16_TFLOPS}** | "
