@@ -67,7 +67,7 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "4bc7078947482471",
+    "digest": "a288f02d65105c5e",
     "ring_1m_gqa32x8_d128": 3518228644,
     "prefill_bf16_h32_d128": 597125977,
     "mla_h16_d512": 4261983591,

@@ -795,9 +795,7 @@ using ic = std::integral_constant<int, N>;
 // serialise the prefetch); their completion is waited for explicitly.
 __device__ inline void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Wait until at most `tiles` tiles' loads (LPT load instructions each) of
-// this wave are still in flight, then synchronise the workgroup.
-// The wait is the s_waitcnt builtin rather than asm: the compiler's own wait
+// s_waitcnt vmcnt(N) as the builtin rather than asm: the compiler's own wait
 // insertion then knows which loads have landed, and does not add a wait for
 // every load in flight (the next tile's prefetch included) before the first
 // LDS read after a loop back edge.
@@ -809,6 +807,8 @@ __device__ inline void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
+// Wait until at most `tiles` tiles' loads (LPT load instructions each) of
+// this wave are still in flight, then synchronise the workgroup.
 template <int LPT>
 __device__ inline void wait_tiles_in_flight(int tiles) {
     switch (tiles) {
