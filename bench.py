@@ -746,7 +746,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one device's ring share on one GPU; --gpus must be 1 "
-              "(the multi-GPU ring is not part of this build)", file=sys.stderr)
+              "(the ring across GPUs is not implemented: each device's share runs on one GPU)", file=sys.stderr)
         sys.exit(2)
     if args.profile:  # the parent only starts rocprofv3 runs; it never touches the GPU itself
         profile([s for s in args.profile.split(",") if s], args.profile_out, args.profile_steps)
