@@ -308,9 +308,12 @@ constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
 // Q and dO tiles are read ahead.  As inline asm the results stay in VGPRs,
 // where the vector work reads them, and the resident K and V fragments in
 // AGPRs (the builtin would put every accumulator of this kernel in AGPRs and
-// copy the scores out); the s_nops after the last MFMA cover the wait states
-// before a vector instruction may touch a result, which the compiler does not
-// see inside asm.
+// copy the scores out).  The compiler does not see an MFMA inside asm, so it
+// inserts none of the wait states around one: the s_nop in front of each MFMA
+// gives the 2 that a vector write of a source register needs before the matrix
+// core reads it (the compiler may copy a K or V fragment into its AGPRs just
+// before), and the s_nops after the last one those before a vector
+// instruction may touch a result.
 template <class C, int RB>
 __device__ inline void kv_scores(const char *qt, const char *gt, const int (&kaddr)[C::NKA],
                                  const bf16x8 (&kf)[C::DS], const bf16x8 (&vf)[C::DS], f32x16 (&s)[RB],
@@ -326,9 +329,9 @@ __device__ inline void kv_scores(const char *qt, const char *gt, const int (&kad
         const int ds = n / (2 * RB), rb = (n / 2) % RB;
         if constexpr (RA_TUNE_KV_ASM) {
             if (n & 1)
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp[rb]) : "v"(fr[n % PF]), "a"(vf[ds]));
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp[rb]) : "v"(fr[n % PF]), "a"(vf[ds]));
             else
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s[rb]) : "v"(fr[n % PF]), "a"(kf[ds]));
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s[rb]) : "v"(fr[n % PF]), "a"(kf[ds]));
         } else {
             if (n & 1) dp[rb] = mfma(fr[n % PF], vf[ds], dp[rb]);
             else s[rb] = mfma(fr[n % PF], kf[ds], s[rb]);
@@ -806,8 +809,10 @@ __device__ inline void exchange_sum(const char *x, int lane, f32x16 &s, f32x16 &
 // Partial S (A fragments from tile a) and dP (from tile b) over the wave's
 // SDS reduction steps, the B operands of step ds in AGPRs (bs[ds], bd[ds]):
 // inline-asm MFMAs whose results stay in VGPRs, where the exchange and the
-// vector work read them (the builtin's AGPR form would copy them out); the
-// s_nops cover the wait states before a vector instruction may read them.
+// vector work read them (the builtin's AGPR form would copy them out).  The
+// s_nop in front of each MFMA covers a vector write of a source register just
+// before it, the s_nops after the last one the wait states before a vector
+// instruction may read the results: the compiler sees neither inside asm.
 template <int NS, class KF>
 __device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[NS], const bf16x8 (&bd)[NS], f32x16 &s,
                                       f32x16 &dp) {
@@ -819,13 +824,13 @@ __device__ inline void partial_scores(KF &&frag, const bf16x8 (&bs)[NS], const b
     for (int n = 0; n < 2 * NS; ++n) {
         const int ds = n / 2;
         if (n == 0)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "a"(bs[0]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "a"(bs[0]));
         else if (n == 1)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(dp) : "v"(fr[1]), "a"(bd[0]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(dp) : "v"(fr[1]), "a"(bd[0]));
         else if (n % 2 == 0)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "a"(bs[ds]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "a"(bs[ds]));
         else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp) : "v"(fr[n % PF]), "a"(bd[ds]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dp) : "v"(fr[n % PF]), "a"(bd[ds]));
         if (n + PF < 2 * NS) fr[n % PF] = frag(n + PF);
         if (n % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
     }

@@ -740,9 +740,11 @@ static_assert(C::KB == 1, "one 32-key block per tile");
 // inline asm so that the scores stay out of the AGPRs, which O fills (the
 // builtin's accumulator takes the AGPR form in this kernel, and there are no
 // 16 AGPRs to spare).  Consecutive MFMAs accumulate into the same registers,
-// which the hardware chains back to back; the s_nops after the last one
-// cover the wait states before a VALU instruction may read the result,
-// which the compiler does not see inside asm.
+// which the hardware chains back to back.  The compiler sees no MFMA inside
+// asm and inserts no wait states for one: the s_nop in front of each covers a
+// vector write of a source register just before it (2 wait states), the
+// s_nops after the last one those before a VALU instruction may read the
+// result.
 __device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const bf16x8 (&qf)[C::DS], f32x16 &s) {
     constexpr int N = C::DS;
     constexpr int PF = C::PF;
@@ -752,11 +754,11 @@ __device__ inline void scores(const char *kt, const int (&kaddr)[C::NKA], const 
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         if (n == 0)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "v"(qf[0]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(fr[0]), "v"(qf[0]));
         else if (n < N - 1)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "v"(qf[n]));
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(fr[n % PF]), "v"(qf[n]));
         else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
                          : "+v"(s)
                          : "v"(fr[n % PF]), "v"(qf[n]));
         if (n + PF < N) fr[n % PF] = kfrag<C>(kt, kaddr, n + PF, 0);
