@@ -67,18 +67,18 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "a288f02d65105c5e",
-    "ring_1m_gqa32x8_d128": 3518228644,
-    "prefill_bf16_h32_d128": 597125977,
-    "mla_h16_d512": 4261983591,
-    "decode_b4_gqa32x8_cache1m": 17249843572,
-    "decode_b4_gqa32x8_cache1m_fp8": 8661259940,
-    "decode_b4_gqa32x8_cache1m_bhsd": 17250037549,
-    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661455867,
-    "local_w4096_s4096_h32_d128": 951516396,
-    "docs4096_h32_d128": 190456000,
-    "bwd:prefill_bf16_h32_d128": 10649250326,
-    "bwd:mla_h16_d512": 105461362777,
+    "digest": "bfd648ce0ce6cd53",
+    "ring_1m_gqa32x8_d128": 3518684359,
+    "prefill_bf16_h32_d128": 579572430,
+    "mla_h16_d512": 4261483261,
+    "decode_b4_gqa32x8_cache1m": 17250192331,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661256152,
+    "decode_b4_gqa32x8_cache1m_bhsd": 17250474765,
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661488849,
+    "local_w4096_s4096_h32_d128": 953045405,
+    "docs4096_h32_d128": 191152446,
+    "bwd:prefill_bf16_h32_d128": 10671112090,
+    "bwd:mla_h16_d512": 105669749448,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
