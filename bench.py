@@ -39,6 +39,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import shlex
 import statistics
@@ -82,6 +83,9 @@ MEASURED_TRAFFIC = {
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
+# minimum GPU time of each secondary workload's warmup and of its timed steps
+SECONDARY_WARMUP_S = 0.3
+SECONDARY_TIMED_S = 0.2
 SECONDARY = ("prefill_bf16_h32_d128,mla_h16_d512,decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,"
              "tiny_ring_fp32,bwd:prefill_bf16_h32_d128,inplace:prefill_bf16_h32_d128,inplace:ring_1m_gqa32x8_d128,"
              "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128,bwd:mla_h16_d512,"
@@ -315,6 +319,16 @@ class WorkloadRun:
     def step(self):
         self.ra.ring_attn_fwd(self.x.q, self.chunks, self.wl.causal, self.wl.q_offset,
                               flags=self.flags, out=self.out, ctx=self.ctx, workspace=self.ws, **self.masks)
+
+    def estimate_step_s(self):
+        """Wall time of one step after one untimed step (for sizing warmup)."""
+        torch = self.torch
+        self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.step()
+        torch.cuda.synchronize()
+        return max(time.perf_counter() - t0, 1e-5)
 
     def time(self, steps, warmup, during=None):
         """Mean wall time per step and the per-step HIP-event times (ms) on
@@ -790,8 +804,16 @@ def main():
     sec_steps = args.secondary_steps or max(3, args.steps // 2)
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         r = make_run(name)
-        s2, e2 = r.time(sec_steps, max(1, args.warmup))
+        # Short steps are warmed up and timed for a minimum span of GPU time:
+        # after the idle gap of setting a workload up, the board takes tens of
+        # milliseconds of load to reach its steady clocks, which a few steps
+        # of a millisecond or two do not cover.
+        est = r.estimate_step_s()
+        warm = max(1, args.warmup, math.ceil(SECONDARY_WARMUP_S / est))
+        steps2 = max(sec_steps, math.ceil(SECONDARY_TIMED_S / est))
+        s2, e2 = r.time(steps2, warm)
         res = r.result(s2, e2)
+        res["timed_steps"], res["warmup_steps"] = steps2, warm
         print(f"[bench] {res}", file=sys.stderr, flush=True)
         secondary.append(res)
         del r
