@@ -86,6 +86,8 @@ HEADLINE = "ring_1m_gqa32x8_d128"
 # minimum GPU time of each secondary workload's warmup and of its timed steps
 SECONDARY_WARMUP_S = 0.3
 SECONDARY_TIMED_S = 0.2
+# minimum GPU time of the warmup before the profiled (timed) steps
+PROFILE_WARMUP_S = 0.3
 SECONDARY = ("prefill_bf16_h32_d128,mla_h16_d512,decode_b4_gqa32x8_cache1m,decode_b4_gqa32x8_cache1m_fp8,"
              "tiny_ring_fp32,bwd:prefill_bf16_h32_d128,inplace:prefill_bf16_h32_d128,inplace:ring_1m_gqa32x8_d128,"
              "local_w4096_s4096_h32_d128,docs4096_h32_d128,bwd:docs4096_h32_d128,bwd:mla_h16_d512,"
@@ -554,20 +556,40 @@ def _csv_rows(d, suffix):
     return rows
 
 
-def _counters(d, pattern):
-    """{counter: [value per dispatch]} and the dispatch durations (ns) of the
-    kernels whose name contains `pattern`."""
+def _counters(d, pattern, last=None):
+    """{counter: [value per dispatch]} over the dispatches of the kernels whose
+    name contains `pattern` (only the `last` ones in dispatch order, when
+    given), and how many dispatches those are."""
     per = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         if pattern not in r.get("Kernel_Name", ""):
             continue
-        key = r["Dispatch_Id"]
+        key = int(r["Dispatch_Id"])
         per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    keys = sorted(per)
+    if last:
+        keys = keys[-last:]
     vals = {}
-    for disp in per.values():
-        for k, v in disp.items():
+    for key in keys:
+        for k, v in per[key].items():
             vals.setdefault(k, []).append(v)
-    return vals, len(per)
+    return vals, len(keys)
+
+
+def _child_line(d):
+    """The JSON line a profiled bench.py child printed (its stdout), or None."""
+    try:
+        with open(os.path.join(d, "rocprof.log")) as f:
+            out = f.read().split("---- stderr ----")[0]
+    except OSError:
+        return None
+    for line in reversed(out.splitlines()):
+        if line.startswith("{"):
+            try:
+                return json.loads(line)
+            except ValueError:
+                return None
+    return None
 
 
 def profile(names, outdir, steps):
@@ -586,7 +608,7 @@ def profile(names, outdir, steps):
     for name in names:
         base = name.split(":", 1)[-1]
         child = [me, "--workload", name, "--secondary", "", "--no-cpu", "--steps", str(steps), "--warmup", "1",
-                 "--no-clock"]
+                 "--warmup-s", str(PROFILE_WARMUP_S), "--no-clock"]
         tagb = name.replace(":", "_")
         runs = {}
         runs["trace"] = _rocprof_run(["--kernel-trace", "--stats"], outdir, tagb + "_trace", child, 900)
@@ -607,20 +629,29 @@ def write_profile_summary(name, runs, calib, outdir, steps):
     stats = _csv_rows(runs["trace"][0], "kernel_stats.csv")
     all_traces = _csv_rows(runs["trace"][0], "kernel_trace.csv")
     pattern = next((p for p in patterns if any(p in r.get("Kernel_Name", "") for r in all_traces)), patterns[0])
-    traces = [r for r in all_traces if pattern in r.get("Kernel_Name", "")]
+    traces = sorted((r for r in all_traces if pattern in r.get("Kernel_Name", "")),
+                    key=lambda r: int(r["Start_Timestamp"]))
+    # The traced command runs untimed steps (its warmup, sized to a minimum GPU
+    # time, and the step-time estimate) before the timed ones; its JSON line
+    # says how many.  Only the timed steps' dispatches are priced, in the trace
+    # and in each counter run.
+    child = _child_line(runs["trace"][0]) or {}
+    untimed = (child.get("run_info") or {}).get("untimed_steps", 1)
+    per_step = len(traces) / (steps + untimed) if traces else float("nan")
+    n_timed = max(1, round(steps * per_step)) if traces else 0
+    all_durs = len(traces)
+    traces = traces[-n_timed:] if traces else traces
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in traces]
     avg_ns = statistics.fmean(durs) if durs else float("nan")
-    pipes, n_disp = _counters(runs["pipes"][0], pattern)
-    lds, _ = _counters(runs["lds"][0], pattern)
-    fetch, _ = _counters(runs["fetch"][0], pattern)
-    write, _ = _counters(runs["write"][0], pattern)
+    pipes, n_disp = _counters(runs["pipes"][0], pattern, n_timed)
+    lds, _ = _counters(runs["lds"][0], pattern, n_timed)
+    fetch, _ = _counters(runs["fetch"][0], pattern, n_timed)
+    write, _ = _counters(runs["write"][0], pattern, n_timed)
     mean = lambda v: statistics.fmean(v) if v else float("nan")
     flops, kv_bytes = algorithmic(wl)
     if name.startswith("bwd:"):
         flops = visible_pairs(wl) * wl.Hq * 2 * (3 * wl.d_qk + 2 * wl.d_v)
-    # launches of the dominant kernel per step (the trace covers warmup + steps)
-    n_steps = steps + 1
-    per_step = len(durs) / n_steps if durs else float("nan")
+    n_steps = steps
     grbm = mean(pipes.get("GRBM_GUI_ACTIVE", [])) / N_XCD  # cycles (the counter sums the XCDs)
     clock_ghz = grbm / avg_ns if durs else float("nan")
     mfma_busy = mean(pipes.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (grbm * N_SIMD)
@@ -665,11 +696,11 @@ def write_profile_summary(name, runs, calib, outdir, steps):
         lines.append(f"| `{r.get('Name', '')[:110]}` | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
                      f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} |")
     fmt = lambda v, p=3: "n/a" if v != v else f"{v:.{p}g}" if abs(v) < 1e4 else f"{v:.4e}"
-    lines += ["", f"## Dominant kernel `{short}` (derived; {len(durs)} dispatches in the trace, "
-                  f"{n_disp} in each counter run)", "",
+    lines += ["", f"## Dominant kernel `{short}` (derived over the {len(durs)} dispatches of the {steps} timed "
+                  f"steps: the last of {all_durs} in the trace, and of each counter run)", "",
               "| Quantity | Value | How |", "|---|---|---|",
-              f"| average duration | {fmt(avg_ns / 1e3, 5)} µs | kernel trace, dispatches matching `{pattern}` |",
-              f"| launches per step | {fmt(per_step)} | dispatches / ({steps} timed + 1 warmup steps) |",
+              f"| average duration | {fmt(avg_ns / 1e3, 5)} µs | kernel trace, timed dispatches matching `{pattern}` |",
+              f"| launches per step | {fmt(per_step)} | dispatches / ({steps} timed + {untimed} untimed steps) |",
               f"| shader clock | {fmt(clock_ghz, 4)} GHz | GRBM_GUI_ACTIVE / {N_XCD} XCDs / average duration |",
               f"| MFMA busy | {fmt(100 * mfma_busy, 4)} % | SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/{N_XCD} x "
               f"{N_SIMD} SIMDs) |",
@@ -688,8 +719,9 @@ def write_profile_summary(name, runs, calib, outdir, steps):
               f"| algorithmic K/V+Q+out bytes per launch | {fmt(alg_bytes_launch)} | K+V once, Q, out |"]
     # the staging copies of the ring stand-in: their time and how much of it
     # overlaps the attention kernels (kernel-trace intervals)
+    t_timed = int(traces[0]["Start_Timestamp"]) if traces else 0
     copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in all_traces
-              if "copyBuffer" in r.get("Kernel_Name", "")]
+              if "copyBuffer" in r.get("Kernel_Name", "") and int(r["End_Timestamp"]) > t_timed]
     attn = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in traces)
     copy_ns = sum(e - b for b, e in copies)
     over_ns = 0
@@ -708,14 +740,7 @@ def write_profile_summary(name, runs, calib, outdir, steps):
                   "both from the kernel trace (copies run on the side stream) |"]
     # the bench's own HIP-event timing of the traced command (its JSON line),
     # the figure the bench line reports, for comparison with the trace
-    ev = None
-    try:
-        with open(os.path.join(runs["trace"][0], "rocprof.log")) as f:
-            out = f.read().split("---- stderr ----")[0]
-        js = [json.loads(l) for l in out.splitlines() if l.startswith("{")]
-        ev = js[-1].get("roofline", {}).get("achieved") if js else None
-    except (OSError, ValueError):
-        ev = None
+    ev = (child.get("roofline") or {}).get("achieved")
     if ev:
         ev_ns = (alg_flops_launch / ev * 1e-3) if bound == "mfma" else (alg_bytes_launch / ev)
         unit = "TFLOP/s" if bound == "mfma" else "GB/s"
@@ -749,6 +774,9 @@ def main():
     ap.add_argument("--secondary", default=SECONDARY, help="comma list, '' for none")
     ap.add_argument("--secondary-steps", type=int, default=0, help="timed steps of each secondary (default steps/2)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--warmup-s", type=float, default=0.0, metavar="SECONDS",
+                    help="warm the headline workload up for at least this much GPU time (more steps than "
+                         "--warmup when its steps are short; the profile runs use it)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the board clock")
     ap.add_argument("--profile", default="", metavar="NAMES",
                     help="run the rocprofv3 harness on these workloads (comma list) and write summaries")
@@ -787,8 +815,12 @@ def main():
         t0 = time.perf_counter()
         clock["sclk_mhz"] = sample_sclk_mhz()
         clock["t"] = (t0, time.perf_counter())
+    warm, est_steps = args.warmup, 0
+    if args.warmup_s > 0:
+        warm = max(warm, math.ceil(args.warmup_s / run.estimate_step_s()))
+        est_steps = 2  # the two untimed steps of the estimate
     t_start = time.perf_counter()
-    sec, ev_ms = run.time(args.steps, args.warmup, during=None if args.no_clock else sample)
+    sec, ev_ms = run.time(args.steps, warm, during=None if args.no_clock else sample)
     t_end = time.perf_counter()
     head = run.result(sec, ev_ms)
     print(f"[bench] {head}", file=sys.stderr, flush=True)
@@ -839,7 +871,7 @@ def main():
         "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -856,6 +888,7 @@ def main():
                      "cus": props.multi_processor_count, "sclk_mhz_sampled": clock.get("sclk_mhz"),
                      "sclk_sampled_during_timed_steps": clock_inside,
                      "sclk_max_mhz": 2400, "host_cpu": model, "host_affinity_cores": affinity,
+                     "untimed_steps": est_steps + warm,
                      "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                      "source_digest": source_digest(), "git_rev": git_revision()},
         "secondary": secondary,

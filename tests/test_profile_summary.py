@@ -95,8 +95,9 @@ def test_profile_summary_figures(tmp_path):
     assert out["achieved_tflops"] == pytest.approx(flops / LAUNCHES / avg_ns / 1e3)
     assert out["achieved_gbs"] == pytest.approx(kv_bytes / LAUNCHES / avg_ns)
     st = out["staging"]
-    assert st["copies"] == len(DUR_NS)
-    assert st["copy_ns"] == sum(d // 2 for d in DUR_NS)
+    timed = DUR_NS[-STEPS * LAUNCHES:]  # only the timed steps' launches (and their copies) are priced
+    assert st["copies"] == len(timed)
+    assert st["copy_ns"] == sum(d // 2 for d in timed)
     assert st["overlap_ns"] == st["copy_ns"]  # every copy lies inside its launch
     assert st["copy_frac_of_kernel_time"] == pytest.approx(0.5)
 
@@ -115,3 +116,26 @@ def test_profile_summary_without_event_line(tmp_path):
     text = open(out["file"]).read()
     assert "bench events in the traced command" not in text
     assert out["mfma_busy"] == pytest.approx(0.6)
+
+
+def test_profile_summary_prices_only_timed_steps(tmp_path):
+    """With the child's JSON line reporting 3 untimed steps (warmup and the
+    step estimate), the summary keeps only the last STEPS steps' dispatches:
+    here the untimed launches are made twice as long, and the average must
+    not see them."""
+    global DUR_NS
+    saved = DUR_NS
+    untimed = 3
+    DUR_NS = [2 * d for d in [1_000_000, 1_200_000, 800_000, 1_000_000]] * untimed + \
+        [1_000_000, 1_200_000, 800_000, 1_000_000] * STEPS
+    try:
+        line = json.dumps({"metric": "m", "run_info": {"untimed_steps": untimed}})
+        runs = _runs(str(tmp_path), line)
+        out = bench.write_profile_summary(NAME, runs, {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}, str(tmp_path), STEPS)
+    finally:
+        DUR_NS = saved
+    assert out["launches_per_step"] == pytest.approx(LAUNCHES)
+    assert out["avg_us"] == pytest.approx(1000.0)
+    assert out["staging"]["copies"] == STEPS * LAUNCHES
+    text = open(out["file"]).read()
+    assert f"{STEPS} timed + {untimed} untimed steps" in text
