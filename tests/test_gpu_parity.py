@@ -167,11 +167,17 @@ def test_resume_and_merge():
     check(merged.reshape(B, Lq, Hq, dv).float().cpu().numpy(), ref, "bf16", "merge")
 
 
-def test_merge_matches_oracle_merge():
+# few parts (flat kernel) and many (parts split over thread groups merged
+# through LDS: 64 key ranges at d=128 as split-KV decoding makes them, a
+# ragged share of 37 parts over 8 groups at d=64 with two rows per workgroup,
+# 16 parts over 2 groups at d=512, 9 parts at d=256), rows not a multiple of
+# the rows per workgroup
+@pytest.mark.parametrize("n,rows,dv", [(5, 300, 128), (64, 301, 128), (37, 203, 64), (16, 77, 512),
+                                       (9, 50, 256), (65, 130, 96)])
+def test_merge_matches_oracle_merge(n, rows, dv):
     import oracle
 
-    rng = np.random.default_rng(3)
-    n, rows, dv = 5, 300, 128
+    rng = np.random.default_rng(3 + n)
     m = rng.standard_normal((n, rows)) * 3
     m[1, :50] = -np.inf  # parts that saw no key
     m[:, 7] = -np.inf    # a row no part saw
@@ -190,6 +196,12 @@ def test_merge_matches_oracle_merge():
     got = out.cpu().numpy()
     check(got, ref_out[0, :, 0], "fp32", "merge out")
     assert np.isneginf(mm.cpu().numpy()[7]) and ll.cpu().numpy()[7] == 0 and np.all(got[7] == 0)
+    # the merged state: m exactly (a maximum), l and O relative to it
+    fin = ~np.isneginf(acc.m[0, 0])
+    assert np.array_equal(np.isneginf(mm.cpu().numpy()), ~fin)
+    np.testing.assert_allclose(mm.cpu().numpy()[fin], acc.m[0, 0][fin], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(ll.cpu().numpy(), acc.l[0, 0], rtol=1e-5, atol=0)
+    np.testing.assert_allclose(OO.cpu().numpy(), acc.O[0, 0], rtol=1e-5, atol=1e-5 * np.abs(acc.O).max())
 
 
 def test_order_invariance_and_determinism():
