@@ -68,18 +68,18 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "bfd648ce0ce6cd53",
-    "ring_1m_gqa32x8_d128": 3518684359,
-    "prefill_bf16_h32_d128": 579572430,
-    "mla_h16_d512": 4261483261,
-    "decode_b4_gqa32x8_cache1m": 17250192331,
-    "decode_b4_gqa32x8_cache1m_fp8": 8661256152,
-    "decode_b4_gqa32x8_cache1m_bhsd": 17250474765,
-    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661488849,
-    "local_w4096_s4096_h32_d128": 953045405,
-    "docs4096_h32_d128": 191152446,
-    "bwd:prefill_bf16_h32_d128": 10671112090,
-    "bwd:mla_h16_d512": 105669749448,
+    "digest": "0789c10386868e72",
+    "ring_1m_gqa32x8_d128": 3518123522,
+    "prefill_bf16_h32_d128": 589148337,
+    "mla_h16_d512": 4262485043,
+    "decode_b4_gqa32x8_cache1m": 17250047940,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661079063,
+    "decode_b4_gqa32x8_cache1m_bhsd": 17250169873,
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661292657,
+    "local_w4096_s4096_h32_d128": 944393953,
+    "docs4096_h32_d128": 190463631,
+    "bwd:prefill_bf16_h32_d128": 10668025299,
+    "bwd:mla_h16_d512": 106238805987,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
