@@ -1133,17 +1133,33 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
                 const float ks = exp_scale(exk[bi]), vs = exp_scale(exv[bi]);
                 const char *kt = kst(u);
                 const char *vt = vst(u);
+                // every K code of the wave's tile is read from LDS before the
+                // first score MFMA, and every V^T code before the softmax, so
+                // the LDS latency is paid once per tile rather than per MFMA
+                u32x4 rk[C::KB][D / 32];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                    for (int cc = 0; cc < D / 32; ++cc)
+                        rk[kb][cc] = *reinterpret_cast<const u32x4 *>(kt + kaddr[cc] + kb * 32 * ROWB);
                 f32x16 s[C::KB];
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
                     s[kb] = bias;
 #pragma unroll
                     for (int cc = 0; cc < D / 32; ++cc) {
-                        const u32x4 raw = *reinterpret_cast<const u32x4 *>(kt + kaddr[cc] + kb * 32 * ROWB);
-                        s[kb] = mfma(widen(u32x2{raw[0], raw[1]}, ks), qf[2 * cc], s[kb]);
-                        s[kb] = mfma(widen(u32x2{raw[2], raw[3]}, ks), qf[2 * cc + 1], s[kb]);
+                        s[kb] = mfma(widen(u32x2{rk[kb][cc][0], rk[kb][cc][1]}, ks), qf[2 * cc], s[kb]);
+                        s[kb] = mfma(widen(u32x2{rk[kb][cc][2], rk[kb][cc][3]}, ks), qf[2 * cc + 1], s[kb]);
                     }
                 }
+                u32x2 rv[2 * C::KB][C::DB];
+#pragma unroll
+                for (int kss = 0; kss < 2 * C::KB; ++kss)
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db)
+                        rv[kss][db] = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                       (__attribute__((address_space(3))) i32x2 *)(vt + vaddr[db] + kss * 16 * ROWB)));
                 if (!full) mask_scores<C>(s, vis, (int)(wk0 - kbeg), g);
                 update_max_biased<C>(s, m_run, m_true, lsum, oacc, bias);
                 bf16x8 pf[2 * C::KB];
@@ -1151,12 +1167,7 @@ void fwd_fp8kv_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int kss = 0; kss < 2 * C::KB; ++kss)
 #pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        const u32x2 raw = __builtin_bit_cast(
-                            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                       (__attribute__((address_space(3))) i32x2 *)(vt + vaddr[db] + kss * 16 * ROWB)));
-                        oacc[db] = mfma(widen(raw, vs), pf[kss], oacc[db]);
-                    }
+                    for (int db = 0; db < C::DB; ++db) oacc[db] = mfma(widen(rv[kss][db], vs), pf[kss], oacc[db]);
             }
             // (after the last tile too, where nothing is in flight: every path
             // round the loop then ends with a wait the compiler can see, and it
