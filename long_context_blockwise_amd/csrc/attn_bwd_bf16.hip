@@ -953,6 +953,14 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[0][4 * j + e] = a0[e] + a1[e], dp[4 * j + e] = b0[e] + b1[e];
                 }
+                // the K^T fragments of the dQ products, all read before P and dS
+                // are computed (read one before each product, every product
+                // waited for its own reads)
+                bf16x8 kf[2][SDB];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int j = 0; j < SDB; ++j) kf[ks][j] = vfrag<C>(kt, vaddr, ks, SDB * hf + j);
                 if (!keys_all_seen(a, ch.start, k0, 32, kend, wg_tlo, wg_thi))
                     mask_scores<C>(s, vis, (int)(k0 - kbeg), g);
                 // dS^T = P^T (dP^T - D), packed as the B operands of dQ^T += K^T dS^T
@@ -972,7 +980,7 @@ void bwd_dq_wide_kernel(const BwdArgs A) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int j = 0; j < SDB; ++j) acc[j] = mfma(vfrag<C>(kt, vaddr, ks, SDB * hf + j), pf[ks], acc[j]);
+                    for (int j = 0; j < SDB; ++j) acc[j] = mfma(kf[ks][j], pf[ks], acc[j]);
             }
             // the next tile is in place; this stage and the partials are free
             // (after the last tile too, where nothing is in flight: every path
@@ -1125,6 +1133,16 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
             exchange_put(xch, w, lane, s, dp);
             tile_barrier();
             exchange_sum(xch, lane, s, dp);
+            // the dO^T and Q^T fragments of the dV and dK products, all read
+            // before P and dS are computed (as in the dQ kernel)
+            bf16x8 gfr[2][SDB], qfr[2][SDB];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < SDB; ++j) {
+                    gfr[ks][j] = vfrag<C>(gt, vaddr, ks, SDB * w + j);
+                    qfr[ks][j] = vfrag<C>(qt, vaddr, ks, SDB * w + j);
+                }
             if (!(t0 + 31 < a.Lq && keys_all_seen(a, ch.start, wk0, 32, len, t0, thi))) {
                 // element i is row t0 + 4g + ro(i), ro(i) = 8(i/4) + i%4, of the lane's key
                 const int64_t big = 1 << 30;
@@ -1171,8 +1189,8 @@ void bwd_dkdv_wide_kernel(const BwdArgs A) {
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int j = 0; j < SDB; ++j) {
-                    dv[j] = mfma(vfrag<C>(gt, vaddr, ks, SDB * w + j), pp[ks], dv[j]);
-                    dk[j] = mfma(vfrag<C>(qt, vaddr, ks, SDB * w + j), pd[ks], dk[j]);
+                    dv[j] = mfma(gfr[ks][j], pp[ks], dv[j]);
+                    dk[j] = mfma(qfr[ks][j], pd[ks], dk[j]);
                 }
         }
         // the next tile is in place; this stage and the partials are free
