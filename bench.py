@@ -68,18 +68,18 @@ KERNEL_SOURCES = ("long_context_blockwise_amd/csrc/attn_fwd_bf16.hip", "long_con
                   "long_context_blockwise_amd/csrc/tile_common.h", "long_context_blockwise_amd/csrc/ra_internal.h",
                   "long_context_blockwise_amd/csrc/ring_attn.cpp", "long_context_blockwise_amd/csrc/merge.hip")
 MEASURED_TRAFFIC = {
-    "digest": "91d6c6d5487a678f",
-    "ring_1m_gqa32x8_d128": 3518267464,
-    "prefill_bf16_h32_d128": 589286981,
-    "mla_h16_d512": 4261467304,
-    "decode_b4_gqa32x8_cache1m": 17249792844,
-    "decode_b4_gqa32x8_cache1m_fp8": 8661584634,
-    "decode_b4_gqa32x8_cache1m_bhsd": 17250039781,
-    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661848867,
-    "local_w4096_s4096_h32_d128": 950053454,
-    "docs4096_h32_d128": 190530387,
-    "bwd:prefill_bf16_h32_d128": 10724026294,
-    "bwd:mla_h16_d512": 106318966312,
+    "digest": "e2e31f289d21efb3",
+    "ring_1m_gqa32x8_d128": 3518201363,
+    "prefill_bf16_h32_d128": 600605906,
+    "mla_h16_d512": 4261628265,
+    "decode_b4_gqa32x8_cache1m": 17250013029,
+    "decode_b4_gqa32x8_cache1m_fp8": 8661515163,
+    "decode_b4_gqa32x8_cache1m_bhsd": 17250147298,
+    "decode_b4_gqa32x8_cache1m_fp8_bhsd": 8661657975,
+    "local_w4096_s4096_h32_d128": 947904156,
+    "docs4096_h32_d128": 190502846,
+    "bwd:prefill_bf16_h32_d128": 10444776712,
+    "bwd:mla_h16_d512": 109414190501,
 }
 
 HEADLINE = "ring_1m_gqa32x8_d128"
