@@ -103,6 +103,23 @@ def test_decode_split_kv(Lq, G, B):
     check(out2.float().cpu().numpy(), ref, "bf16", "decode via ring schedule")
 
 
+@pytest.mark.parametrize("dtype,d,Hq,Hkv", [("bf16", 128, 16, 8), ("fp32", 64, 8, 8)])
+def test_decode_split_kv_many_chunks(dtype, d, Hq, Hkv):
+    """Split-KV decoding over 129 chunks: launches of 64 chunks, a launch of
+    one ragged last chunk, and a merge of 129 partial states per row (split
+    over thread groups)."""
+    lens = (128,) * 128 + (100,)
+    cache = sum(lens)
+    Lq = 4
+    wl = wl_of(B=2, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, lens=lens, Lq=Lq, q_offset=cache - Lq, causal=True,
+               std=0.5 if dtype == "bf16" else 1.0)
+    x = inputs.make(wl, DEV)
+    ref, _ = oracle_out(x.q, x.chunks(), wl.q_offset, True)
+    out, _ = run(x, flags=ra.RA_FLAG_SPLIT_KV)
+    got = out.float().cpu().numpy() if dtype == "bf16" else out.cpu().numpy()
+    check(got, ref, dtype, f"decode {dtype} over {len(lens)} chunks")
+
+
 def test_decode_fp32_and_d512_split():
     wl = wl_of(B=1, Hq=16, Hkv=1, d=512, lens=(256, 256), Lq=8, q_offset=504, causal=True,
                std=4 / 512 ** 0.5)
